@@ -1,0 +1,149 @@
+"""TEST INFRASTRUCTURE ONLY: reference fp8 (e4m3) quantisation and fp8 attention.
+
+Where it comes from.  The VisualGen FLUX 3 article (everytik.com translation, section
+量化注意力与稀疏注意力) runs attention with fp8 Q/K (qk_dtype) and fp8 V (v_dtype) but
+prints no quantisation recipe; the kongchang.com English page ("Accelerated Deployment
+of FLUX 3 Klein on NVIDIA Blackwell", section "Reducing Numerical Precision") only says
+that narrow formats need block-wise scale factors.  The recipe below is this library's
+plainest reading of those two facts:
+
+  * format: OCP FP8 E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits,
+    subnormal step 2**-9, largest finite 448, no infinities; S.1111.111 is NaN);
+  * Q and K: one scale per (b, h, block of 128 consecutive packed tokens);
+  * V: one scale per (b, h, channel) over all tokens;
+  * scale = amax / 448 and codes = e4m3(clamp(x * (448 / amax), -448, 448)), with
+    amax, both quotients and the product in binary32 (round to nearest even) and the
+    e4m3 rounding also to nearest even; amax == 0 gives scale 1 and all-zero codes;
+  * P: the softmax numerators, taken relative to an integer row maximum in base 2
+    and multiplied by 2**8, are rounded to e4m3 before the P.V product; the row sum
+    uses the unrounded numerators.
+
+Scales are dequantisation multipliers: x ~= decode(code) * scale.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+E4M3_MAX = 448.0
+QK_BLOCK = 128          # tokens per Q/K scale block
+P_SCALE_LOG2 = 8        # P is stored as e4m3(2**8 * p)
+
+
+# --------------------------------------------------------------------- the format
+def e4m3_encode(x) -> np.ndarray:
+    """Round to the nearest e4m3 value (ties to even) after clamping to +-448.
+
+    Works on any real array; values are handled in float64, where every step below is
+    exact.  NaN maps to 0x7F (with its sign); the sign of zero is kept.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    sign = np.signbit(x).astype(np.uint8) << np.uint8(7)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    nan = np.isnan(x)
+    a = np.where(nan, 0.0, a)
+    _, E = np.frexp(a)                      # a = f * 2**E, f in [0.5, 1)
+    e = E.astype(np.int64) - 1              # a in [2**e, 2**(e+1))
+    normal = a >= 2.0 ** -6
+    q = np.where(normal, e - 3, -9)         # spacing of e4m3 values near a
+    r = np.rint(a / np.exp2(q.astype(np.float64)))   # ties to even; exact division
+    # normal: value = r * 2**(e-3), r in [8, 16] -> code = (e+7)*8 + (r-8);
+    #         r == 16 rolls over into the next binade by itself.
+    # subnormal: value = r * 2**-9, r in [0, 8] -> code = r (8 is the smallest normal).
+    code = np.where(normal, (e + 7) * 8 + (r.astype(np.int64) - 8), r.astype(np.int64))
+    code = np.where(nan, 0x7F, code)
+    return (code.astype(np.uint8) | sign)
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """e4m3 codes (uint8) -> float64 values (NaN for the two NaN codes)."""
+    c = np.asarray(code, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    E = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(E == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2((E - 7).astype(np.float64)))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return s * val
+
+
+# --------------------------------------------------------------------- quantisers
+def _widen_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _scales_from_amax(amax: np.ndarray):
+    amax = amax.astype(np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1), amax)
+    scale = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)
+    return scale, inv
+
+
+def quantise_qk(x_tok: np.ndarray, block: int = QK_BLOCK):
+    """Q or K, token-major [B, N, H, D] bf16 bits -> (codes [B, N, H, D] uint8,
+    scales [B, H, ceil(N/block)] float32).  A short last block uses its own rows."""
+    B, N, H, D = x_tok.shape
+    x = _widen_f32(x_tok)
+    nblk = -(-N // block)
+    codes = np.empty((B, N, H, D), dtype=np.uint8)
+    scales = np.empty((B, H, nblk), dtype=np.float32)
+    for blk in range(nblk):
+        lo, hi = blk * block, min(N, (blk + 1) * block)
+        xb = x[:, lo:hi]                                   # [B, t, H, D]
+        amax = np.abs(xb).max(axis=(1, 3))                 # [B, H]
+        scale, inv = _scales_from_amax(amax)
+        scales[:, :, blk] = scale
+        y = (xb * inv[:, None, :, None]).astype(np.float32)   # binary32 product
+        codes[:, lo:hi] = e4m3_encode(y)
+    return codes, scales
+
+
+def quantise_v(x_tok: np.ndarray):
+    """V, token-major [B, N, H, D] bf16 bits -> (codes [B, N, H, D] uint8,
+    scales [B, H, D] float32), one scale per channel over all tokens."""
+    x = _widen_f32(x_tok)
+    amax = np.abs(x).max(axis=1)                            # [B, H, D]
+    scale, inv = _scales_from_amax(amax)
+    y = (x * inv[:, None, :, :]).astype(np.float32)
+    return e4m3_encode(y), scale
+
+
+# --------------------------------------------------------------------- fp8 attention
+def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: float, sel,
+                       block: int = QK_BLOCK):
+    """Attention on the fp8 operands, selected rows (b, h, i).
+
+    For each row, in float64 with exactly dequantised operands:
+        t_j  = (q_i . k_j) * softmax_scale / ln 2            (logit in base-2 units)
+        M    = ceil(max_j t_j)                               (integer row maximum)
+        p_j  = 2 ** (t_j - M)                                (in (0, 1])
+        P_j  = decode(e4m3(2**8 * p_j))                      (P rounded to e4m3)
+        O[c] = (sum_j P_j * v_j[c]) / (2**8 * sum_j p_j)
+        lse  = (M + log2 sum_j p_j) * ln 2
+    q8/k8/v8 are token-major [B, N, H, D] codes; q_scale/k_scale [B, H, nblk];
+    v_scale [B, H, D].  Returns (O [n, D], lse [n]).
+    """
+    B, N, H, D = q8.shape
+    sel = np.asarray(sel, dtype=np.int64).reshape(-1, 3)
+    out = np.empty((len(sel), D), dtype=np.float64)
+    lse = np.empty((len(sel),), dtype=np.float64)
+    blk_of = np.arange(N) // block
+    cache = {}
+    for r, (b, h, i) in enumerate(sel):
+        key = (int(b), int(h))
+        if key not in cache:
+            kd = e4m3_decode(k8[b, :, h, :]) * k_scale[b, h, blk_of][:, None].astype(np.float64)
+            vd = e4m3_decode(v8[b, :, h, :]) * v_scale[b, h][None, :].astype(np.float64)
+            cache = {key: (kd, vd)}                       # keep one (b, h) at a time
+        kd, vd = cache[key]
+        qd = e4m3_decode(q8[b, i, h, :]) * float(q_scale[b, h, i // block])
+        t = (kd @ qd) * (softmax_scale / math.log(2.0))
+        M = math.ceil(t.max())
+        p = np.exp2(t - M)
+        P = e4m3_decode(e4m3_encode(p * 2.0 ** P_SCALE_LOG2))
+        l = p.sum()
+        out[r] = (P @ vd) / (2.0 ** P_SCALE_LOG2 * l)
+        lse[r] = (M + math.log2(l)) * math.log(2.0)
+    return out, lse
