@@ -1,0 +1,153 @@
+/*
+ * joint_attn -- joint multi-stream attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  In FLUX 3 Image Klein's diffusion transformer the text tokens, the
+ * noisy target-image tokens and zero or more reference-image tokens are kept in
+ * separate streams and meet only in one joint self-attention over their concatenation
+ * (VisualGen FLUX 3 article, everytik.com translation, section
+ * 使用 TensorRT LLM VisualGen 进行 FLUX 3 推理; several reference images may be passed,
+ * section 离线推理).  The article's section 量化注意力与稀疏注意力 names that attention as
+ * the main cost at 2048x2048 and offers bf16 and fp8 (qk_dtype / v_dtype) variants.
+ * This library computes it as unmasked scaled-dot-product attention,
+ *     O = softmax(Q K^T * softmax_scale) V        (per batch b and head h),
+ * in four calls: pack the streams, then either the bf16 forward, or the fp8 quantiser
+ * followed by the fp8 forward.
+ *
+ * Conventions for every call.
+ *   - Tensor pointers are DEVICE pointers (HBM) owned by the caller; the library never
+ *     allocates, frees or keeps them.  "Host" marks the few host pointers.
+ *   - Each call validates its arguments first; on any error nothing is launched and
+ *     nothing is written.  Otherwise it enqueues its kernels on `stream` (a hipStream_t
+ *     passed as void*; NULL = the default stream) and returns without synchronising.
+ *   - Return value: JA_OK (0) or an error code below; joint_attn_strerror() names it.
+ *     No C++ exception crosses this interface and the library never aborts.
+ *   - Calls keep no state between them and may be issued from several host threads.
+ *   - bf16 is IEEE binary32's top 16 bits; e4m3 is the OCP FP8 E4M3 format (bias 7,
+ *     3 mantissa bits, max finite 448, no infinities).
+ *   - Layouts (all dense, row-major, innermost last):
+ *       BNHD  [B][N][H][D]   token-major, what a per-stream projection produces
+ *       BHND  [B][H][N][D]   head-major, packed Q and K
+ *       BHDN  [B][H][D][ld]  channel-major with row pitch ld >= N, ld % 16 == 0, used for
+ *                            V (columns N..ld-1 are padding that pack writes as zero)
+ *   - Supported head sizes D: 64 and 128.  N may be any positive length (no multiple
+ *     required); N == 0 is accepted and does nothing.
+ */
+#ifndef JOINT_ATTN_H
+#define JOINT_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JA_OK 0
+#define JA_EINVAL 1        /* NULL pointer, non-positive size, inconsistent sizes, overflow */
+#define JA_EUNSUPPORTED 2  /* head size not 64/128, misaligned pointer, too many streams */
+#define JA_EHIP 3          /* the HIP runtime refused a launch; see joint_attn_last_hip_error */
+
+#define JA_LAYOUT_BHND 0
+#define JA_LAYOUT_BHDN 1
+
+#define JA_MAX_STREAMS 16   /* text + target + up to 14 reference images */
+#define JA_QK_BLOCK 128     /* tokens per fp8 scale block of Q and K */
+
+/* Human-readable name of a status code (static string). */
+const char *joint_attn_strerror(int status);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int joint_attn_last_hip_error(void);
+
+/* Smallest legal BHDN pitch for N tokens: N rounded up to a multiple of 16. */
+int64_t joint_attn_vt_ld(int64_t N);
+
+/*
+ * joint_attn_pack -- concatenate token streams along the token axis (the joint
+ * sequence of the VisualGen FLUX 3 article's joint attention; stream order text,
+ * noisy target, then reference images in the order they were given).
+ *
+ *   n_streams  1..JA_MAX_STREAMS
+ *   src        host array of n_streams device pointers; stream s is bf16 BNHD
+ *              [B][lens[s]][H][D] (a zero-length stream may pass NULL)
+ *   lens       host array of n_streams token counts (>= 0)
+ *   layout     JA_LAYOUT_BHND: dst is bf16 [B][H][N][D] (use for Q and K)
+ *              JA_LAYOUT_BHDN: dst is bf16 [B][H][D][ld] (use for V); padding zeroed
+ *   ld         row pitch for BHDN (ignored for BHND)
+ *   offsets    host output, n_streams + 1 entries: offsets[0] = 0,
+ *              offsets[s + 1] = offsets[s] + lens[s]; N = offsets[n_streams].
+ *              Written even when N == 0.
+ * Every element is copied bit for bit.  Source and destination must not overlap.
+ * Pointers must be 16-byte aligned.
+ */
+int joint_attn_pack(int n_streams, const void *const *src, const int64_t *lens,
+                    int B, int H, int D, int layout, int64_t ld,
+                    void *dst, int64_t *offsets, void *stream);
+
+/*
+ * joint_attn_fwd_bf16 -- O = softmax(Q K^T * softmax_scale) V over all N packed
+ * tokens, per (b, h), bf16 operands with fp32 accumulation and an online softmax.
+ *
+ *   q, k           bf16 BHND [B][H][N][D]
+ *   vt             bf16 BHDN [B][H][D][ldv] (only columns < N are read)
+ *   softmax_scale  usually 1/sqrt(D); must be finite and > 0
+ *   o              bf16 BNHD [B][N][H][D] (stream s's output is rows
+ *                  offsets[s] .. offsets[s+1]-1 of every batch)
+ *   lse            fp32 [B][H][N], natural-log log-sum-exp of each query row's logits,
+ *                  or NULL
+ * Results are deterministic (fixed reduction order, no atomics).
+ */
+int joint_attn_fwd_bf16(const void *q, const void *k, const void *vt,
+                        int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
+                        void *o, float *lse, void *stream);
+
+/*
+ * joint_attn_quant_fp8 -- quantise packed bf16 Q, K, V to e4m3 with dequantisation
+ * scales (x ~= decode(code) * scale).  The article's fp8 attention setting
+ * (section 量化注意力与稀疏注意力) fixes only that Q, K and V are fp8; the scaling
+ * granularity follows the block-wise-scale advice of the kongchang.com English page
+ * (section "Reducing Numerical Precision"):
+ *   Q, K: one scale per (b, h, block of JA_QK_BLOCK consecutive packed tokens; the last
+ *         block may be shorter), scale = amax / 448;
+ *   V:    one scale per (b, h, channel) over all N tokens, scale = amax / 448;
+ *   code = e4m3(clamp(x * (448 / amax), -448, 448)), binary32 arithmetic and e4m3
+ *         rounding to nearest even; amax == 0 gives scale 1 and zero codes; the sign of
+ *         a zero result is kept.  Inputs must be finite.
+ *
+ *   q, k       bf16 BHND [B][H][N][D]      -> q8, k8   e4m3 BHND [B][H][N][D]
+ *   vt         bf16 BHDN [B][H][D][ldv]    -> v8t      e4m3 BHDN [B][H][D][ldv],
+ *                                                     padding columns written as 0
+ *   q_scale, k_scale  fp32 [B][H][ceil(N / JA_QK_BLOCK)]
+ *   v_scale           fp32 [B][H][D]
+ * Codes and scales are bit-exact functions of the inputs.
+ */
+int joint_attn_quant_fp8(const void *q, const void *k, const void *vt,
+                         int B, int H, int64_t N, int D, int64_t ldv,
+                         void *q8, void *k8, void *v8t,
+                         float *q_scale, float *k_scale, float *v_scale, void *stream);
+
+/*
+ * joint_attn_fwd_fp8 -- attention on the e4m3 operands of joint_attn_quant_fp8.
+ *   QK^T on fp8 matrix cores with fp32 accumulation; per-block Q/K scales and
+ *   softmax_scale are folded into the base-2 exponent; the softmax numerators, taken
+ *   relative to an integer row maximum M (base 2) and multiplied by 2^8, are rounded to
+ *   e4m3 for the fp8 P.V product; the row sum uses the unrounded numerators; the
+ *   per-channel V scale is applied in the epilogue:
+ *     t_j = (q8_i . k8_j) * qs * ks * softmax_scale * log2(e),  p_j = 2^(t_j - M),
+ *     O[c] = vs[c] * sum_j e4m3(2^8 p_j) v8_j[c] / (2^8 sum_j p_j).
+ *
+ *   q8, k8            e4m3 BHND [B][H][N][D]
+ *   v8t               e4m3 BHDN [B][H][D][ldv]
+ *   q_scale, k_scale  fp32 [B][H][ceil(N / JA_QK_BLOCK)];  v_scale fp32 [B][H][D]
+ *   o                 bf16 BNHD [B][N][H][D];  lse fp32 [B][H][N] or NULL
+ *   mode              must be 0 (the plain recipe above)
+ */
+int joint_attn_fwd_fp8(const void *q8, const void *k8, const void *v8t,
+                       const float *q_scale, const float *k_scale, const float *v_scale,
+                       int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
+                       int mode, void *o, float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JOINT_ATTN_H */

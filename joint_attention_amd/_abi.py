@@ -1,0 +1,204 @@
+"""Python binding of libjoint_attn (ctypes).  Argument marshalling only.
+
+Every function here checks tensor placement/dtype/shape, allocates outputs with torch
+when the caller gives none, and calls the C entry point of the same name on the
+current HIP stream.  All arithmetic runs in the library's gfx950 kernels; there is no
+fallback path.  If the shared library is missing, calls raise instead of computing.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libjoint_attn.so")
+
+JA_OK, JA_EINVAL, JA_EUNSUPPORTED, JA_EHIP = 0, 1, 2, 3
+JA_LAYOUT_BHND, JA_LAYOUT_BHDN = 0, 1
+JA_MAX_STREAMS = 16
+JA_QK_BLOCK = 128
+
+EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
+           "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_quant_fp8",
+           "joint_attn_fwd_fp8")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class JointAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip_error: int = 0):
+        lib_ = _lib
+        msg = lib_.joint_attn_strerror(status).decode() if lib_ is not None else str(status)
+        extra = " (hipError %d)" % hip_error if status == JA_EHIP else ""
+        super().__init__("%s failed: %s%s" % (fn, msg, extra))
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the shared library once and declare every export's signature."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError("libjoint_attn.so is not built (%s); run "
+                               "`python -m joint_attention_amd.build`" % path)
+        h = ctypes.CDLL(path)
+        P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        h.joint_attn_strerror.restype = ctypes.c_char_p
+        h.joint_attn_strerror.argtypes = [I]
+        h.joint_attn_last_hip_error.restype = I
+        h.joint_attn_last_hip_error.argtypes = []
+        h.joint_attn_vt_ld.restype = I64
+        h.joint_attn_vt_ld.argtypes = [I64]
+        h.joint_attn_pack.restype = I
+        h.joint_attn_pack.argtypes = [I, P, P, I, I, I, I, I64, P, P, P]
+        h.joint_attn_fwd_bf16.restype = I
+        h.joint_attn_fwd_bf16.argtypes = [P, P, P, I, I, I64, I, I64, F, P, P, P]
+        h.joint_attn_quant_fp8.restype = I
+        h.joint_attn_quant_fp8.argtypes = [P, P, P, I, I, I64, I, I64, P, P, P, P, P, P, P]
+        h.joint_attn_fwd_fp8.restype = I
+        h.joint_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, I, I64, I, I64, F, I, P, P, P]
+        _lib = h
+        return h
+
+
+def _check(fn: str, status: int):
+    if status != JA_OK:
+        raise JointAttnError(fn, status, load().joint_attn_last_hip_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, dtype, name: str, ndim: int):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %d-D tensor" % (name, ndim))
+
+
+def joint_attn_vt_ld(N: int) -> int:
+    return int(load().joint_attn_vt_ld(int(N)))
+
+
+def joint_attn_pack(streams, layout: str = "bhnd", ld: int | None = None, out=None):
+    """Concatenate per-stream bf16 [B, L_s, H, D] tensors along tokens.
+
+    layout "bhnd" -> [B, H, N, D] (Q, K); "bhdn" -> [B, H, D, ld] (V; ld defaults to
+    joint_attn_vt_ld(N), padding zeroed).  Returns (packed, offsets list of n+1 ints).
+    """
+    torch = _torch()
+    streams = list(streams)
+    if not 1 <= len(streams) <= JA_MAX_STREAMS:
+        raise ValueError("need 1..%d streams" % JA_MAX_STREAMS)
+    for i, s in enumerate(streams):
+        _need(s, torch.bfloat16, "stream %d" % i, 4)
+    B, _, H, D = streams[0].shape
+    for s in streams:
+        if s.shape[0] != B or s.shape[2] != H or s.shape[3] != D or s.device != streams[0].device:
+            raise ValueError("streams must share B, H, D and the device")
+    N = sum(int(s.shape[1]) for s in streams)
+    lay = {"bhnd": JA_LAYOUT_BHND, "bhdn": JA_LAYOUT_BHDN}[layout]
+    if lay == JA_LAYOUT_BHDN:
+        ld = joint_attn_vt_ld(N) if ld is None else int(ld)
+        shape = (B, H, D, ld)
+    else:
+        ld = 0
+        shape = (B, H, N, D)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=streams[0].device)
+    elif tuple(out.shape) != shape:
+        raise ValueError("out must have shape %s" % (shape,))
+    _need(out, torch.bfloat16, "out", 4)
+    ptrs = (ctypes.c_void_p * len(streams))(*[s.data_ptr() if s.numel() else None for s in streams])
+    lens = (ctypes.c_int64 * len(streams))(*[int(s.shape[1]) for s in streams])
+    offs = (ctypes.c_int64 * (len(streams) + 1))()
+    st = load().joint_attn_pack(len(streams), ptrs, lens, B, H, D, lay, ld,
+                                out.data_ptr() if out.numel() else None, offs, _stream(out))
+    _check("joint_attn_pack", st)
+    return out, list(offs)
+
+
+def joint_attn_fwd_bf16(q, k, vt, softmax_scale: float | None = None, out=None,
+                        return_lse: bool = False):
+    """q, k: bf16 [B, H, N, D]; vt: bf16 [B, H, D, ldv].  Returns O [B, N, H, D]
+    (and lse [B, H, N] fp32 if asked)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, N, D = q.shape
+    if tuple(k.shape) != (B, H, N, D) or vt.shape[:3] != (B, H, D):
+        raise ValueError("k must match q; vt must be [B, H, D, ldv]")
+    ldv = int(vt.shape[3])
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out", 4)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    st = load().joint_attn_fwd_bf16(q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D, ldv,
+                                    scale, out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None, _stream(q))
+    _check("joint_attn_fwd_bf16", st)
+    return (out, lse) if return_lse else out
+
+
+def joint_attn_quant_fp8(q, k, vt, N: int | None = None):
+    """Returns (q8, k8, v8t, q_scale, k_scale, v_scale); codes are uint8 tensors."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, Nq, D = q.shape
+    N = Nq if N is None else int(N)
+    ldv = int(vt.shape[3])
+    dev = q.device
+    nblk = -(-N // JA_QK_BLOCK)
+    q8 = torch.empty((B, H, N, D), dtype=torch.uint8, device=dev)
+    k8 = torch.empty((B, H, N, D), dtype=torch.uint8, device=dev)
+    v8t = torch.empty((B, H, D, ldv), dtype=torch.uint8, device=dev)
+    qs = torch.empty((B, H, nblk), dtype=torch.float32, device=dev)
+    ks = torch.empty((B, H, nblk), dtype=torch.float32, device=dev)
+    vs = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    st = load().joint_attn_quant_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D, ldv,
+                                     q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), qs.data_ptr(),
+                                     ks.data_ptr(), vs.data_ptr(), _stream(q))
+    _check("joint_attn_quant_fp8", st)
+    return q8, k8, v8t, qs, ks, vs
+
+
+def joint_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, softmax_scale: float | None = None,
+                       mode: int = 0, out=None, return_lse: bool = False):
+    """fp8 attention on joint_attn_quant_fp8's outputs.  Returns O bf16 [B, N, H, D]."""
+    torch = _torch()
+    for t, n in ((q8, "q8"), (k8, "k8"), (v8t, "v8t")):
+        _need(t, torch.uint8, n, 4)
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, torch.float32, n, 3)
+    B, H, N, D = q8.shape
+    ldv = int(v8t.shape[3])
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q8.device)
+    _need(out, torch.bfloat16, "out", 4)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if return_lse else None
+    st = load().joint_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(),
+                                   q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+                                   B, H, N, D, ldv, scale, int(mode), out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None, _stream(q8))
+    _check("joint_attn_fwd_fp8", st)
+    return (out, lse) if return_lse else out

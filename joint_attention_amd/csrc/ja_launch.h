@@ -1,0 +1,26 @@
+// Host-side launchers of the gfx950 kernels (internal to libjoint_attn; arguments are
+// validated by the C entry points before any of these is called).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ja {
+
+hipError_t launch_pack(int n_streams, const void* const* src, const int64_t* offsets, int B,
+                       int H, int D, int layout, int64_t ld, void* dst, hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, int H, int N,
+                           int D, int64_t ldv, float softmax_scale, void* o, float* lse,
+                           hipStream_t stream);
+
+hipError_t launch_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int N,
+                            int D, int64_t ldv, void* q8, void* k8, void* v8t, float* q_scale,
+                            float* k_scale, float* v_scale, hipStream_t stream);
+
+hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
+                          const float* k_scale, const float* v_scale, int B, int H, int N, int D,
+                          int64_t ldv, float softmax_scale, void* o, float* lse,
+                          hipStream_t stream);
+
+}  // namespace ja

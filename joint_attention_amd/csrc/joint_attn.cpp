@@ -1,0 +1,137 @@
+// C-ABI entry points of libjoint_attn: argument validation, then kernel launches.
+// Declarations and the contract of every call are in include/joint_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "joint_attn.h"
+#include "ja_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxInt = 2147483647;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool head_size_ok(int D) { return D == 64 || D == 128; }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return JA_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return JA_EHIP;
+}
+
+// Shared checks of the attention-shaped calls: sizes, pitch, and that every launch
+// dimension and 32-bit in-kernel index stays in range.
+int check_shape(int B, int H, int64_t N, int D, int64_t ldv) {
+    if (B <= 0 || H <= 0 || N < 0 || D <= 0) return JA_EINVAL;
+    if (!head_size_ok(D)) return JA_EUNSUPPORTED;
+    if (N > kMaxInt / 2 || ldv < N || ldv % 16 != 0) return JA_EINVAL;
+    if ((int64_t)B * H > 65535) return JA_EINVAL;
+    const int64_t qtiles = (N + 63) / 64;             // finest query tiling any kernel uses
+    if (qtiles * B * H > kMaxInt) return JA_EINVAL;
+    if ((int64_t)B * H * D * ldv > ((int64_t)1 << 46)) return JA_EINVAL;   // element counts
+    return JA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* joint_attn_strerror(int status) {
+    switch (status) {
+        case JA_OK: return "ok";
+        case JA_EINVAL: return "invalid argument";
+        case JA_EUNSUPPORTED: return "unsupported argument (head size, alignment, stream count or mode)";
+        case JA_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int joint_attn_last_hip_error(void) { return g_last_hip_error; }
+
+int64_t joint_attn_vt_ld(int64_t N) { return N <= 0 ? 0 : (N + 15) / 16 * 16; }
+
+int joint_attn_pack(int n_streams, const void* const* src, const int64_t* lens, int B, int H,
+                    int D, int layout, int64_t ld, void* dst, int64_t* offsets, void* stream) {
+    if (n_streams <= 0 || !src || !lens || !offsets) return JA_EINVAL;
+    if (n_streams > JA_MAX_STREAMS) return JA_EUNSUPPORTED;
+    if (B <= 0 || H <= 0 || D <= 0) return JA_EINVAL;
+    if (!head_size_ok(D)) return JA_EUNSUPPORTED;
+    if (layout != JA_LAYOUT_BHND && layout != JA_LAYOUT_BHDN) return JA_EINVAL;
+    int64_t off[JA_MAX_STREAMS + 1];
+    off[0] = 0;
+    for (int s = 0; s < n_streams; ++s) {
+        if (lens[s] < 0 || lens[s] > kMaxInt) return JA_EINVAL;
+        if (lens[s] > 0 && !src[s]) return JA_EINVAL;
+        if (lens[s] > 0 && !aligned16(src[s])) return JA_EUNSUPPORTED;
+        off[s + 1] = off[s] + lens[s];
+    }
+    const int64_t N = off[n_streams];
+    if (N > kMaxInt / 2 || (int64_t)B * N > kMaxInt || (int64_t)B * H > 65535) return JA_EINVAL;
+    if (layout == JA_LAYOUT_BHDN && (ld < N || ld % 16 != 0)) return JA_EINVAL;
+    const int64_t cols = layout == JA_LAYOUT_BHDN ? ld : N;
+    if (cols > 0 && !dst) return JA_EINVAL;
+    if (cols > 0 && !aligned16(dst)) return JA_EUNSUPPORTED;
+    for (int s = 0; s <= n_streams; ++s) offsets[s] = off[s];
+    if (cols == 0) return JA_OK;
+    return hip_status(ja::launch_pack(n_streams, src, off, B, H, D, layout, ld, dst,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int joint_attn_fwd_bf16(const void* q, const void* k, const void* vt, int B, int H, int64_t N,
+                        int D, int64_t ldv, float softmax_scale, void* o, float* lse,
+                        void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (N == 0) return JA_OK;
+    if (!q || !k || !vt || !o) return JA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return JA_EUNSUPPORTED;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
+    return hip_status(ja::launch_fwd_bf16(q, k, vt, B, H, (int)N, D, ldv, softmax_scale, o, lse,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int joint_attn_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int64_t N,
+                         int D, int64_t ldv, void* q8, void* k8, void* v8t, float* q_scale,
+                         float* k_scale, float* v_scale, void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (N == 0) return JA_OK;
+    if (!q || !k || !vt || !q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale)
+        return JA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(q8) || !aligned16(k8) ||
+        !aligned16(v8t))
+        return JA_EUNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+         reinterpret_cast<uintptr_t>(v_scale)) & 3u)
+        return JA_EUNSUPPORTED;
+    return hip_status(ja::launch_quant_fp8(q, k, vt, B, H, (int)N, D, ldv, q8, k8, v8t, q_scale,
+                                           k_scale, v_scale, static_cast<hipStream_t>(stream)));
+}
+
+int joint_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
+                       const float* k_scale, const float* v_scale, int B, int H, int64_t N, int D,
+                       int64_t ldv, float softmax_scale, int mode, void* o, float* lse,
+                       void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (mode != 0) return JA_EUNSUPPORTED;
+    if (N == 0) return JA_OK;
+    if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o) return JA_EINVAL;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o))
+        return JA_EUNSUPPORTED;
+    if (((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+          reinterpret_cast<uintptr_t>(v_scale)) & 3u) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return JA_EUNSUPPORTED;
+    return hip_status(ja::launch_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, B, H, (int)N, D,
+                                         ldv, softmax_scale, o, lse,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

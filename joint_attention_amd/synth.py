@@ -125,19 +125,28 @@ def make_streams(w: Workload, seed: int | None = None) -> Streams:
     return out
 
 
-def row_sample(w: Workload, n_rows: int, seed: int = 1234) -> np.ndarray:
+def row_sample(w: Workload, n_rows: int, seed: int = 1234, n_pairs: int | None = None) -> np.ndarray:
     """(b, h, i) triples for sampled parity checks at full size: every row within two
-    tokens of each stream boundary and of both ends, plus evenly spread random rows."""
+    tokens of each stream boundary and of both ends, plus random rows; restricted to
+    n_pairs random (b, h) pairs when given.  Sorted by (b, h, i)."""
     rng = np.random.default_rng(seed)
+    all_pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    if n_pairs is not None:
+        idx = rng.choice(len(all_pairs), min(n_pairs, len(all_pairs)), replace=False)
+        pairs = [all_pairs[i] for i in sorted(idx)]
+    else:
+        pairs = all_pairs
     offs = np.concatenate([[0], np.cumsum(w.stream_lens)])
     edge = set()
     for o in offs:
         for d in range(-2, 3):
             if 0 <= o + d < w.N:
                 edge.add(int(o + d))
-    rows = []
+    rows = set()
     for i in sorted(edge):
-        rows.append((int(rng.integers(w.B)), int(rng.integers(w.H)), i))
+        b, h = pairs[int(rng.integers(len(pairs)))]
+        rows.add((b, h, i))
     while len(rows) < n_rows:
-        rows.append((int(rng.integers(w.B)), int(rng.integers(w.H)), int(rng.integers(w.N))))
-    return np.asarray(rows, dtype=np.int64)
+        b, h = pairs[int(rng.integers(len(pairs)))]
+        rows.add((b, h, int(rng.integers(w.N))))
+    return np.asarray(sorted(rows), dtype=np.int64)

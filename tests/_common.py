@@ -1,0 +1,74 @@
+"""Shared helpers of the test suite: seeded inputs on both sides, parity measures."""
+from __future__ import annotations
+
+import functools
+import math
+
+import numpy as np
+
+from joint_attention_amd import synth
+
+# bf16 path bar vs the fp64 oracle, and the fp8 path bar vs the fp8 reference
+BF16_REL_F = 5e-3
+BF16_MAX_ABS = 2e-2
+FP8_REL_F = 5e-3
+FP8_MAX_ABS = 2e-2
+
+
+def rel_frobenius(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.linalg.norm((got - ref).ravel()) / np.linalg.norm(ref.ravel()))
+
+
+def max_abs(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.abs(got - ref).max())
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+@functools.lru_cache(maxsize=2)
+def host_streams(name_or_w, seed: int | None = None):
+    w = synth.WORKLOADS[name_or_w] if isinstance(name_or_w, str) else name_or_w
+    return synth.make_streams(w, seed)
+
+
+def packed_host(streams: synth.Streams):
+    """Oracle-side packing of q, k, v: token-major [B, N, H, D] bf16 bits + offsets."""
+    import oracle
+    q, offs = oracle.pack_tokens(streams.q)
+    k, _ = oracle.pack_tokens(streams.k)
+    v, _ = oracle.pack_tokens(streams.v)
+    return q, k, v, offs
+
+
+def to_device(bits: np.ndarray):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.cuda()
+
+
+def from_device_bf16(t) -> np.ndarray:
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def device_packed(streams: synth.Streams):
+    """Upload the streams and pack them with the library: (q, k, vt, offsets)."""
+    import joint_attention_amd as ja
+    qs = [to_device(s) for s in streams.q]
+    ks = [to_device(s) for s in streams.k]
+    vs = [to_device(s) for s in streams.v]
+    q, offs = ja.joint_attn_pack(qs, "bhnd")
+    k, _ = ja.joint_attn_pack(ks, "bhnd")
+    vt, _ = ja.joint_attn_pack(vs, "bhdn")
+    return q, k, vt, offs
+
+
+def gather_rows(o_tok: np.ndarray, sel: np.ndarray) -> np.ndarray:
+    """Rows (b, h, i) of a token-major [B, N, H, D] array -> [n, D]."""
+    return o_tok[sel[:, 0], sel[:, 2], sel[:, 1], :]
+
+
+def softmax_scale(D: int) -> float:
+    return 1.0 / math.sqrt(D)

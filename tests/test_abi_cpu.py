@@ -1,0 +1,94 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments
+before touching the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import joint_attention_amd as ja
+from joint_attention_amd import _abi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "joint_attn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(joint_attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ja.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ja.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert set(declared) == set(_abi.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_ld(lib):
+    assert lib.joint_attn_strerror(0) == b"ok"
+    assert b"invalid" in lib.joint_attn_strerror(1)
+    assert lib.joint_attn_strerror(99) == b"unknown status"
+    assert [lib.joint_attn_vt_ld(n) for n in (0, 1, 16, 17, 288, 16896)] == [0, 16, 16, 32, 288, 16896]
+
+
+def _pack(lib, n, srcs, lens, B=1, H=2, D=128, layout=0, ld=0, dst=None):
+    P = ctypes.c_void_p
+    src_arr = (P * max(n, 1))(*srcs) if srcs is not None else None
+    len_arr = (ctypes.c_int64 * max(n, 1))(*lens) if lens is not None else None
+    offs = (ctypes.c_int64 * (max(n, 1) + 1))()
+    st = lib.joint_attn_pack(n, src_arr, len_arr, B, H, D, layout, ld, dst, offs, None)
+    return st, list(offs)
+
+
+def test_pack_validation(lib):
+    fake = 0x10000                                   # aligned, never dereferenced
+    assert _pack(lib, 0, [], [])[0] == 1
+    assert _pack(lib, 17, [fake] * 17, [1] * 17)[0] == 2
+    assert _pack(lib, 2, [fake, fake], [4, 4], D=96)[0] == 2
+    assert _pack(lib, 2, [fake, fake], [4, -1])[0] == 1
+    assert _pack(lib, 2, [fake, None], [4, 4], dst=fake)[0] == 1        # NULL non-empty stream
+    assert _pack(lib, 2, [fake, fake + 8], [4, 4], dst=fake)[0] == 2    # misaligned source
+    assert _pack(lib, 2, [fake, fake], [4, 4], dst=None)[0] == 1        # NULL destination
+    assert _pack(lib, 2, [fake, fake], [4, 4], layout=1, ld=8, dst=fake)[0] == 1   # ld < N
+    assert _pack(lib, 2, [fake, fake], [4, 4], layout=1, ld=24, dst=fake)[0] == 1  # ld % 16
+    assert _pack(lib, 2, [fake, fake], [4, 4], layout=7, dst=fake)[0] == 1
+    # all-empty streams: a successful no-op that still reports offsets
+    st, offs = _pack(lib, 3, [None, None, None], [0, 0, 0])
+    assert st == 0 and offs == [0, 0, 0, 0]
+
+
+def test_attention_validation(lib):
+    fake = 0x10000
+    f = lib.joint_attn_fwd_bf16
+    assert f(fake, fake, fake, 1, 2, 64, 96, 64, 0.1, fake, None, None) == 2      # D
+    assert f(fake, fake, fake, 0, 2, 64, 128, 64, 0.1, fake, None, None) == 1     # B
+    assert f(fake, fake, fake, 1, 2, 64, 128, 48, 0.1, fake, None, None) == 1     # ldv < N
+    assert f(fake, fake, fake, 1, 2, 64, 128, 72, 0.1, fake, None, None) == 1     # ldv % 16
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.0, fake, None, None) == 1     # scale
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, float("nan"), fake, None, None) == 1
+    assert f(None, fake, fake, 1, 2, 64, 128, 64, 0.1, fake, None, None) == 1
+    assert f(fake + 4, fake, fake, 1, 2, 64, 128, 64, 0.1, fake, None, None) == 2
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, fake, fake + 2, None) == 2  # lse align
+    assert f(None, None, None, 1, 2, 0, 128, 0, 0.1, None, None, None) == 0       # N == 0
+    g = lib.joint_attn_fwd_fp8
+    assert g(fake, fake, fake, fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 1, fake, None, None) == 2
+    assert g(fake, fake, fake, None, fake, fake, 1, 2, 64, 128, 64, 0.1, 0, fake, None, None) == 1
+    q = lib.joint_attn_quant_fp8
+    assert q(fake, fake, fake, 1, 2, 64, 128, 64, fake, fake, fake, None, fake, fake, None) == 1
+    assert q(fake, fake, fake, 1, 2, 64, 128, 64, fake, fake, fake + 3, fake, fake, fake, None) == 2
+
+
+def test_python_binding_rejects_cpu_tensors(lib):
+    import torch
+    x = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ja.joint_attn_pack([x])
