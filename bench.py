@@ -1,0 +1,237 @@
+"""Benchmark of the joint-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t2i_2048_bf16]
+
+Workload: FLUX 3 Image Klein 2048x2048 text-to-image joint attention -- batch 2
+(classifier-free guidance), 24 heads of 128, 512 text + 16384 image tokens
+(N = 16896), seeded synthetic bf16 inputs (joint_attention_amd.synth), resident in HBM
+before timing starts.
+
+One timed step of the bf16 path = pack(Q), pack(K), pack(V^T) -> joint_attn_fwd_bf16.
+The fp8 path (pack x3 -> joint_attn_quant_fp8 -> joint_attn_fwd_fp8) on the same
+inputs is timed the same way in its own loop and reported under "fp8".
+value = algorithmic attention flops (4 B H N^2 D) per bf16 step / step time.
+
+Per-kernel durations come from HIP events recorded on the launch stream around every
+launch inside the timed loops.  The CPU baseline times the fp64 oracle on a bounded
+sample of query rows of the same workload on this host's cores.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "joint-attention TFLOP/s at 2048^2 (16896 tok, bf16/fp8); % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="t2i_2048_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle sample")
+    ap.add_argument("--skip-fp8", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, host, target_s: float):
+    """fp64 oracle on a bounded row sample of the same inputs; TFLOP/s on 4*N*D per row."""
+    import numpy as np
+    import oracle
+    from joint_attention_amd import synth
+    qh, kh, vh = host
+    scale = 1.0 / math.sqrt(w.D)
+    threads = oracle.default_threads()
+    probe = synth.row_sample(w, 256, seed=7)
+    t0 = time.perf_counter()
+    oracle.attention_rows(qh, kh, vh, scale, probe, threads)
+    t_probe = time.perf_counter() - t0
+    n = int(max(256, min(200000, 256 * target_s / max(t_probe, 1e-6))))
+    sel = synth.row_sample(w, n, seed=8)
+    t0 = time.perf_counter()
+    oracle.attention_rows(qh, kh, vh, scale, sel, threads)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.N * w.D * len(sel)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d query rows (every row near a stream boundary + random rows, "
+                      "row_sample seed 8) of %s: B=%d H=%d N=%d D=%d, fp64, %.1f s"
+                      % (len(sel), w.name, w.B, w.H, w.N, w.D, dt),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import joint_attention_amd as ja
+    from joint_attention_amd import synth
+
+    if not os.path.exists(ja.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "no GPU visible"
+    torch.cuda.set_device(0)
+    ja.load()
+
+    w = synth.WORKLOADS[args.workload]
+    log("generating %s inputs (B=%d H=%d N=%d D=%d)" % (w.name, w.B, w.H, w.N, w.D))
+    st = synth.make_streams(w)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    qs_d = [dev(s) for s in st.q]
+    ks_d = [dev(s) for s in st.k]
+    vs_d = [dev(s) for s in st.v]
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(w.D)
+    N, B, H, D = w.N, w.B, w.H, w.D
+    ldv = ja.joint_attn_vt_ld(N)
+    q = torch.empty((B, H, N, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty_like(q)
+    vt = torch.empty((B, H, D, ldv), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((B, N, H, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def step_bf16(rec):
+        e0, e1, e2 = (ev(), ev(), ev()) if rec else (None, None, None)
+        if rec:
+            e0.record(stream)
+        ja.joint_attn_pack(qs_d, "bhnd", out=q)
+        ja.joint_attn_pack(ks_d, "bhnd", out=k)
+        ja.joint_attn_pack(vs_d, "bhdn", out=vt)
+        if rec:
+            e1.record(stream)
+        ja.joint_attn_fwd_bf16(q, k, vt, scale, out=o)
+        if rec:
+            e2.record(stream)
+        return (e0, e1, e2)
+
+    def timed(step, steps, warmup):
+        for _ in range(warmup):
+            step(False)
+        torch.cuda.synchronize()
+        evs = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            evs.append(step(True))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        durs = [[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in evs]
+        return wall, np.asarray(durs)
+
+    log("timing bf16 path: %d warmup + %d steps" % (args.warmup, args.steps))
+    wall, durs = timed(step_bf16, args.steps, args.warmup)
+    ms_step = wall * 1e3 / args.steps
+    pack_ms, fwd_ms = durs.mean(axis=0)
+    flops = float(w.flops)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D,
+                   "stream_lens": list(w.stream_lens), "step": "pack q,k,v + fwd_bf16"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "fwd_bf16_kernel<128>",
+                     "avg_launch_ms": round(float(fwd_ms), 4),
+                     "min_launch_ms": round(float(durs[:, 1].min()), 4)},
+        "kernels_ms": {"pack_qkv": round(float(pack_ms), 4), "fwd_bf16": round(float(fwd_ms), 4)},
+        "pct_of_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+    }
+
+    if not args.skip_fp8:
+        q8 = torch.empty((B, H, N, D), dtype=torch.uint8, device="cuda")
+        k8 = torch.empty_like(q8)
+        v8t = torch.empty((B, H, D, ldv), dtype=torch.uint8, device="cuda")
+        nblk = -(-N // ja.JA_QK_BLOCK)
+        qsc = torch.empty((B, H, nblk), dtype=torch.float32, device="cuda")
+        ksc = torch.empty_like(qsc)
+        vsc = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
+        lib = ja.load()
+        sptr = stream.cuda_stream
+
+        def step_fp8(rec):
+            e = [ev() for _ in range(4)] if rec else None
+            if rec:
+                e[0].record(stream)
+            ja.joint_attn_pack(qs_d, "bhnd", out=q)
+            ja.joint_attn_pack(ks_d, "bhnd", out=k)
+            ja.joint_attn_pack(vs_d, "bhdn", out=vt)
+            if rec:
+                e[1].record(stream)
+            rc = lib.joint_attn_quant_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D,
+                                          ldv, q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(),
+                                          qsc.data_ptr(), ksc.data_ptr(), vsc.data_ptr(), sptr)
+            assert rc == 0, rc
+            if rec:
+                e[2].record(stream)
+            ja.joint_attn_fwd_fp8(q8, k8, v8t, qsc, ksc, vsc, scale, out=o)
+            if rec:
+                e[3].record(stream)
+            return e
+
+        log("timing fp8 path")
+        wall8, durs8 = timed(step_fp8, args.steps, args.warmup)
+        ms8 = wall8 * 1e3 / args.steps
+        p8, qn8, f8 = durs8.mean(axis=0)
+        out["fp8"] = {
+            "workload": "t2i_2048_fp8 (same inputs)", "dtype": "fp8 e4m3 (fp32 accumulate)",
+            "value": round(flops / (ms8 * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms8, 4),
+            "step": "pack q,k,v + quant_fp8 + fwd_fp8",
+            "kernels_ms": {"pack_qkv": round(float(p8), 4), "quant_fp8": round(float(qn8), 4),
+                           "fwd_fp8": round(float(f8), 4)},
+            "fwd_fp8_tflops": round(flops / (f8 * 1e-3) / 1e12, 2),
+            "frac_of_fp8_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "frac_of_bf16_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        log("cpu baseline (oracle)")
+        qh, _ = oracle.pack_tokens(st.q)
+        kh, _ = oracle.pack_tokens(st.k)
+        vh, _ = oracle.pack_tokens(st.v)
+        cb = cpu_baseline(w, (qh, kh, vh), args.cpu_seconds)
+        cb.pop("seconds")
+        out["cpu_baseline"] = {k2: (round(v2, 6) if isinstance(v2, float) else v2)
+                               for k2, v2 in cb.items()}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
