@@ -69,42 +69,62 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(
     for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
         for (int a = 0; a < 16; ++a) oacc[ob][a] = 0.f;
+    // m: the row maximum used as the exponent offset (base-2 units).  It is raised only
+    // when a tile's maximum exceeds it by more than kLazy, so most tiles skip the
+    // rescale of O; the numerators 2^(t - m) then stay below 2^kLazy.
+    constexpr float kLazy = 8.f;
     float m = -INFINITY, l = 0.f;
 
     const int nkt = (N + BC - 1) / BC;
+    const int nfull = N / BC;             // tiles with all 64 keys inside the sequence
     uint4 kreg[KCH], vreg[VCH];
 
-    auto load_tile = [&](int kt) {
+    auto load_full = [&](int kt) {
         const int k0 = kt * BC;
-        const bool full = k0 + BC <= N;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int idx = tid + i * NTHREADS, row = idx / DC, ch = idx % DC;
+            kreg[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)(k0 + row) * D + ch * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int idx = tid + i * NTHREADS, row = idx / (BC / 8), ch = idx % (BC / 8);
+            vreg[i] = *reinterpret_cast<const uint4*>(Vbh + (int64_t)row * ldv + k0 + ch * 8);
+        }
+    };
+    // last, partial tile: keys >= N read as zero (K rows and V^T columns)
+    auto load_tail = [&](int kt) {
+        const int k0 = kt * BC;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             const int idx = tid + i * NTHREADS, row = idx / DC, ch = idx % DC;
             const int key = k0 + row;
             kreg[i] = make_uint4(0, 0, 0, 0);
-            if (full || key < N)
+            if (key < N)
                 kreg[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + ch * 8);
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int idx = tid + i * NTHREADS, row = idx / (BC / 8), ch = idx % (BC / 8);
             const int key = k0 + ch * 8;
-            vreg[i] = make_uint4(0, 0, 0, 0);
-            if (full || key < N) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (key < N) {
                 // key < N and key % 8 == 0 keep key + 8 <= ldv (ldv % 16 == 0)
-                uint4 v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)row * ldv + key);
-                if (!full) {
-                    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)row * ldv + key);
+                uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (key + 2 * e >= N) wv[e] = 0;
-                        else if (key + 2 * e + 1 >= N) wv[e] &= 0xFFFFu;
-                    }
-                    v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                for (int e = 0; e < 4; ++e) {
+                    if (key + 2 * e >= N) wv[e] = 0;
+                    else if (key + 2 * e + 1 >= N) wv[e] &= 0xFFFFu;
                 }
-                vreg[i] = v;
+                v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             }
+            vreg[i] = v;
         }
+    };
+    auto load_tile = [&](int kt) {
+        if (kt < nfull) load_full(kt);
+        else load_tail(kt);
     };
     auto store_tile = [&]() {
 #pragma unroll
@@ -115,35 +135,31 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int idx = tid + i * NTHREADS, row = idx / (BC / 8), ch = idx % (BC / 8);
-            *reinterpret_cast<uint4*>(&sv[row * BC + ((ch ^ (row % 8)) * 8)]) = vreg[i];
+            *reinterpret_cast<uint4*>(&sv[row * BC + ((ch ^ ((row >> 1) & 7)) * 8)]) = vreg[i];
         }
     };
 
-    load_tile(0);
-    for (int kt = 0; kt < nkt; ++kt) {
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < nkt) load_tile(kt + 1);
-
+    auto tile = [&](int kt) {
         // S^T for two 32-key blocks
         floatx16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int a = 0; a < 16; ++a) s[kb][a] = 0.f;
             const int krow = kb * 32 + swap_bits23(r32);
 #pragma unroll
             for (int c = 0; c < NQC; ++c) {
                 const int u = 2 * c + hh;
                 const bf16x8 av =
                     *reinterpret_cast<const bf16x8*>(&sk[krow * D + ((u ^ (krow % DC)) * 8)]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], s[kb], 0, 0, 0);
+                if (c == 0) {
+                    const floatx16 zero = {};
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], zero, 0, 0, 0);
+                } else {
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], s[kb], 0, 0, 0);
+                }
             }
         }
-
-        // keys past the end of the sequence (last tile only)
-        const int k0 = kt * BC;
-        if (k0 + BC > N) {
+        if (kt >= nfull) {                        // last, partial tile (uniform branch)
+            const int k0 = kt * BC;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -153,41 +169,41 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(
                 }
         }
 
-        // online softmax in base 2: scores are scaled by c2 = scale * log2(e)
+        // online softmax in base 2: t = s * c2 with c2 = scale * log2(e)
         float mx = s[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[kb][a]);
-        mx = wave_halves_max(mx);
-        const float m_new = fmaxf(m, mx * c2);
-        const float alpha = fast_exp2(m - m_new);
-        m = m_new;
-        l *= alpha;
+        mx = wave_halves_max(mx) * c2;
+        if (__ballot(mx > m + kLazy) != 0) {       // wave-uniform: some row's max grew a lot
+            const float m_new = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - m_new);
+            m = m_new;
+            l *= alpha;
 #pragma unroll
-        for (int ob = 0; ob < NOB; ++ob)
+            for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-            for (int a = 0; a < 16; ++a) oacc[ob][a] *= alpha;
+                for (int a = 0; a < 16; ++a) oacc[ob][a] *= alpha;
+        }
 
         bf16x8 pf[4];
+        const float nm = -m;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                floatx2 pr[4];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float p = fast_exp2(fmaf(s[kb][8 * u + e], c2, -m));
-                    l += p;
-                    pr[e / 2][e % 2] = p;
-                }
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bf16x2 pb = __builtin_convertvector(pr[e], bf16x2);
+                    floatx2 pr = {fast_exp2(fmaf(s[kb][8 * u + 2 * e], c2, nm)),
+                                  fast_exp2(fmaf(s[kb][8 * u + 2 * e + 1], c2, nm))};
+                    const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+                    // row sum of the bf16 numerators that feed the P.V product
+                    l = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(__bf16)1.f, (__bf16)1.f}, l,
+                                                        false);
                     pf[2 * kb + u][2 * e] = pb[0];
                     pf[2 * kb + u][2 * e + 1] = pb[1];
                 }
-            }
 
         // O^T += V^T P^T
 #pragma unroll
@@ -196,11 +212,19 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int u = 2 * t + hh;
-                const bf16x8 av =
-                    *reinterpret_cast<const bf16x8*>(&sv[vrow * BC + ((u ^ (vrow % 8)) * 8)]);
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(
+                    &sv[vrow * BC + ((u ^ ((vrow >> 1) & 7)) * 8)]);
                 oacc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[t], oacc[ob], 0, 0, 0);
             }
         }
+    };
+
+    load_tile(0);
+    for (int kt = 0; kt < nkt; ++kt) {
+        store_tile();
+        __syncthreads();
+        if (kt + 1 < nkt) load_tile(kt + 1);
+        tile(kt);
         __syncthreads();
     }
 
