@@ -13,7 +13,8 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libjoint_attn.so")
+# JOINT_ATTN_LIB overrides the shared object (e.g. an alternative build of the kernels)
+LIB_PATH = os.environ.get("JOINT_ATTN_LIB") or os.path.join(HERE, "libjoint_attn.so")
 
 JA_OK, JA_EINVAL, JA_EUNSUPPORTED, JA_EHIP = 0, 1, 2, 3
 JA_LAYOUT_BHND, JA_LAYOUT_BHDN = 0, 1

@@ -21,6 +21,13 @@ ARCH = os.environ.get("JA_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["joint_attn.cpp", "pack.hip", "fwd_bf16.hip", "quant_fp8.hip", "fwd_fp8.hip"]
 
+# per-source code-generation options: the bf16 forward keeps its MFMA accumulators in
+# architectural VGPRs where possible, which is what lets its 64 query rows per wave,
+# two score tiles and two P tiles fit without spilling
+# (and, no NaN ever being an operand there, skips the NaN canonicalisation in front of
+# every v_max; infinities keep their meaning)
+EXTRA_FLAGS = {"fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
+
 
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -36,16 +43,22 @@ def compile_flags() -> list[str]:
             "-I" + INCLUDE, "-I" + CSRC]
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source to an object (in parallel), link the shared library."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, jobs: int = 8, out: str | None = None,
+          defines: tuple = ()) -> str:
+    """Compile every source to an object (in parallel), link the shared library
+    (to `out`, default libjoint_attn.so here; `defines` adds -D options)."""
+    lib_path = out or LIB
+    objdir = os.path.join(os.path.dirname(os.path.abspath(lib_path)), "_build",
+                          os.path.basename(lib_path).replace(".so", ""))
     os.makedirs(objdir, exist_ok=True)
     procs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"]
-        cmd = [hipcc()] + compile_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([hipcc()] + compile_flags() + ["-D" + d for d in defines] +
+               EXTRA_FLAGS.get(src, []) + lang +
+               ["-c", os.path.join(CSRC, src), "-o", obj])
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -64,14 +77,17 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             print("\n".join(lines))
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib_path + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    args = [a for a in sys.argv[1:] if a != "-v"]
+    out = next((a[len("--out="):] for a in args if a.startswith("--out=")), None)
+    defs = tuple(a[2:] for a in args if a.startswith("-D"))
+    print(build(verbose="-v" in sys.argv, out=out, defines=defs))

@@ -4,8 +4,11 @@
 // (VisualGen FLUX 3 article, everytik.com translation, sections
 // 使用 TensorRT LLM VisualGen 进行 FLUX 3 推理 and 量化注意力与稀疏注意力).
 //
-// Work split.  One workgroup = 4 waves = 128 query rows of one (b, h); each wave owns
-// 32 query rows for the whole key loop.  Keys are consumed in tiles of 64.
+// Work split.  One workgroup = 4 waves = 256 query rows of one (b, h); each wave owns
+// two 32-row query blocks for the whole key loop (one wave per SIMD, with the whole
+// 512-entry register file: Q, O, two score tiles and two P tiles stay resident).
+// Keys are consumed in tiles of BC = 32; every K or V^T operand read from LDS feeds
+// two MFMAs, one per query block.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64).  The wave computes the
 // transposed scores S^T = K Q^T: operand A = 32 keys (from LDS), operand B = the
@@ -19,36 +22,67 @@
 // carries in the PV step; reading K rows in an order with bits 2 and 3 of the row
 // index swapped makes each lane's 8 scores of a 16-key step 8 consecutive keys.
 //
-// LDS.  K tile [64 keys][D] and V^T tile [D][64 keys], 16-byte chunks XOR-swizzled by
-// row so the 16-byte MFMA operand reads of 32 different rows are bank-conflict free.
-// The next tile's global loads are issued into registers before the current tile's
-// MFMAs and written to LDS after them.
+// Software pipeline.  Iteration j runs the softmax of tile j on the vector ALU while
+// the matrix cores run P(j-1) V(j-1) and Q K(j+1)^T; the three are independent, and
+// the loop body is written as an explicit sequence of steps (one LDS operand read, two
+// MFMAs and a slice of the softmax each) separated by scheduling fences.  K and V^T
+// tiles are double-buffered in LDS and filled by direct global->LDS 16-byte loads
+// (lane l's 16 bytes land at base + 16 l), one tile ahead; one barrier per iteration.
+// Chunks are XOR-swizzled by row so that the 16-byte operand reads of 16 consecutive
+// lanes (16 different rows) hit distinct banks; the swizzle is applied on the global
+// side of the direct loads.
+//
+// Softmax details.  Scores are scaled to base 2 (c2 = scale * log2 e) in the FMA that
+// subtracts the running maximum m.  m is raised only when a tile's maximum exceeds it
+// by more than 16, so O is rescaled rarely; the numerators stay below 2^16.  The row
+// sum accumulates the bf16-rounded numerators with v_dot2 (the same values that
+// enter P V).
+#include <type_traits>
+
 #include "ja_device.h"
 #include "ja_launch.h"
 
 namespace ja {
 namespace {
 
-constexpr int BR = 128;          // query rows per workgroup
-constexpr int BC = 64;           // keys per tile
-constexpr int NTHREADS = 256;
+constexpr int NTHREADS = 256;    // 4 waves, one query slice each
+#ifndef FWD_QB
+#define FWD_QB 1
+#endif
+#ifndef FWD_BC
+#define FWD_BC 32
+#endif
+#ifndef FWD_LEAD
+#define FWD_LEAD 3
+#endif
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-template <int D>
-__global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(
+// QB: 32-row query blocks per wave; BC: keys per tile.  QB = 2 runs one wave per SIMD
+// with the whole register file; QB = 1 runs two workgroups per CU.
+template <int D, int QB, int BC>
+__global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ VT,
     int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE,
     int n_qtiles, int total) {
-    constexpr int DC = D / 8;            // 16-byte chunks per K row
-    constexpr int NQC = D / 16;          // k-steps of the QK product
-    constexpr int NOB = D / 32;          // 32-channel blocks of the output
-    constexpr int KCH = BC * DC / NTHREADS;
-    constexpr int VCH = D * (BC / 8) / NTHREADS;
-    __shared__ __attribute__((aligned(16))) __bf16 sk[BC * D];
-    __shared__ __attribute__((aligned(16))) __bf16 sv[D * BC];
+    constexpr int BR = 4 * QB * 32;              // query rows per workgroup
+    constexpr int KB = BC / 32;                  // 32-key blocks per tile
+    constexpr int DC = D / 8;                    // 16-byte chunks per K row
+    constexpr int NQC = D / 16;                  // k-steps of the QK product
+    constexpr int NOB = D / 32;                  // 32-channel blocks of the output
+    constexpr int VCPR = BC / 8;                 // 16-byte chunks per V^T row
+    constexpr int VRPB = 256 / (2 * BC);         // V^T rows per 256 bytes (all 64 banks)
+    constexpr int TILE_ELEMS = BC * D;           // bf16 elements of one K or V^T tile
+    constexpr int LOADS = TILE_ELEMS * 2 / 1024 / (NTHREADS / 64);   // 1 KB loads per wave
+    static_assert(LOADS >= 1, "tile smaller than one load per wave");
+    constexpr float kLazy = 16.f;
+    __shared__ __attribute__((aligned(1024))) __bf16 sk0[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) __bf16 sk1[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) __bf16 sv0[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) __bf16 sv1[TILE_ELEMS];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
     const int r32 = lane & 31, hh = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, total);
     const int bh = wg / n_qtiles, qt = wg - bh * n_qtiles;
@@ -56,202 +90,363 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_bf16_kernel(
     const __bf16* Qbh = Q + (int64_t)bh * N * D;
     const __bf16* Kbh = K + (int64_t)bh * N * D;
     const __bf16* Vbh = VT + (int64_t)bh * D * ldv;
-
-    const int q_row = qt * BR + w * 32 + r32;
-    const int q_ld = min(q_row, N - 1);
-    bf16x8 qf[NQC];
-#pragma unroll
-    for (int c = 0; c < NQC; ++c)
-        qf[c] = *reinterpret_cast<const bf16x8*>(Qbh + (int64_t)q_ld * D + 16 * c + 8 * hh);
-
-    floatx16 oacc[NOB];
-#pragma unroll
-    for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) oacc[ob][a] = 0.f;
-    // m: the row maximum used as the exponent offset (base-2 units).  It is raised only
-    // when a tile's maximum exceeds it by more than kLazy, so most tiles skip the
-    // rescale of O; the numerators 2^(t - m) then stay below 2^kLazy.
-    constexpr float kLazy = 8.f;
-    float m = -INFINITY, l = 0.f;
-
     const int nkt = (N + BC - 1) / BC;
-    const int nfull = N / BC;             // tiles with all 64 keys inside the sequence
-    uint4 kreg[KCH], vreg[VCH];
 
-    auto load_full = [&](int kt) {
-        const int k0 = kt * BC;
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / DC, ch = idx % DC;
-            kreg[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)(k0 + row) * D + ch * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / (BC / 8), ch = idx % (BC / 8);
-            vreg[i] = *reinterpret_cast<const uint4*>(Vbh + (int64_t)row * ldv + k0 + ch * 8);
-        }
+    // ---- direct global->LDS loads: lane `lane` of wave w fills tile bytes
+    //      (w*LOADS + i) * 1024 + 16 * lane; the swizzle is inverted on the global side
+    auto k_row = [&](int i) { return ((w * LOADS + i) * 1024 + lane * 16) / (2 * D); };
+    auto k_chunk = [&](int i) {
+        const int off = (w * LOADS + i) * 1024 + lane * 16;
+        return ((off % (2 * D)) / 16) ^ ((off / (2 * D)) % DC);
     };
-    // last, partial tile: keys >= N read as zero (K rows and V^T columns)
-    auto load_tail = [&](int kt) {
-        const int k0 = kt * BC;
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / DC, ch = idx % DC;
-            const int key = k0 + row;
-            kreg[i] = make_uint4(0, 0, 0, 0);
-            if (key < N)
-                kreg[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + ch * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / (BC / 8), ch = idx % (BC / 8);
-            const int key = k0 + ch * 8;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (key < N) {
-                // key < N and key % 8 == 0 keep key + 8 <= ldv (ldv % 16 == 0)
-                v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)row * ldv + key);
-                uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (key + 2 * e >= N) wv[e] = 0;
-                    else if (key + 2 * e + 1 >= N) wv[e] &= 0xFFFFu;
-                }
-                v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-            }
-            vreg[i] = v;
-        }
+    auto v_row = [&](int i) { return ((w * LOADS + i) * 1024 + lane * 16) / (2 * BC); };
+    auto v_chunk = [&](int i) {
+        const int off = (w * LOADS + i) * 1024 + lane * 16;
+        return ((off % (2 * BC)) / 16) ^ (((off / (2 * BC)) / VRPB) % VCPR);
     };
-    auto load_tile = [&](int kt) {
-        if (kt < nfull) load_full(kt);
-        else load_tail(kt);
-    };
-    auto store_tile = [&]() {
+    // per-lane byte offsets of the direct loads (constant over the key loop); the tile
+    // base is wave-uniform, so full tiles need no per-lane address arithmetic
+    uint32_t k_off[LOADS], v_off[LOADS];
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / DC, ch = idx % DC;
-            *reinterpret_cast<uint4*>(&sk[row * D + ((ch ^ (row % DC)) * 8)]) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / (BC / 8), ch = idx % (BC / 8);
-            *reinterpret_cast<uint4*>(&sv[row * BC + ((ch ^ ((row >> 1) & 7)) * 8)]) = vreg[i];
-        }
-    };
-
-    auto tile = [&](int kt) {
-        // S^T for two 32-key blocks
-        floatx16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int krow = kb * 32 + swap_bits23(r32);
-#pragma unroll
-            for (int c = 0; c < NQC; ++c) {
-                const int u = 2 * c + hh;
-                const bf16x8 av =
-                    *reinterpret_cast<const bf16x8*>(&sk[krow * D + ((u ^ (krow % DC)) * 8)]);
-                if (c == 0) {
-                    const floatx16 zero = {};
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], zero, 0, 0, 0);
-                } else {
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[c], s[kb], 0, 0, 0);
-                }
-            }
-        }
-        if (kt >= nfull) {                        // last, partial tile (uniform branch)
-            const int k0 = kt * BC;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    const int key = k0 + kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8);
-                    if (key >= N) s[kb][a] = -INFINITY;
-                }
-        }
-
-        // online softmax in base 2: t = s * c2 with c2 = scale * log2(e)
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[kb][a]);
-        mx = wave_halves_max(mx) * c2;
-        if (__ballot(mx > m + kLazy) != 0) {       // wave-uniform: some row's max grew a lot
-            const float m_new = fmaxf(m, mx);
-            const float alpha = fast_exp2(m - m_new);
-            m = m_new;
-            l *= alpha;
-#pragma unroll
-            for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-                for (int a = 0; a < 16; ++a) oacc[ob][a] *= alpha;
-        }
-
-        bf16x8 pf[4];
-        const float nm = -m;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    floatx2 pr = {fast_exp2(fmaf(s[kb][8 * u + 2 * e], c2, nm)),
-                                  fast_exp2(fmaf(s[kb][8 * u + 2 * e + 1], c2, nm))};
-                    const bf16x2 pb = __builtin_convertvector(pr, bf16x2);
-                    // row sum of the bf16 numerators that feed the P.V product
-                    l = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(__bf16)1.f, (__bf16)1.f}, l,
-                                                        false);
-                    pf[2 * kb + u][2 * e] = pb[0];
-                    pf[2 * kb + u][2 * e + 1] = pb[1];
-                }
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int ob = 0; ob < NOB; ++ob) {
-            const int vrow = ob * 32 + r32;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int u = 2 * t + hh;
-                const bf16x8 av = *reinterpret_cast<const bf16x8*>(
-                    &sv[vrow * BC + ((u ^ ((vrow >> 1) & 7)) * 8)]);
-                oacc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[t], oacc[ob], 0, 0, 0);
-            }
-        }
-    };
-
-    load_tile(0);
-    for (int kt = 0; kt < nkt; ++kt) {
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < nkt) load_tile(kt + 1);
-        tile(kt);
-        __syncthreads();
+    for (int i = 0; i < LOADS; ++i) {
+        k_off[i] = (uint32_t)(k_row(i) * D + k_chunk(i) * 8) * 2u;
+        v_off[i] = (uint32_t)(v_row(i) * (int)ldv + v_chunk(i) * 8) * 2u;
     }
+    auto issue_k = [&](int kt, __bf16* slot) {
+        const int k0 = kt * BC;
+        if (k0 + BC <= N) {
+            const char* base = reinterpret_cast<const char*>(Kbh + (int64_t)k0 * D);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i)
+                global_load_lds16(base + k_off[i], slot + (w * LOADS + i) * 512);
+        } else {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int key = min(k0 + k_row(i), N - 1);     // rows past N: any finite row
+                global_load_lds16(Kbh + (int64_t)key * D + k_chunk(i) * 8,
+                                  slot + (w * LOADS + i) * 512);
+            }
+        }
+    };
+    auto issue_v = [&](int kt, __bf16* slot) {
+        const int k0 = kt * BC;
+        if (k0 + BC <= (int)ldv) {
+            const char* base = reinterpret_cast<const char*>(Vbh + k0);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i)
+                global_load_lds16(base + v_off[i], slot + (w * LOADS + i) * 512);
+        } else {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                // columns past the padded row are clamped into it; the epilogue zeroes
+                // every column >= N of the last tile before it is used
+                const int col = min(k0 + v_chunk(i) * 8, (int)ldv - 8);
+                global_load_lds16(Vbh + (int64_t)v_row(i) * ldv + col,
+                                  slot + (w * LOADS + i) * 512);
+            }
+        }
+    };
+    auto wait_loads_and_sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's direct loads landed
+        __syncthreads();
+    };
 
-    const float l_tot = wave_halves_sum(l);
-    const float inv = 1.f / l_tot;
-    if (q_row < N) {
-        __bf16* orow = O + (((int64_t)b * N + q_row) * H + h) * D;
+    // ---- resident state
+    const int q_base = qt * BR + w * (QB * 32) + r32;     // query row of block 0
+    bf16x8 qf[QB][NQC];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int q_ld = min(q_base + 32 * qb, N - 1);
+#pragma unroll
+        for (int c = 0; c < NQC; ++c)
+            qf[qb][c] =
+                *reinterpret_cast<const bf16x8*>(Qbh + (int64_t)q_ld * D + 16 * c + 8 * hh);
+    }
+    floatx16 oacc[QB][NOB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                floatx4 v = {oacc[ob][4 * j] * inv, oacc[ob][4 * j + 1] * inv,
-                             oacc[ob][4 * j + 2] * inv, oacc[ob][4 * j + 3] * inv};
-                *reinterpret_cast<bf16x4*>(orow + ob * 32 + j * 8 + hh * 4) =
-                    __builtin_convertvector(v, bf16x4);
+            for (int a = 0; a < 16; ++a) oacc[qb][ob][a] = 0.f;
+    // m: row maximum used as the exponent offset (base 2), raised only when a tile's
+    // maximum exceeds it by more than kLazy; l: running row sum (per lane half)
+    float m[QB], l[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m[qb] = -INFINITY;
+        l[qb] = 0.f;
+    }
+
+    // ---- MFMA steps: one LDS operand read shared by QB MFMAs
+    // PV step i = (t, ob): A = V^T rows ob*32.., keys 16t.. of the tile; B = P^T block t.
+    // QK step i = (c, kb): A = K rows kb*32.. (bits 2/3 swapped), channels 16c..; B = Q.
+    constexpr int NPV = 2 * KB * NOB;
+    constexpr int NQK = NQC * KB;
+    auto pv_operand = [&](const __bf16* vs, int i) {
+        const int t = i / NOB, ob = i % NOB;
+        const int vrow = ob * 32 + r32;
+        const int u = 2 * t + hh;
+        return *reinterpret_cast<const bf16x8*>(
+            &vs[vrow * BC + ((u ^ ((vrow / VRPB) % VCPR)) * 8)]);
+    };
+    auto qk_operand = [&](const __bf16* ks, int i) {
+        const int c = i / KB, kb = i % KB;
+        const int krow = kb * 32 + swap_bits23(r32);
+        const int u = 2 * c + hh;
+        return *reinterpret_cast<const bf16x8*>(&ks[krow * D + ((u ^ (krow % DC)) * 8)]);
+    };
+
+    // score and P tiles alternate between two register sets with the iteration parity
+    floatx16 sA[QB][KB], sB[QB][KB];
+    bf16x8 pA[QB][2 * KB], pB[QB][2 * KB];
+
+    auto mfma_pv = [&](int i, const bf16x8& av, const bf16x8 (&pf)[QB][2 * KB]) {
+        const int t = i / NOB, ob = i % NOB;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][ob] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[qb][t], oacc[qb][ob], 0, 0, 0);
+    };
+    auto mfma_qk = [&](int i, const bf16x8& av, floatx16 (&s)[QB][KB]) {
+        const int c = i / KB, kb = i % KB;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (c == 0) {
+                const floatx16 zero = {};
+                s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[qb][c], zero, 0, 0, 0);
+            } else {
+                s[qb][kb] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[qb][c], s[qb][kb], 0, 0, 0);
             }
-        if (LSE != nullptr && hh == 0)
-            LSE[(int64_t)bh * N + q_row] = (m + log2f(l_tot)) * kLn2;
+        }
+    };
+    auto pv_all = [&](const __bf16* vs, const bf16x8 (&pf)[QB][2 * KB]) {
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) mfma_pv(i, pv_operand(vs, i), pf);
+    };
+    auto qk_all = [&](const __bf16* ks, floatx16 (&s)[QB][KB]) {
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) mfma_qk(i, qk_operand(ks, i), s);
+    };
+
+    // ---- softmax pieces
+    auto row_max = [&](floatx16 (&s)[QB][KB], int qb) {
+        float mx = s[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[qb][kb][a]);
+        return wave_halves_max(mx) * c2;
+    };
+    // numerators of a pair of elements: k = ((qb * KB + kb) * 2 + u) * 4 + e covers
+    // accumulator slots 8u + 2e and 8u + 2e + 1 of block (qb, kb)
+    constexpr int NEXP = QB * KB * 8;
+    auto exp_pair = [&](floatx16 (&s)[QB][KB], bf16x8 (&pf)[QB][2 * KB], int k,
+                        const float (&nm)[QB]) {
+        const int e = k % 4, u = (k / 4) % 2, kb = (k / 8) % KB, qb = k / (8 * KB);
+        floatx2 pr = {fast_exp2(fmaf(s[qb][kb][8 * u + 2 * e], c2, nm[qb])),
+                      fast_exp2(fmaf(s[qb][kb][8 * u + 2 * e + 1], c2, nm[qb]))};
+        bf16x2 pb = __builtin_convertvector(pr, bf16x2);
+        // keep the numerators at this point of the schedule (no sinking past the fences)
+        uint32_t pbits = __builtin_bit_cast(uint32_t, pb);
+        asm volatile("" : "+v"(pbits));
+        pb = __builtin_bit_cast(bf16x2, pbits);
+        // the row sum takes the same bf16 numerators that enter P V
+        l[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(__bf16)1.f, (__bf16)1.f}, l[qb],
+                                                false);
+        asm volatile("" : "+v"(l[qb]));
+        pf[qb][2 * kb + u][2 * e] = pb[0];
+        pf[qb][2 * kb + u][2 * e + 1] = pb[1];
+    };
+    auto mask_tail = [&](floatx16 (&s)[QB][KB], int kt) {
+        const int k0 = kt * BC;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int a = 0; a < 16; ++a) {
+                    const int key = k0 + kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8);
+                    if (key >= N) s[qb][kb][a] = -INFINITY;
+                }
+    };
+
+    // prologue: K_0, K_1 -> LDS; S_0
+    issue_k(0, sk0);
+    if (nkt > 1) issue_k(1, sk1);
+    wait_loads_and_sync();
+    qk_all(sk0, sA);
+
+    // iteration j: softmax(S_j) || P_{j-1} V_{j-1} and Q K_{j+1}^T; loads V_j, K_{j+2}
+    auto iteration = [&](int j, auto parity_tag, auto has_pv_tag, auto has_qk_tag) {
+        constexpr int P = decltype(parity_tag)::value;
+        constexpr bool HAS_PV = decltype(has_pv_tag)::value;
+        constexpr bool HAS_QK = decltype(has_qk_tag)::value;
+        __bf16* const my_k = P ? sk1 : sk0;       // K_{j+2} goes here (held K_j)
+        __bf16* const my_v = P ? sv1 : sv0;       // V_j goes here (held V_{j-2})
+        const __bf16* const rd_k = P ? sk0 : sk1; // holds K_{j+1}
+        const __bf16* const rd_v = P ? sv0 : sv1; // holds V_{j-1}
+        floatx16 (&s_in)[QB][KB] = P ? sB : sA;    // S_j
+        floatx16 (&s_out)[QB][KB] = P ? sA : sB;   // S_{j+1}
+        bf16x8 (&p_out)[QB][2 * KB] = P ? pB : pA; // P_j
+        bf16x8 (&p_in)[QB][2 * KB] = P ? pA : pB;  // P_{j-1}
+        if (!HAS_QK && (N % BC) != 0) mask_tail(s_in, j);
+        wait_loads_and_sync();
+        issue_v(j, my_v);
+        if (HAS_QK) issue_k(min(j + 2, nkt - 1), my_k);
+
+        constexpr int S0 = HAS_PV ? 0 : NPV;           // first MFMA step
+        constexpr int S1 = HAS_QK ? NPV + NQK : NPV;   // one past the last step
+        constexpr int NST = S1 - S0;
+        constexpr int LEAD = FWD_LEAD;                 // operand reads run this far ahead
+        constexpr int FIRST = QB + 1;                  // steps before the numerators start
+        float mx[QB], nm[QB], alpha[QB];
+        bool grow[QB];
+        auto decide = [&]() {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                grow[qb] = __ballot(mx[qb] > m[qb] + kLazy) != 0;   // wave-uniform
+                const float m_new = grow[qb] ? fmaxf(m[qb], mx[qb]) : m[qb];
+                alpha[qb] = fast_exp2(m[qb] - m_new);
+                m[qb] = m_new;
+                l[qb] *= alpha[qb];
+                nm[qb] = -m_new;
+            }
+        };
+        // step order: with both products present, PV and QK steps alternate so that
+        // each dependent QK accumulation is separated by an independent PV MFMA
+        auto step_id = [&](int k) -> int {       // returns a PV index (< NPV) or NPV + QK index
+            if constexpr (HAS_PV && HAS_QK) {
+                if constexpr (NPV == NQK) return (k & 1) ? NPV + (k >> 1) : (k >> 1);
+            }
+            return S0 + k;
+        };
+        auto load_op = [&](int st) -> bf16x8 {
+            return st < NPV ? pv_operand(rd_v, st) : qk_operand(rd_k, st - NPV);
+        };
+        if constexpr (NST <= FIRST) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) mx[qb] = row_max(s_in, qb);
+            decide();
+#pragma unroll
+            for (int e = 0; e < NEXP; ++e) exp_pair(s_in, p_out, e, nm);
+            if constexpr (HAS_PV) pv_all(rd_v, p_in);
+            if constexpr (HAS_QK) qk_all(rd_k, s_out);
+        } else {
+            bf16x8 opnd[LEAD + 1];
+#pragma unroll
+            for (int k = 0; k < LEAD; ++k) opnd[k] = load_op(step_id(k));
+#pragma unroll
+            for (int k = 0; k < NST; ++k) {
+                const int st = step_id(k);
+                if (k + LEAD < NST) opnd[(k + LEAD) % (LEAD + 1)] = load_op(step_id(k + LEAD));
+                if (st < NPV) mfma_pv(st, opnd[k % (LEAD + 1)], p_in);
+                else mfma_qk(st - NPV, opnd[k % (LEAD + 1)], s_out);
+                // softmax slice: row maxima, the rescale decision, then numerators
+                if (k < QB) mx[k] = row_max(s_in, k);
+                if (k == QB) decide();
+                if (k >= FIRST) {
+                    const int lo = (k - FIRST) * NEXP / (NST - FIRST);
+                    const int hi = (k - FIRST + 1) * NEXP / (NST - FIRST);
+#pragma unroll
+                    for (int e = lo; e < hi; ++e) exp_pair(s_in, p_out, e, nm);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // O holds P_{j-1} V_{j-1} in the old scale: rescale after those products.  The
+        // rescale is rare; the empty volatile asm keeps the compiler from turning the
+        // branch into unconditional multiplies.
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            if (grow[qb]) {
+                asm volatile("");
+#pragma unroll
+                for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                    for (int a = 0; a < 16; ++a) oacc[qb][ob][a] *= alpha[qb];
+            }
+    };
+
+    using F = std::false_type;
+    using T = std::true_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (nkt == 1) {
+        iteration(0, P0{}, F{}, F{});
+    } else {
+        iteration(0, P0{}, F{}, T{});
+        int j = 1;
+        for (; j + 2 <= nkt - 1; j += 2) {
+            iteration(j, P1{}, T{}, T{});
+            iteration(j + 1, P0{}, T{}, T{});
+        }
+        if (j < nkt - 1) {
+            iteration(j, P1{}, T{}, T{});
+            ++j;
+        }
+        if (j & 1) iteration(j, P1{}, T{}, F{});
+        else iteration(j, P0{}, T{}, F{});
+    }
+
+    // epilogue: P_last V_last; columns >= N of the last V^T tile are zeroed first
+    {
+        const int jl = nkt - 1;
+        __bf16* const vs = (jl & 1) ? sv1 : sv0;
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        if ((N % BC) != 0) {
+            const int k0 = jl * BC;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int c0 = k0 + v_chunk(i) * 8;
+                if (c0 + 8 > N) {
+                    __bf16* p = vs + (w * LOADS + i) * 512 + lane * 8;
+                    uint4 v = *reinterpret_cast<uint4*>(p);
+                    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (c0 + 2 * e >= N) wv[e] = 0;
+                        else if (c0 + 2 * e + 1 >= N) wv[e] &= 0xFFFFu;
+                    }
+                    *reinterpret_cast<uint4*>(p) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                }
+            }
+        }
+        __syncthreads();
+        if (jl & 1) pv_all(vs, pB);
+        else pv_all(vs, pA);
+    }
+
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = wave_halves_sum(l[qb]);
+        const float inv = 1.f / l_tot;
+        const int q_row = q_base + 32 * qb;
+        if (q_row < N) {
+            __bf16* orow = O + (((int64_t)b * N + q_row) * H + h) * D;
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    floatx4 v = {oacc[qb][ob][4 * j] * inv, oacc[qb][ob][4 * j + 1] * inv,
+                                 oacc[qb][ob][4 * j + 2] * inv, oacc[qb][ob][4 * j + 3] * inv};
+                    *reinterpret_cast<bf16x4*>(orow + ob * 32 + j * 8 + hh * 4) =
+                        __builtin_convertvector(v, bf16x4);
+                }
+            if (LSE != nullptr && hh == 0)
+                LSE[(int64_t)bh * N + q_row] = (m[qb] + log2f(l_tot)) * kLn2;
+        }
     }
 }
 
-template <int D>
+template <int D, int QB, int BC>
 hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, int N,
                     int64_t ldv, float softmax_scale, void* o, float* lse, hipStream_t stream) {
+    constexpr int BR = 4 * QB * 32;
     const int n_qtiles = (N + BR - 1) / BR;
     const int total = n_qtiles * B * H;
-    hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(total), dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC>), dim3(total), dim3(NTHREADS), 0, stream,
                        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                        static_cast<const __bf16*>(vt), H, N, ldv, softmax_scale * kLog2e,
                        static_cast<__bf16*>(o), lse, n_qtiles, total);
@@ -263,8 +458,8 @@ hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, int H, int N,
                            int D, int64_t ldv, float softmax_scale, void* o, float* lse,
                            hipStream_t stream) {
-    return D == 64 ? launch_d<64>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse, stream)
-                   : launch_d<128>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse, stream);
+    return D == 64 ? launch_d<64, FWD_QB, FWD_BC>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse, stream)
+                   : launch_d<128, FWD_QB, FWD_BC>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse, stream);
 }
 
 }  // namespace ja
