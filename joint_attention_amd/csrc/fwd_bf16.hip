@@ -24,17 +24,19 @@
 //
 // Software pipeline.  Iteration j runs the softmax of tile j on the vector ALU while
 // the matrix cores run P(j-1) V(j-1) and Q K(j+1)^T; the three are independent, and
-// the loop body is written as an explicit sequence of steps (one LDS operand read, two
-// MFMAs and a slice of the softmax each) separated by scheduling fences.  K and V^T
-// tiles are double-buffered in LDS and filled by direct global->LDS 16-byte loads
-// (lane l's 16 bytes land at base + 16 l), one tile ahead; one barrier per iteration.
+// the loop body is written as an explicit sequence of steps (one LDS operand read, one
+// or two MFMAs and a slice of the softmax each) separated by scheduling fences.  K and
+// V^T tiles are double-buffered in LDS; each lane stages one 16-byte chunk per tile in
+// registers a full iteration ahead and writes it to LDS after the iteration's single
+// barrier (direct global->LDS loads would force every LDS-operand wait to drain them).
 // Chunks are XOR-swizzled by row so that the 16-byte operand reads of 16 consecutive
 // lanes (16 different rows) hit distinct banks; the swizzle is applied on the global
-// side of the direct loads.
+// side of the loads, so each LDS store is a linear 16-byte write.
 //
 // Softmax details.  Scores are scaled to base 2 (c2 = scale * log2 e) in the FMA that
-// subtracts the running maximum m.  m is raised only when a tile's maximum exceeds it
-// by more than 16, so O is rescaled rarely; the numerators stay below 2^16.  The row
+// subtracts the running offset m.  m is raised (to the exact row maximum, combining the
+// two lane halves) only when some lane's own maximum exceeds it by more than 16, so the
+// cross-lane step and the rescale of O are rare; the numerators stay below 2^16.  The row
 // sum accumulates the bf16-rounded numerators with v_dot2 (the same values that
 // enter P V).
 #include <type_traits>
@@ -45,7 +47,9 @@
 namespace ja {
 namespace {
 
-constexpr int NTHREADS = 256;    // 4 waves, one query slice each
+#ifndef FWD_NW
+#define FWD_NW 8
+#endif
 #ifndef FWD_QB
 #define FWD_QB 1
 #endif
@@ -58,14 +62,16 @@ constexpr int NTHREADS = 256;    // 4 waves, one query slice each
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-// QB: 32-row query blocks per wave; BC: keys per tile.  QB = 2 runs one wave per SIMD
-// with the whole register file; QB = 1 runs two workgroups per CU.
-template <int D, int QB, int BC>
-__global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
+// NW: waves per workgroup (each owns QB 32-row query blocks); BC: keys per tile.  With
+// NW * QB = 8 one workgroup covers 256 query rows, so every K/V tile loaded into LDS
+// serves 256 rows, and two waves share each SIMD.
+template <int D, int NW, int QB, int BC>
+__global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ VT,
     int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE,
     int n_qtiles, int total) {
-    constexpr int BR = 4 * QB * 32;              // query rows per workgroup
+    constexpr int NTHREADS = NW * 64;
+    constexpr int BR = NW * QB * 32;             // query rows per workgroup
     constexpr int KB = BC / 32;                  // 32-key blocks per tile
     constexpr int DC = D / 8;                    // 16-byte chunks per K row
     constexpr int NQC = D / 16;                  // k-steps of the QK product
@@ -92,8 +98,9 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
     const __bf16* Vbh = VT + (int64_t)bh * D * ldv;
     const int nkt = (N + BC - 1) / BC;
 
-    // ---- direct global->LDS loads: lane `lane` of wave w fills tile bytes
-    //      (w*LOADS + i) * 1024 + 16 * lane; the swizzle is inverted on the global side
+    // ---- K / V^T tile loads, staged through registers: lane `lane` of wave w owns
+    //      tile bytes (w*LOADS + i) * 1024 + 16 * lane; the swizzle is inverted on the
+    //      global side, so the LDS store is one linear 16-byte write per chunk
     auto k_row = [&](int i) { return ((w * LOADS + i) * 1024 + lane * 16) / (2 * D); };
     auto k_chunk = [&](int i) {
         const int off = (w * LOADS + i) * 1024 + lane * 16;
@@ -104,51 +111,65 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
         const int off = (w * LOADS + i) * 1024 + lane * 16;
         return ((off % (2 * BC)) / 16) ^ (((off / (2 * BC)) / VRPB) % VCPR);
     };
-    // per-lane byte offsets of the direct loads (constant over the key loop); the tile
-    // base is wave-uniform, so full tiles need no per-lane address arithmetic
     uint32_t k_off[LOADS], v_off[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         k_off[i] = (uint32_t)(k_row(i) * D + k_chunk(i) * 8) * 2u;
         v_off[i] = (uint32_t)(v_row(i) * (int)ldv + v_chunk(i) * 8) * 2u;
     }
-    auto issue_k = [&](int kt, __bf16* slot) {
+    uint4 kst[LOADS], vst[LOADS];                 // staged tiles (global -> registers)
+    auto load_k = [&](int kt) {
         const int k0 = kt * BC;
         if (k0 + BC <= N) {
             const char* base = reinterpret_cast<const char*>(Kbh + (int64_t)k0 * D);
 #pragma unroll
             for (int i = 0; i < LOADS; ++i)
-                global_load_lds16(base + k_off[i], slot + (w * LOADS + i) * 512);
+                kst[i] = *reinterpret_cast<const uint4*>(base + k_off[i]);
         } else {
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
                 const int key = min(k0 + k_row(i), N - 1);     // rows past N: any finite row
-                global_load_lds16(Kbh + (int64_t)key * D + k_chunk(i) * 8,
-                                  slot + (w * LOADS + i) * 512);
+                kst[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + k_chunk(i) * 8);
             }
         }
     };
-    auto issue_v = [&](int kt, __bf16* slot) {
+    auto load_v = [&](int kt) {
         const int k0 = kt * BC;
-        if (k0 + BC <= (int)ldv) {
+        if (k0 + BC <= N) {
             const char* base = reinterpret_cast<const char*>(Vbh + k0);
 #pragma unroll
             for (int i = 0; i < LOADS; ++i)
-                global_load_lds16(base + v_off[i], slot + (w * LOADS + i) * 512);
+                vst[i] = *reinterpret_cast<const uint4*>(base + v_off[i]);
         } else {
+            // last tile: columns >= N read as zero (the row may be padded with anything)
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
-                // columns past the padded row are clamped into it; the epilogue zeroes
-                // every column >= N of the last tile before it is used
-                const int col = min(k0 + v_chunk(i) * 8, (int)ldv - 8);
-                global_load_lds16(Vbh + (int64_t)v_row(i) * ldv + col,
-                                  slot + (w * LOADS + i) * 512);
+                const int c0 = k0 + v_chunk(i) * 8;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (c0 < N) {
+                    // c0 < N, c0 % 8 == 0 and ldv % 16 == 0 keep c0 + 8 <= ldv
+                    v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)v_row(i) * ldv + c0);
+                    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (c0 + 2 * e >= N) wv[e] = 0;
+                        else if (c0 + 2 * e + 1 >= N) wv[e] &= 0xFFFFu;
+                    }
+                    v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                }
+                vst[i] = v;
             }
         }
     };
-    auto wait_loads_and_sync = [&]() {
-        __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's direct loads landed
-        __syncthreads();
+    auto store_k = [&](__bf16* slot) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            *reinterpret_cast<uint4*>(slot + (w * LOADS + i) * 512 + lane * 8) = kst[i];
+    };
+    auto store_v = [&](__bf16* slot) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            *reinterpret_cast<uint4*>(slot + (w * LOADS + i) * 512 + lane * 8) = vst[i];
     };
 
     // ---- resident state
@@ -243,7 +264,7 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
     // accumulator slots 8u + 2e and 8u + 2e + 1 of block (qb, kb)
     constexpr int NEXP = QB * KB * 8;
     auto exp_pair = [&](floatx16 (&s)[QB][KB], bf16x8 (&pf)[QB][2 * KB], int k,
-                        const float (&nm)[QB]) {
+                        const float (&nm)[QB], float (&sum)[QB]) {
         const int e = k % 4, u = (k / 4) % 2, kb = (k / 8) % KB, qb = k / (8 * KB);
         floatx2 pr = {fast_exp2(fmaf(s[qb][kb][8 * u + 2 * e], c2, nm[qb])),
                       fast_exp2(fmaf(s[qb][kb][8 * u + 2 * e + 1], c2, nm[qb]))};
@@ -253,9 +274,9 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
         asm volatile("" : "+v"(pbits));
         pb = __builtin_bit_cast(bf16x2, pbits);
         // the row sum takes the same bf16 numerators that enter P V
-        l[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(__bf16)1.f, (__bf16)1.f}, l[qb],
-                                                false);
-        asm volatile("" : "+v"(l[qb]));
+        sum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pb, bf16x2{(__bf16)1.f, (__bf16)1.f}, sum[qb],
+                                                  false);
+        asm volatile("" : "+v"(sum[qb]));
         pf[qb][2 * kb + u][2 * e] = pb[0];
         pf[qb][2 * kb + u][2 * e + 1] = pb[1];
     };
@@ -272,11 +293,17 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
                 }
     };
 
-    // prologue: K_0, K_1 -> LDS; S_0
-    issue_k(0, sk0);
-    if (nkt > 1) issue_k(1, sk1);
-    wait_loads_and_sync();
+    // prologue: K_0, K_1 -> LDS; S_0; stage K_2 and V_0
+    load_k(0);
+    store_k(sk0);
+    if (nkt > 1) {
+        load_k(1);
+        store_k(sk1);
+    }
+    __syncthreads();
     qk_all(sk0, sA);
+    load_k(min(2, nkt - 1));
+    load_v(0);
 
     // iteration j: softmax(S_j) || P_{j-1} V_{j-1} and Q K_{j+1}^T; loads V_j, K_{j+2}
     auto iteration = [&](int j, auto parity_tag, auto has_pv_tag, auto has_qk_tag) {
@@ -292,27 +319,42 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
         bf16x8 (&p_out)[QB][2 * KB] = P ? pB : pA; // P_j
         bf16x8 (&p_in)[QB][2 * KB] = P ? pA : pB;  // P_{j-1}
         if (!HAS_QK && (N % BC) != 0) mask_tail(s_in, j);
-        wait_loads_and_sync();
-        issue_v(j, my_v);
-        if (HAS_QK) issue_k(min(j + 2, nkt - 1), my_k);
+        __syncthreads();
+        // the staged K_{j+2} and V_j go to the slots freed by the barrier; then stage
+        // K_{j+3} and V_{j+1} (indices past the end reload the last tile, unused)
+        if (HAS_QK) store_k(my_k);
+        store_v(my_v);
+        if (HAS_QK) load_k(min(j + 3, nkt - 1));
+        load_v(min(j + 1, nkt - 1));
 
         constexpr int S0 = HAS_PV ? 0 : NPV;           // first MFMA step
         constexpr int S1 = HAS_QK ? NPV + NQK : NPV;   // one past the last step
         constexpr int NST = S1 - S0;
         constexpr int LEAD = FWD_LEAD;                 // operand reads run this far ahead
-        constexpr int FIRST = QB + 1;                  // steps before the numerators start
-        float mx[QB], nm[QB], alpha[QB];
+        // Offset update.  Each lane first takes the maximum of its own scores only; the
+        // wave raises m (exact maximum over both lane halves, rescale of l now and of O
+        // after this iteration's P V products) only if some lane's maximum exceeds m by
+        // more than kLazy -- a uniform branch that is rarely taken after the first tile.
+        constexpr int FIRST = QB;                      // steps before the numerators start
+        float nm[QB], alpha[QB];
         bool grow[QB];
-        auto decide = [&]() {
+        auto check = [&](int qb) {
+            float mx = s_in[qb][0][0];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                grow[qb] = __ballot(mx[qb] > m[qb] + kLazy) != 0;   // wave-uniform
-                const float m_new = grow[qb] ? fmaxf(m[qb], mx[qb]) : m[qb];
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s_in[qb][kb][a]);
+            grow[qb] = __ballot(mx * c2 > m[qb] + kLazy) != 0;   // wave-uniform
+            alpha[qb] = 1.f;
+            if (grow[qb]) {
+                asm volatile("");
+                const float mrow = wave_halves_max(mx) * c2;
+                const float m_new = fmaxf(m[qb], mrow);
                 alpha[qb] = fast_exp2(m[qb] - m_new);
                 m[qb] = m_new;
                 l[qb] *= alpha[qb];
-                nm[qb] = -m_new;
             }
+            nm[qb] = -m[qb];
         };
         // step order: with both products present, PV and QK steps alternate so that
         // each dependent QK accumulation is separated by an independent PV MFMA
@@ -327,10 +369,9 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
         };
         if constexpr (NST <= FIRST) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) mx[qb] = row_max(s_in, qb);
-            decide();
+            for (int qb = 0; qb < QB; ++qb) check(qb);
 #pragma unroll
-            for (int e = 0; e < NEXP; ++e) exp_pair(s_in, p_out, e, nm);
+            for (int e = 0; e < NEXP; ++e) exp_pair(s_in, p_out, e, nm, l);
             if constexpr (HAS_PV) pv_all(rd_v, p_in);
             if constexpr (HAS_QK) qk_all(rd_k, s_out);
         } else {
@@ -343,21 +384,18 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
                 if (k + LEAD < NST) opnd[(k + LEAD) % (LEAD + 1)] = load_op(step_id(k + LEAD));
                 if (st < NPV) mfma_pv(st, opnd[k % (LEAD + 1)], p_in);
                 else mfma_qk(st - NPV, opnd[k % (LEAD + 1)], s_out);
-                // softmax slice: row maxima, the rescale decision, then numerators
-                if (k < QB) mx[k] = row_max(s_in, k);
-                if (k == QB) decide();
+                // softmax slice: offset check first, then numerators
+                if (k < QB) check(k);
                 if (k >= FIRST) {
                     const int lo = (k - FIRST) * NEXP / (NST - FIRST);
                     const int hi = (k - FIRST + 1) * NEXP / (NST - FIRST);
 #pragma unroll
-                    for (int e = lo; e < hi; ++e) exp_pair(s_in, p_out, e, nm);
+                    for (int e = lo; e < hi; ++e) exp_pair(s_in, p_out, e, nm, l);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // O holds P_{j-1} V_{j-1} in the old scale: rescale after those products.  The
-        // rescale is rare; the empty volatile asm keeps the compiler from turning the
-        // branch into unconditional multiplies.
+        // O holds P_{j-1} V_{j-1} in the old scale: rescale after those products
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
             if (grow[qb]) {
@@ -390,29 +428,10 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
         else iteration(j, P0{}, T{}, F{});
     }
 
-    // epilogue: P_last V_last; columns >= N of the last V^T tile are zeroed first
+    // epilogue: P_last V_last (V_last was stored in the last iteration)
     {
         const int jl = nkt - 1;
         __bf16* const vs = (jl & 1) ? sv1 : sv0;
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        if ((N % BC) != 0) {
-            const int k0 = jl * BC;
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int c0 = k0 + v_chunk(i) * 8;
-                if (c0 + 8 > N) {
-                    __bf16* p = vs + (w * LOADS + i) * 512 + lane * 8;
-                    uint4 v = *reinterpret_cast<uint4*>(p);
-                    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (c0 + 2 * e >= N) wv[e] = 0;
-                        else if (c0 + 2 * e + 1 >= N) wv[e] &= 0xFFFFu;
-                    }
-                    *reinterpret_cast<uint4*>(p) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                }
-            }
-        }
         __syncthreads();
         if (jl & 1) pv_all(vs, pB);
         else pv_all(vs, pA);
@@ -440,13 +459,13 @@ __global__ __launch_bounds__(NTHREADS, 2 / QB) void fwd_bf16_kernel(
     }
 }
 
-template <int D, int QB, int BC>
+template <int D, int NW, int QB, int BC>
 hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, int N,
                     int64_t ldv, float softmax_scale, void* o, float* lse, hipStream_t stream) {
-    constexpr int BR = 4 * QB * 32;
+    constexpr int BR = NW * QB * 32;
     const int n_qtiles = (N + BR - 1) / BR;
     const int total = n_qtiles * B * H;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, BC>), dim3(total), dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BC>), dim3(total), dim3(NW * 64), 0, stream,
                        static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                        static_cast<const __bf16*>(vt), H, N, ldv, softmax_scale * kLog2e,
                        static_cast<__bf16*>(o), lse, n_qtiles, total);
@@ -458,8 +477,11 @@ hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, int H, int N,
                            int D, int64_t ldv, float softmax_scale, void* o, float* lse,
                            hipStream_t stream) {
-    return D == 64 ? launch_d<64, FWD_QB, FWD_BC>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse, stream)
-                   : launch_d<128, FWD_QB, FWD_BC>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse, stream);
+    // head size 64 (4 KB tiles) keeps 4 waves so that each wave still moves whole 1 KB loads
+    return D == 64
+        ? launch_d<64, 4, FWD_QB, FWD_BC>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse, stream)
+        : launch_d<128, FWD_NW, FWD_QB, FWD_BC>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse,
+                                                stream);
 }
 
 }  // namespace ja
