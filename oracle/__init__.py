@@ -13,13 +13,15 @@ never imports the product path; the two share no code.
 """
 from .pack import stream_offsets, pack_tokens, to_bhnd, to_bhdn
 from .attention import attention, attention_rows, all_rows, widen_bf16
-from .fp8 import (E4M3_MAX, QK_BLOCK, P_SCALE_LOG2, e4m3_encode, e4m3_decode,
-                  quantise_qk, quantise_v, fp8_attention_rows)
+from .fp8 import (E4M3_MAX, QK_BLOCK, P_SCALE_LOG2, HI_CHANNELS, e4m3_encode, e4m3_decode,
+                  pow2_scale, quantise_qk, quantise_v, select_hi_channels, quantise_qk_split,
+                  fp8_attention_rows)
 from ._native import build, default_threads
 
 __all__ = [
     "stream_offsets", "pack_tokens", "to_bhnd", "to_bhdn",
     "attention", "attention_rows", "all_rows", "widen_bf16",
-    "E4M3_MAX", "QK_BLOCK", "P_SCALE_LOG2", "e4m3_encode", "e4m3_decode",
-    "quantise_qk", "quantise_v", "fp8_attention_rows", "build", "default_threads",
+    "E4M3_MAX", "QK_BLOCK", "P_SCALE_LOG2", "HI_CHANNELS", "e4m3_encode", "e4m3_decode",
+    "pow2_scale", "quantise_qk", "quantise_v", "select_hi_channels", "quantise_qk_split",
+    "fp8_attention_rows", "build", "default_threads",
 ]

@@ -11,12 +11,21 @@ plainest reading of those two facts:
     subnormal step 2**-9, largest finite 448, no infinities; S.1111.111 is NaN);
   * Q and K: one scale per (b, h, block of 128 consecutive packed tokens);
   * V: one scale per (b, h, channel) over all tokens;
-  * scale = amax / 448 and codes = e4m3(clamp(x * (448 / amax), -448, 448)), with
-    amax, both quotients and the product in binary32 (round to nearest even) and the
-    e4m3 rounding also to nearest even; amax == 0 gives scale 1 and all-zero codes;
+  * every scale is a power of two, as the shared scales of the OCP Microscaling (MX)
+    formats are: scale = 2**k with k the smallest integer such that amax <= 448 * 2**k
+    (k >= -126; amax == 0 gives scale 1), so x / scale is exact and
+    codes = e4m3(x / scale) with e4m3 rounding to nearest even (|x / scale| <= 448);
   * P: the softmax numerators, taken relative to an integer row maximum in base 2
     and multiplied by 2**8, are rounded to e4m3 before the P.V product; the row sum
     uses the unrounded numerators.
+
+A second, corrected mode keeps R = 16 channels of Q and K per (b, h) out of the e4m3
+product: the channels with the largest amax(|q_c|) * amax(|k_c|) over all tokens (ties:
+lower index).  Their exact bf16 values, divided by the block scale (exact, the scale
+being a power of two), enter the same logit accumulation; their e4m3 codes are zero.
+This is the residual-correction idea of the article's VC-Attention remark (section
+量化注意力与稀疏注意力: the part of the input with the largest quantisation error gets a
+correction) applied to whole channels, where activation outliers live.
 
 Scales are dequantisation multipliers: x ~= decode(code) * scale.
 """
@@ -29,6 +38,7 @@ import numpy as np
 E4M3_MAX = 448.0
 QK_BLOCK = 128          # tokens per Q/K scale block
 P_SCALE_LOG2 = 8        # P is stored as e4m3(2**8 * p)
+HI_CHANNELS = 16        # channels of Q and K kept out of e4m3 in the corrected mode
 
 
 # --------------------------------------------------------------------- the format
@@ -72,13 +82,16 @@ def _widen_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _scales_from_amax(amax: np.ndarray):
-    amax = amax.astype(np.float32)
-    zero = amax == 0
-    safe = np.where(zero, np.float32(1), amax)
-    scale = np.where(zero, np.float32(1), safe / np.float32(E4M3_MAX)).astype(np.float32)
-    inv = np.where(zero, np.float32(1), np.float32(E4M3_MAX) / safe).astype(np.float32)
-    return scale, inv
+def pow2_scale(amax) -> np.ndarray:
+    """Smallest power of two s (>= 2**-126) with amax <= 448 * s; 1 where amax == 0.
+
+    amax = f * 2**E with f in [0.5, 1): 448 * 2**(E-9) = 0.875 * 2**E, so k = E - 9 when
+    amax <= 0.875 * 2**E and E - 8 otherwise (all comparisons exact in float64)."""
+    a = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(a)
+    k = np.where(f <= 0.875, E - 9, E - 8)
+    k = np.maximum(k, -126)
+    return np.where(a == 0, 1.0, np.ldexp(1.0, k)).astype(np.float32)
 
 
 def quantise_qk(x_tok: np.ndarray, block: int = QK_BLOCK):
@@ -91,28 +104,57 @@ def quantise_qk(x_tok: np.ndarray, block: int = QK_BLOCK):
     scales = np.empty((B, H, nblk), dtype=np.float32)
     for blk in range(nblk):
         lo, hi = blk * block, min(N, (blk + 1) * block)
-        xb = x[:, lo:hi]                                   # [B, t, H, D]
-        amax = np.abs(xb).max(axis=(1, 3))                 # [B, H]
-        scale, inv = _scales_from_amax(amax)
+        xb = x[:, lo:hi].astype(np.float64)                # [B, t, H, D]
+        scale = pow2_scale(np.abs(xb).max(axis=(1, 3)))    # [B, H]
         scales[:, :, blk] = scale
-        y = (xb * inv[:, None, :, None]).astype(np.float32)   # binary32 product
-        codes[:, lo:hi] = e4m3_encode(y)
+        codes[:, lo:hi] = e4m3_encode(xb / scale.astype(np.float64)[:, None, :, None])
     return codes, scales
 
 
 def quantise_v(x_tok: np.ndarray):
     """V, token-major [B, N, H, D] bf16 bits -> (codes [B, N, H, D] uint8,
     scales [B, H, D] float32), one scale per channel over all tokens."""
-    x = _widen_f32(x_tok)
-    amax = np.abs(x).max(axis=1)                            # [B, H, D]
-    scale, inv = _scales_from_amax(amax)
-    y = (x * inv[:, None, :, :]).astype(np.float32)
-    return e4m3_encode(y), scale
+    x = _widen_f32(x_tok).astype(np.float64)
+    scale = pow2_scale(np.abs(x).max(axis=1))               # [B, H, D]
+    return e4m3_encode(x / scale.astype(np.float64)[:, None, :, :]), scale
+
+
+def select_hi_channels(q_tok: np.ndarray, k_tok: np.ndarray, r: int = HI_CHANNELS):
+    """Per (b, h): the r channels with the largest amax(|q_c|) * amax(|k_c|) over all
+    tokens (ties to the lower index), in ascending channel order -> int32 [B, H, r]."""
+    qa = np.abs(_widen_f32(q_tok).astype(np.float64)).max(axis=1)     # [B, H, D]
+    ka = np.abs(_widen_f32(k_tok).astype(np.float64)).max(axis=1)
+    score = qa * ka                                     # exact: bf16 * bf16
+    B, H, D = score.shape
+    sel = np.empty((B, H, r), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            order = sorted(range(D), key=lambda c: (-score[b, h, c], c))[:r]
+            sel[b, h] = sorted(order)
+    return sel
+
+
+def quantise_qk_split(x_tok: np.ndarray, sel: np.ndarray, block: int = QK_BLOCK):
+    """Corrected mode: e4m3 codes as quantise_qk with the selected channels' codes set to
+    zero, plus their exact values divided by the block scale -> (codes [B, N, H, D],
+    scales [B, H, nblk], hi [B, N, H, r] float64)."""
+    codes, scales = quantise_qk(x_tok, block)
+    x = _widen_f32(x_tok).astype(np.float64)
+    B, N, H, D = x.shape
+    r = sel.shape[2]
+    blk_of = np.arange(N) // block
+    hi = np.empty((B, N, H, r))
+    for b in range(B):
+        for h in range(H):
+            codes[b, :, h, sel[b, h]] = 0
+            s_tok = scales[b, h, blk_of].astype(np.float64)
+            hi[b, :, h, :] = x[b][:, h, sel[b, h]] / s_tok[:, None]
+    return codes, scales, hi
 
 
 # --------------------------------------------------------------------- fp8 attention
 def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: float, sel,
-                       block: int = QK_BLOCK):
+                       block: int = QK_BLOCK, q_hi=None, k_hi=None):
     """Attention on the fp8 operands, selected rows (b, h, i).
 
     For each row, in float64 with exactly dequantised operands:
@@ -123,7 +165,9 @@ def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: flo
         O[c] = (sum_j P_j * v_j[c]) / (2**8 * sum_j p_j)
         lse  = (M + log2 sum_j p_j) * ln 2
     q8/k8/v8 are token-major [B, N, H, D] codes; q_scale/k_scale [B, H, nblk];
-    v_scale [B, H, D].  Returns (O [n, D], lse [n]).
+    v_scale [B, H, D].  In the corrected mode q_hi/k_hi [B, N, H, r] hold the kept
+    channels divided by their block scale and add (q_hi . k_hi) * qs * ks to the dot
+    product.  Returns (O [n, D], lse [n]).
     """
     B, N, H, D = q8.shape
     sel = np.asarray(sel, dtype=np.int64).reshape(-1, 3)
@@ -134,12 +178,18 @@ def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: flo
     for r, (b, h, i) in enumerate(sel):
         key = (int(b), int(h))
         if key not in cache:
-            kd = e4m3_decode(k8[b, :, h, :]) * k_scale[b, h, blk_of][:, None].astype(np.float64)
+            ks_tok = k_scale[b, h, blk_of].astype(np.float64)
+            kd = e4m3_decode(k8[b, :, h, :]) * ks_tok[:, None]
             vd = e4m3_decode(v8[b, :, h, :]) * v_scale[b, h][None, :].astype(np.float64)
-            cache = {key: (kd, vd)}                       # keep one (b, h) at a time
-        kd, vd = cache[key]
-        qd = e4m3_decode(q8[b, i, h, :]) * float(q_scale[b, h, i // block])
-        t = (kd @ qd) * (softmax_scale / math.log(2.0))
+            kh = None if k_hi is None else k_hi[b, :, h, :] * ks_tok[:, None]
+            cache = {key: (kd, vd, kh)}                   # keep one (b, h) at a time
+        kd, vd, kh = cache[key]
+        qs = float(q_scale[b, h, i // block])
+        qd = e4m3_decode(q8[b, i, h, :]) * qs
+        dots = kd @ qd
+        if kh is not None:
+            dots = dots + kh @ (q_hi[b, i, h, :] * qs)
+        t = dots * (softmax_scale / math.log(2.0))
         M = math.ceil(t.max())
         p = np.exp2(t - M)
         P = e4m3_decode(e4m3_encode(p * 2.0 ** P_SCALE_LOG2))

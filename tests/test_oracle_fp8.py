@@ -93,26 +93,38 @@ def test_quantise_qk_blocks_follow_packed_tokens():
     for b in range(2):
         for h in range(3):
             for blk, (lo, hi) in enumerate([(0, 128), (128, 130)]):
-                amax = np.float32(np.abs(xw[b, lo:hi, h]).max())
-                assert scales[b, h, blk] == np.float32(amax / np.float32(448))
-    # the block's largest element lands on +-448
+                amax = np.abs(xw[b, lo:hi, h]).max()
+                sc = float(scales[b, h, blk])
+                assert sc == 2.0 ** round(math.log2(sc))          # a power of two
+                assert amax <= 448 * sc and amax > 224 * sc       # the smallest that fits
+    # the block's largest element lands in (224, 448]
     top = np.abs(xw[1, 128:, 2]).argmax()
-    assert (codes[1, 128:, 2].ravel()[top] & 0x7F) == 0x7E
+    assert (codes[1, 128:, 2].ravel()[top] & 0x7F) >= 0x76            # 224 = 0x76
     deq = oracle.e4m3_decode(codes) * np.repeat(scales, [128, 2], axis=2).transpose(0, 2, 1)[..., None]
     rel = np.abs(deq - xw) / np.maximum(np.abs(xw), 1e-30)
     assert rel[np.abs(xw) > np.repeat(scales, [128, 2], axis=2).transpose(0, 2, 1)[..., None] * 2 ** -6].max() <= 2 ** -4
+
+
+def test_pow2_scale_hand_values():
+    # smallest power of two s with amax <= 448 s: 448 -> 1, 449 -> 2, 7 = 448/64 -> 2^-6,
+    # 7.01 -> 2^-5, 1 -> 2^-8 (448/256 = 1.75 >= 1 > 448/512), 0.875 = 448/512 -> 2^-9,
+    # 0 -> 1, a denormal -> 2^-126 (the floor)
+    amax = [448.0, 449.0, 7.0, 7.01, 1.0, 0.875, 0.0, 1e-45]
+    want = [1.0, 2.0, 2.0 ** -6, 2.0 ** -5, 2.0 ** -8, 2.0 ** -9, 1.0, 2.0 ** -126]
+    assert oracle.pow2_scale(np.array(amax)).tolist() == [np.float32(w) for w in want]
 
 
 def test_quantise_zero_block_and_channel():
     x = np.zeros((1, 4, 1, 3), np.float32)
     x[0, :, 0, 1] = [1.0, -2.0, 0.5, 0.25]
     codes, scales = oracle.quantise_qk(_bits(x))
-    assert scales[0, 0, 0] == np.float32(2.0 / 448.0)
+    assert scales[0, 0, 0] == np.float32(2.0 ** -7)           # 2 <= 448 * 2^-7 = 3.5
     vcodes, vscales = oracle.quantise_v(_bits(x))
-    assert vscales[0, 0].tolist() == [1.0, np.float32(2.0 / 448.0), 1.0]   # amax 0 -> 1
+    assert vscales[0, 0].tolist() == [1.0, 2.0 ** -7, 1.0]    # amax 0 -> 1
     assert (vcodes[0, :, 0, 0] == 0).all() and (vcodes[0, :, 0, 2] == 0).all()
-    # channel 1: -2 -> -448 (0xFE), 1 -> 224 (0x76)
-    assert vcodes[0, 1, 0, 1] == 0xFE and vcodes[0, 0, 0, 1] == 0x76
+    # channel 1: -2 / 2^-7 = -256 -> 0xF8; 1 -> 128 -> 0x70; 0.5 -> 64 -> 0x68
+    assert vcodes[0, 1, 0, 1] == 0xF8 and vcodes[0, 0, 0, 1] == 0x70
+    assert vcodes[0, 2, 0, 1] == 0x68
 
 
 def test_fp8_attention_hand_case():
@@ -211,3 +223,55 @@ def test_fp8_attention_uses_each_rows_block_scales():
     o64, l64 = oracle.attention_rows(qv, kv, vd, math.log(2.0), sel)
     np.testing.assert_allclose(o8, o64, rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(l8, l64, rtol=1e-14)
+
+
+def test_select_hi_channels_hand_case():
+    # channel scores amax|q| * amax|k|: c0 = 1*1, c1 = 8*8 (outlier), c2 = 2*3, c3 = 3*2 (tie
+    # with c2: lower index wins); r = 2 keeps {1, 2}
+    q = np.zeros((1, 3, 1, 4), np.float32)
+    k = np.zeros((1, 3, 1, 4), np.float32)
+    q[0, :, 0, :] = [[1, -8, 2, 3], [0.5, 4, -1, 1], [0, 1, 1, -2]]
+    k[0, :, 0, :] = [[1, 1, 3, -2], [-0.5, 8, 1, 1], [0, 1, 1, 1]]
+    assert oracle.select_hi_channels(_bits(q), _bits(k), r=2).tolist() == [[[1, 2]]]
+
+
+def test_quantise_split_zeroes_codes_and_keeps_exact_values():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((1, 130, 2, 8)).astype(np.float32)
+    sel = np.array([[[1, 5], [0, 7]]], np.int32)
+    bits = _bits(x)
+    codes, scales, hi = oracle.quantise_qk_split(bits, sel)
+    c0, s0 = oracle.quantise_qk(bits)
+    assert np.array_equal(scales, s0)
+    xw = oracle.widen_bf16(bits)
+    for h in range(2):
+        others = [c for c in range(8) if c not in sel[0, h]]
+        assert (codes[0, :, h, sel[0, h]] == 0).all()
+        assert np.array_equal(codes[0, :, h, others], c0[0, :, h, others])
+        blk = np.arange(130) // 128
+        back = hi[0, :, h, :] * scales[0, h, blk][:, None]
+        assert np.array_equal(back, xw[0][:, h, sel[0, h]])      # exact
+
+
+def test_fp8_split_mode_exact_case_equals_fp64():
+    # 32 channels, 16 kept in the split; integer base-2 logits (scale ln 2) and values that
+    # e4m3 holds exactly make every rounding exact, so the split-mode fp8 attention must
+    # equal fp64 attention on the original values.  A missing block scale on the kept part,
+    # or a kept channel also counted in the e4m3 part, breaks the equality.
+    rng = np.random.default_rng(8)
+    N, D = 150, 32
+    q = np.zeros((1, N, 1, D)); k = np.zeros((1, N, 1, D))
+    q[0, :, 0, 3] = 1.0; k[0, :, 0, 3] = rng.integers(-4, 2, N)        # kept channel
+    q[0, :, 0, 20] = 2.0; k[0, :, 0, 20] = rng.integers(-2, 1, N) * 0.5  # e4m3 channel
+    v = oracle.e4m3_decode(rng.integers(0, 120, (1, N, 1, D)).astype(np.uint8))
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    sel = np.array([[list(range(0, 16))]], np.int32)
+    q8, qs, qh = oracle.quantise_qk_split(qb, sel)
+    k8, ks, kh = oracle.quantise_qk_split(kb, sel)
+    v8, vs = oracle.quantise_v(vb)
+    rows = [[0, 0, i] for i in range(0, N, 7)]
+    o8, l8 = oracle.fp8_attention_rows(q8, k8, v8, qs, ks, vs, math.log(2.0), rows,
+                                       q_hi=qh, k_hi=kh)
+    o64, l64 = oracle.attention_rows(q, k, v, math.log(2.0), rows)
+    np.testing.assert_allclose(o8, o64, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(l8, l64, rtol=1e-13)
