@@ -174,51 +174,45 @@ def main():
     }
 
     if not args.skip_fp8:
-        q8 = torch.empty((B, H, N, D), dtype=torch.uint8, device="cuda")
-        k8 = torch.empty_like(q8)
-        v8t = torch.empty((B, H, D, ldv), dtype=torch.uint8, device="cuda")
-        nblk = -(-N // ja.JA_QK_BLOCK)
-        qsc = torch.empty((B, H, nblk), dtype=torch.float32, device="cuda")
-        ksc = torch.empty_like(qsc)
-        vsc = torch.empty((B, H, D), dtype=torch.float32, device="cuda")
-        lib = ja.load()
-        sptr = stream.cuda_stream
+        out["fp8"] = {}
+        for mode, name in ((ja.JA_FP8_SPLIT, "split"), (ja.JA_FP8_PLAIN, "plain")):
+            t8 = ja.joint_attn_quant_fp8(q, k, vt, mode)
 
-        def step_fp8(rec):
-            e = [ev() for _ in range(4)] if rec else None
-            if rec:
-                e[0].record(stream)
-            ja.joint_attn_pack(qs_d, "bhnd", out=q)
-            ja.joint_attn_pack(ks_d, "bhnd", out=k)
-            ja.joint_attn_pack(vs_d, "bhdn", out=vt)
-            if rec:
-                e[1].record(stream)
-            rc = lib.joint_attn_quant_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D,
-                                          ldv, q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(),
-                                          qsc.data_ptr(), ksc.data_ptr(), vsc.data_ptr(), sptr)
-            assert rc == 0, rc
-            if rec:
-                e[2].record(stream)
-            ja.joint_attn_fwd_fp8(q8, k8, v8t, qsc, ksc, vsc, scale, out=o)
-            if rec:
-                e[3].record(stream)
-            return e
+            def step_fp8(rec, mode=mode, t8=t8):
+                e = [ev() for _ in range(4)] if rec else None
+                if rec:
+                    e[0].record(stream)
+                ja.joint_attn_pack(qs_d, "bhnd", out=q)
+                ja.joint_attn_pack(ks_d, "bhnd", out=k)
+                ja.joint_attn_pack(vs_d, "bhdn", out=vt)
+                if rec:
+                    e[1].record(stream)
+                ja.joint_attn_quant_fp8(q, k, vt, mode, out=t8)
+                if rec:
+                    e[2].record(stream)
+                ja.joint_attn_fwd_fp8(t8, scale, out=o)
+                if rec:
+                    e[3].record(stream)
+                return e
 
-        log("timing fp8 path")
-        wall8, durs8 = timed(step_fp8, args.steps, args.warmup)
-        ms8 = wall8 * 1e3 / args.steps
-        p8, qn8, f8 = durs8.mean(axis=0)
-        out["fp8"] = {
-            "workload": "t2i_2048_fp8 (same inputs)", "dtype": "fp8 e4m3 (fp32 accumulate)",
-            "value": round(flops / (ms8 * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(ms8, 4),
-            "step": "pack q,k,v + quant_fp8 + fwd_fp8",
-            "kernels_ms": {"pack_qkv": round(float(p8), 4), "quant_fp8": round(float(qn8), 4),
-                           "fwd_fp8": round(float(f8), 4)},
-            "fwd_fp8_tflops": round(flops / (f8 * 1e-3) / 1e12, 2),
-            "frac_of_fp8_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
-            "frac_of_bf16_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        }
+            log("timing fp8 path, mode %d (%s)" % (mode, name))
+            wall8, durs8 = timed(step_fp8, args.steps, args.warmup)
+            ms8 = wall8 * 1e3 / args.steps
+            p8, qn8, f8 = durs8.mean(axis=0)
+            out["fp8"][name] = {
+                "workload": "t2i_2048_fp8 (same inputs)", "mode": mode,
+                "dtype": "fp8 e4m3" + (" + bf16 outlier channels" if mode else "")
+                         + " (fp32 accumulate)",
+                "value": round(flops / (ms8 * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(ms8, 4),
+                "step": "pack q,k,v + quant_fp8 + fwd_fp8",
+                "kernels_ms": {"pack_qkv": round(float(p8), 4), "quant_fp8": round(float(qn8), 4),
+                               "fwd_fp8": round(float(f8), 4)},
+                "fwd_fp8_tflops": round(flops / (f8 * 1e-3) / 1e12, 2),
+                "frac_of_fp8_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                "frac_of_bf16_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            }
+            del t8
 
     if not args.no_cpu_baseline:
         import oracle

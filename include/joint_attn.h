@@ -15,7 +15,9 @@
  *
  * Conventions for every call.
  *   - Tensor pointers are DEVICE pointers (HBM) owned by the caller; the library never
- *     allocates, frees or keeps them.  "Host" marks the few host pointers.
+ *     allocates, frees or keeps them.  "Host" marks the few host pointers.  bf16 and
+ *     e4m3 tensors must be 16-byte aligned, fp32 and int32 arrays 4-byte aligned
+ *     (JA_EUNSUPPORTED otherwise).
  *   - Each call validates its arguments first; on any error nothing is launched and
  *     nothing is written.  Otherwise it enqueues its kernels on `stream` (a hipStream_t
  *     passed as void*; NULL = the default stream) and returns without synchronising.
@@ -51,6 +53,10 @@ extern "C" {
 
 #define JA_MAX_STREAMS 16   /* text + target + up to 14 reference images */
 #define JA_QK_BLOCK 128     /* tokens per fp8 scale block of Q and K */
+#define JA_HI_CHANNELS 16   /* Q/K channels per (b, h) kept out of e4m3 in fp8 mode 1 */
+
+#define JA_FP8_PLAIN 0      /* fp8 mode 0: every Q/K channel in e4m3 */
+#define JA_FP8_SPLIT 1      /* fp8 mode 1: JA_HI_CHANNELS outlier channels in bf16 */
 
 /* Human-readable name of a status code (static string). */
 const char *joint_attn_strerror(int status);
@@ -107,44 +113,65 @@ int joint_attn_fwd_bf16(const void *q, const void *k, const void *vt,
  * granularity follows the block-wise-scale advice of the kongchang.com English page
  * (section "Reducing Numerical Precision"):
  *   Q, K: one scale per (b, h, block of JA_QK_BLOCK consecutive packed tokens; the last
- *         block may be shorter), scale = amax / 448;
- *   V:    one scale per (b, h, channel) over all N tokens, scale = amax / 448;
- *   code = e4m3(clamp(x * (448 / amax), -448, 448)), binary32 arithmetic and e4m3
- *         rounding to nearest even; amax == 0 gives scale 1 and zero codes; the sign of
- *         a zero result is kept.  Inputs must be finite.
+ *         block may be shorter);
+ *   V:    one scale per (b, h, channel) over all N tokens;
+ *   every scale is a power of two, as in the OCP Microscaling formats: the smallest
+ *   s = 2^k (k >= -126) with amax <= 448 s (s = 1 when amax == 0), so x / s is exact and
+ *   code = e4m3(x / s), rounded to nearest even; the sign of a zero result is kept.
+ *   Inputs must be finite.
+ *
+ *   mode JA_FP8_PLAIN (0): the above.
+ *   mode JA_FP8_SPLIT (1): additionally, per (b, h), the JA_HI_CHANNELS channels with the
+ *     largest amax|q_c| * amax|k_c| over all tokens (ties to the lower index) are kept
+ *     out of e4m3 -- the article's VC-Attention remark (same section) gives the part of
+ *     the input with the largest quantisation error a residual correction; activation
+ *     outliers sit in whole channels.  Their codes are written as 0 and their exact
+ *     values divided by the block scale go to q_hi / k_hi.
  *
  *   q, k       bf16 BHND [B][H][N][D]      -> q8, k8   e4m3 BHND [B][H][N][D]
  *   vt         bf16 BHDN [B][H][D][ldv]    -> v8t      e4m3 BHDN [B][H][D][ldv],
  *                                                     padding columns written as 0
  *   q_scale, k_scale  fp32 [B][H][ceil(N / JA_QK_BLOCK)]
  *   v_scale           fp32 [B][H][D]
- * Codes and scales are bit-exact functions of the inputs.
+ *   mode 1 only (ignored, may be NULL, in mode 0):
+ *   q_hi, k_hi  bf16 [B][H][N][JA_HI_CHANNELS]  kept channels / block scale
+ *   hi_idx      int32 [B][H][JA_HI_CHANNELS]    kept channel indices, ascending
+ *   ch_amax     fp32 [B][H][2][D]               per-channel amax of Q (0) and K (1)
+ * Codes, scales, q_hi/k_hi and hi_idx are bit-exact functions of the inputs.
  */
 int joint_attn_quant_fp8(const void *q, const void *k, const void *vt,
-                         int B, int H, int64_t N, int D, int64_t ldv,
+                         int B, int H, int64_t N, int D, int64_t ldv, int mode,
                          void *q8, void *k8, void *v8t,
-                         float *q_scale, float *k_scale, float *v_scale, void *stream);
+                         float *q_scale, float *k_scale, float *v_scale,
+                         void *q_hi, void *k_hi, int32_t *hi_idx, float *ch_amax,
+                         void *stream);
 
 /*
  * joint_attn_fwd_fp8 -- attention on the e4m3 operands of joint_attn_quant_fp8.
- *   QK^T on fp8 matrix cores with fp32 accumulation; per-block Q/K scales and
- *   softmax_scale are folded into the base-2 exponent; the softmax numerators, taken
- *   relative to an integer row maximum M (base 2) and multiplied by 2^8, are rounded to
- *   e4m3 for the fp8 P.V product; the row sum uses the unrounded numerators; the
- *   per-channel V scale is applied in the epilogue:
- *     t_j = (q8_i . k8_j) * qs * ks * softmax_scale * log2(e),  p_j = 2^(t_j - M),
- *     O[c] = vs[c] * sum_j e4m3(2^8 p_j) v8_j[c] / (2^8 sum_j p_j).
+ *   QK^T on fp8 matrix cores with fp32 accumulation (mode 1 adds the kept channels on a
+ *   bf16 MFMA into the same accumulator); per-block Q/K scales and softmax_scale are
+ *   folded into the base-2 exponent; the softmax numerators, taken relative to an
+ *   integer row maximum M (base 2) and multiplied by 2^8, are rounded to e4m3 for the
+ *   fp8 P.V product; the row sum uses the unrounded numerators; the per-channel V scale
+ *   is applied in the epilogue:
+ *     t_j = (q8_i . k8_j + q_hi_i . k_hi_j) * qs * ks * softmax_scale * log2(e),
+ *     p_j = 2^(t_j - M),  O[c] = vs[c] * sum_j e4m3(2^8 p_j) v8_j[c] / (2^8 sum_j p_j).
+ *   The fp8 matrix cores sum each group of 8 products at reduced precision (relative to
+ *   the group's largest product), so on inputs with large-magnitude channels mode 0
+ *   differs from exact fp8 arithmetic by up to ~2e-2 (relative Frobenius).
  *
  *   q8, k8            e4m3 BHND [B][H][N][D]
  *   v8t               e4m3 BHDN [B][H][D][ldv]
  *   q_scale, k_scale  fp32 [B][H][ceil(N / JA_QK_BLOCK)];  v_scale fp32 [B][H][D]
+ *   mode              JA_FP8_PLAIN or JA_FP8_SPLIT (then q_hi, k_hi as written by the
+ *                     quantiser; NULL in mode 0)
  *   o                 bf16 BNHD [B][N][H][D];  lse fp32 [B][H][N] or NULL
- *   mode              must be 0 (the plain recipe above)
  */
 int joint_attn_fwd_fp8(const void *q8, const void *k8, const void *v8t,
                        const float *q_scale, const float *k_scale, const float *v_scale,
                        int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
-                       int mode, void *o, float *lse, void *stream);
+                       int mode, const void *q_hi, const void *k_hi,
+                       void *o, float *lse, void *stream);
 
 #ifdef __cplusplus
 }

@@ -4,10 +4,11 @@ The compute path is libjoint_attn.so (hand-written HIP kernels behind a C ABI, s
 include/joint_attn.h); this package is its thin Python binding plus the seeded
 synthetic-input generator used by the tests and the benchmark.
 """
-from ._abi import (JointAttnError, load, joint_attn_vt_ld, joint_attn_pack,
+from ._abi import (JointAttnError, Fp8Tensors, load, joint_attn_vt_ld, joint_attn_pack,
                    joint_attn_fwd_bf16, joint_attn_quant_fp8, joint_attn_fwd_fp8,
-                   EXPORTS, LIB_PATH, JA_QK_BLOCK)
+                   EXPORTS, LIB_PATH, JA_QK_BLOCK, JA_HI_CHANNELS, JA_FP8_PLAIN, JA_FP8_SPLIT)
 
-__all__ = ["JointAttnError", "load", "joint_attn_vt_ld", "joint_attn_pack",
+__all__ = ["JointAttnError", "Fp8Tensors", "load", "joint_attn_vt_ld", "joint_attn_pack",
            "joint_attn_fwd_bf16", "joint_attn_quant_fp8", "joint_attn_fwd_fp8",
-           "EXPORTS", "LIB_PATH", "JA_QK_BLOCK"]
+           "EXPORTS", "LIB_PATH", "JA_QK_BLOCK", "JA_HI_CHANNELS", "JA_FP8_PLAIN",
+           "JA_FP8_SPLIT"]

@@ -20,6 +20,8 @@ JA_OK, JA_EINVAL, JA_EUNSUPPORTED, JA_EHIP = 0, 1, 2, 3
 JA_LAYOUT_BHND, JA_LAYOUT_BHDN = 0, 1
 JA_MAX_STREAMS = 16
 JA_QK_BLOCK = 128
+JA_HI_CHANNELS = 16
+JA_FP8_PLAIN, JA_FP8_SPLIT = 0, 1
 
 EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
            "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_quant_fp8",
@@ -60,9 +62,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_fwd_bf16.restype = I
         h.joint_attn_fwd_bf16.argtypes = [P, P, P, I, I, I64, I, I64, F, P, P, P]
         h.joint_attn_quant_fp8.restype = I
-        h.joint_attn_quant_fp8.argtypes = [P, P, P, I, I, I64, I, I64, P, P, P, P, P, P, P]
+        h.joint_attn_quant_fp8.argtypes = [P, P, P, I, I, I64, I, I64, I, P, P, P, P, P, P,
+                                           P, P, P, P, P]
         h.joint_attn_fwd_fp8.restype = I
-        h.joint_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, I, I64, I, I64, F, I, P, P, P]
+        h.joint_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, I, I64, I, I64, F, I, P, P, P, P,
+                                         P]
         _lib = h
         return h
 
@@ -159,47 +163,85 @@ def joint_attn_fwd_bf16(q, k, vt, softmax_scale: float | None = None, out=None,
     return (out, lse) if return_lse else out
 
 
-def joint_attn_quant_fp8(q, k, vt, N: int | None = None):
-    """Returns (q8, k8, v8t, q_scale, k_scale, v_scale); codes are uint8 tensors."""
+class Fp8Tensors:
+    """Outputs of joint_attn_quant_fp8 (device tensors); the split-mode fields are None
+    in mode 0."""
+
+    def __init__(self, mode, q8, k8, v8t, q_scale, k_scale, v_scale, q_hi=None, k_hi=None,
+                 hi_idx=None, ch_amax=None):
+        self.mode = mode
+        self.q8, self.k8, self.v8t = q8, k8, v8t
+        self.q_scale, self.k_scale, self.v_scale = q_scale, k_scale, v_scale
+        self.q_hi, self.k_hi, self.hi_idx, self.ch_amax = q_hi, k_hi, hi_idx, ch_amax
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def joint_attn_quant_fp8(q, k, vt, mode: int = JA_FP8_PLAIN, out: Fp8Tensors | None = None
+                         ) -> Fp8Tensors:
+    """q, k: bf16 [B, H, N, D]; vt: bf16 [B, H, D, ldv] -> Fp8Tensors (codes as uint8).
+    `out` (from an earlier call with the same shapes and mode) is reused if given."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
         _need(t, torch.bfloat16, n, 4)
-    B, H, Nq, D = q.shape
-    N = Nq if N is None else int(N)
+    B, H, N, D = q.shape
     ldv = int(vt.shape[3])
     dev = q.device
     nblk = -(-N // JA_QK_BLOCK)
-    q8 = torch.empty((B, H, N, D), dtype=torch.uint8, device=dev)
-    k8 = torch.empty((B, H, N, D), dtype=torch.uint8, device=dev)
-    v8t = torch.empty((B, H, D, ldv), dtype=torch.uint8, device=dev)
-    qs = torch.empty((B, H, nblk), dtype=torch.float32, device=dev)
-    ks = torch.empty((B, H, nblk), dtype=torch.float32, device=dev)
-    vs = torch.empty((B, H, D), dtype=torch.float32, device=dev)
-    st = load().joint_attn_quant_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D, ldv,
-                                     q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(), qs.data_ptr(),
-                                     ks.data_ptr(), vs.data_ptr(), _stream(q))
+    if out is not None:
+        if (out.mode != mode or tuple(out.q8.shape) != (B, H, N, D)
+                or tuple(out.v8t.shape) != (B, H, D, ldv)):
+            raise ValueError("joint_attn_quant_fp8: `out` does not match the inputs or mode")
+    else:
+        out = _alloc_fp8(mode, B, H, N, D, ldv, nblk, dev)
+    st = load().joint_attn_quant_fp8(
+        q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D, ldv, int(mode),
+        out.q8.data_ptr(), out.k8.data_ptr(), out.v8t.data_ptr(), out.q_scale.data_ptr(),
+        out.k_scale.data_ptr(), out.v_scale.data_ptr(), _ptr(out.q_hi), _ptr(out.k_hi),
+        _ptr(out.hi_idx), _ptr(out.ch_amax), _stream(q))
     _check("joint_attn_quant_fp8", st)
-    return q8, k8, v8t, qs, ks, vs
+    return out
 
 
-def joint_attn_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, softmax_scale: float | None = None,
-                       mode: int = 0, out=None, return_lse: bool = False):
-    """fp8 attention on joint_attn_quant_fp8's outputs.  Returns O bf16 [B, N, H, D]."""
+def _alloc_fp8(mode, B, H, N, D, ldv, nblk, dev) -> Fp8Tensors:
     torch = _torch()
-    for t, n in ((q8, "q8"), (k8, "k8"), (v8t, "v8t")):
-        _need(t, torch.uint8, n, 4)
-    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
-        _need(t, torch.float32, n, 3)
-    B, H, N, D = q8.shape
-    ldv = int(v8t.shape[3])
+    out = Fp8Tensors(
+        mode,
+        torch.empty((B, H, N, D), dtype=torch.uint8, device=dev),
+        torch.empty((B, H, N, D), dtype=torch.uint8, device=dev),
+        torch.empty((B, H, D, ldv), dtype=torch.uint8, device=dev),
+        torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+        torch.empty((B, H, nblk), dtype=torch.float32, device=dev),
+        torch.empty((B, H, D), dtype=torch.float32, device=dev))
+    if mode == JA_FP8_SPLIT:
+        out.q_hi = torch.empty((B, H, N, JA_HI_CHANNELS), dtype=torch.bfloat16, device=dev)
+        out.k_hi = torch.empty((B, H, N, JA_HI_CHANNELS), dtype=torch.bfloat16, device=dev)
+        out.hi_idx = torch.empty((B, H, JA_HI_CHANNELS), dtype=torch.int32, device=dev)
+        out.ch_amax = torch.empty((B, H, 2, D), dtype=torch.float32, device=dev)
+    return out
+
+
+def joint_attn_fwd_fp8(t: Fp8Tensors, softmax_scale: float | None = None, out=None,
+                       return_lse: bool = False):
+    """fp8 attention on joint_attn_quant_fp8's outputs (its mode).  Returns O bf16
+    [B, N, H, D] (and lse)."""
+    torch = _torch()
+    for x, n in ((t.q8, "q8"), (t.k8, "k8"), (t.v8t, "v8t")):
+        _need(x, torch.uint8, n, 4)
+    for x, n in ((t.q_scale, "q_scale"), (t.k_scale, "k_scale"), (t.v_scale, "v_scale")):
+        _need(x, torch.float32, n, 3)
+    B, H, N, D = t.q8.shape
+    ldv = int(t.v8t.shape[3])
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if out is None:
-        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q8.device)
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=t.q8.device)
     _need(out, torch.bfloat16, "out", 4)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if return_lse else None
-    st = load().joint_attn_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8t.data_ptr(),
-                                   q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
-                                   B, H, N, D, ldv, scale, int(mode), out.data_ptr(),
-                                   lse.data_ptr() if lse is not None else None, _stream(q8))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=t.q8.device) if return_lse else None
+    st = load().joint_attn_fwd_fp8(
+        t.q8.data_ptr(), t.k8.data_ptr(), t.v8t.data_ptr(), t.q_scale.data_ptr(),
+        t.k_scale.data_ptr(), t.v_scale.data_ptr(), B, H, N, D, ldv, scale, int(t.mode),
+        _ptr(t.q_hi), _ptr(t.k_hi), out.data_ptr(), _ptr(lse), _stream(t.q8))
     _check("joint_attn_fwd_fp8", st)
     return (out, lse) if return_lse else out

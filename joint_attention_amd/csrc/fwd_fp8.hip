@@ -14,6 +14,10 @@
 // in.  P is stored as e4m3(2^8 * p); the 2^8 is folded into the exponent and the row
 // sum is taken over the same 2^8-scaled fp32 values, so it cancels in O = acc / l.
 // The per-channel V scale is applied in the epilogue.
+//
+// Split mode (HI): the 16 kept channels of Q and K (bf16, already divided by their
+// power-of-two block scales) add one v_mfma_f32_32x32x16_bf16 per 32x32 score block
+// into the same accumulator, so t = (q8.k8 + q_hi.k_hi) * qs * ks * scale * log2 e.
 #include "ja_device.h"
 #include "ja_launch.h"
 
@@ -27,10 +31,11 @@ static_assert(BR == JA_QK_BLOCK && JA_QK_BLOCK % BC == 0, "scale blocks must ali
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-template <int D>
+template <int D, bool HI>
 __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8T,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
+    const __bf16* __restrict__ QH, const __bf16* __restrict__ KH,
     int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE,
     int n_qtiles, int total) {
     constexpr int KROWB = D;                 // bytes per K row
@@ -42,6 +47,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
     static_assert(KCH >= 1 && VCH >= 1, "tile too small for the workgroup");
     __shared__ __attribute__((aligned(16))) uint8_t sk[BC * KROWB];
     __shared__ __attribute__((aligned(16))) uint8_t sv[D * BC];
+    constexpr int HC = JA_HI_CHANNELS;           // kept channels (bf16), 2 x 16 bytes per key
+    __shared__ __attribute__((aligned(16))) __bf16 skh[HI ? BC * HC : 8];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int r32 = lane & 31, hh = lane >> 5;
@@ -56,6 +63,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
 
     const int q_row = qt * BR + w * 32 + r32;
     const int q_ld = min(q_row, N - 1);
+    const __bf16* KHbh = HI ? KH + (int64_t)bh * N * HC : nullptr;
+    bf16x8 qhf = {};
+    if (HI) qhf = *reinterpret_cast<const bf16x8*>(QH + ((int64_t)bh * N + q_ld) * HC + 8 * hh);
     intx8 qf[NQC];
 #pragma unroll
     for (int c = 0; c < NQC; ++c) {
@@ -73,7 +83,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
     float m = -INFINITY, l = 0.f;
 
     const int nkt = (N + BC - 1) / BC;
-    uint4 kreg[KCH], vreg[VCH];
+    uint4 kreg[KCH], vreg[VCH], khreg = make_uint4(0, 0, 0, 0);
 
     auto load_tile = [&](int kt) {
         const int k0 = kt * BC;
@@ -85,6 +95,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
             kreg[i] = make_uint4(0, 0, 0, 0);
             if (full || key < N)
                 kreg[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + ch * 16);
+        }
+        if (HI && tid < BC * 2) {               // 2 chunks of 8 kept channels per key
+            const int key = k0 + tid / 2;
+            khreg = make_uint4(0, 0, 0, 0);
+            if (full || key < N)
+                khreg = *reinterpret_cast<const uint4*>(KHbh + (int64_t)key * HC + (tid % 2) * 8);
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
@@ -106,6 +122,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
         }
     };
     auto store_tile = [&]() {
+        if (HI && tid < BC * 2) {
+            const int row = tid / 2, half = (tid % 2) ^ ((row >> 3) & 1);
+            *reinterpret_cast<uint4*>(&skh[row * HC + half * 8]) = khreg;
+        }
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             const int idx = tid + i * NTHREADS, row = idx / DC, ch = idx % DC;
@@ -149,6 +169,11 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
                                   (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
                 s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                     av, qf[c], s[kb], 0, 0, 0, 0, 0, 0);
+            }
+            if (HI) {
+                const int half = hh ^ ((krow >> 3) & 1);
+                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&skh[krow * HC + half * 8]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qhf, s[kb], 0, 0, 0);
             }
         }
 
@@ -227,9 +252,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int c0 = ob * 32 + j * 8 + hh * 4;
-                const float4 sv4 = *reinterpret_cast<const float4*>(vs + c0);
-                floatx4 v = {oacc[ob][4 * j] * inv * sv4.x, oacc[ob][4 * j + 1] * inv * sv4.y,
-                             oacc[ob][4 * j + 2] * inv * sv4.z, oacc[ob][4 * j + 3] * inv * sv4.w};
+                // v_scale is only 4-byte aligned by contract: four scalar loads
+                floatx4 v = {oacc[ob][4 * j] * inv * vs[c0], oacc[ob][4 * j + 1] * inv * vs[c0 + 1],
+                             oacc[ob][4 * j + 2] * inv * vs[c0 + 2],
+                             oacc[ob][4 * j + 3] * inv * vs[c0 + 3]};
                 *reinterpret_cast<bf16x4*>(orow + c0) = __builtin_convertvector(v, bf16x4);
             }
         if (LSE != nullptr && hh == 0)
@@ -237,15 +263,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
     }
 }
 
-template <int D>
+template <int D, bool HI>
 hipError_t launch_d(const void* q8, const void* k8, const void* v8t, const float* qs,
-                    const float* ks, const float* vs, int B, int H, int N, int64_t ldv,
-                    float softmax_scale, void* o, float* lse, hipStream_t stream) {
+                    const float* ks, const float* vs, const void* qh, const void* kh, int B,
+                    int H, int N, int64_t ldv, float softmax_scale, void* o, float* lse,
+                    hipStream_t stream) {
     const int n_qtiles = (N + BR - 1) / BR;
     const int total = n_qtiles * B * H;
-    hipLaunchKernelGGL(fwd_fp8_kernel<D>, dim3(total), dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, HI>), dim3(total), dim3(NTHREADS), 0, stream,
                        static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
-                       static_cast<const uint8_t*>(v8t), qs, ks, vs, H, N, ldv,
+                       static_cast<const uint8_t*>(v8t), qs, ks, vs,
+                       static_cast<const __bf16*>(qh), static_cast<const __bf16*>(kh), H, N, ldv,
                        softmax_scale * kLog2e, static_cast<__bf16*>(o), lse, n_qtiles, total);
     return hipGetLastError();
 }
@@ -254,12 +282,17 @@ hipError_t launch_d(const void* q8, const void* k8, const void* v8t, const float
 
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
                           const float* k_scale, const float* v_scale, int B, int H, int N, int D,
-                          int64_t ldv, float softmax_scale, void* o, float* lse,
-                          hipStream_t stream) {
-    return D == 64 ? launch_d<64>(q8, k8, v8t, q_scale, k_scale, v_scale, B, H, N, ldv,
-                                  softmax_scale, o, lse, stream)
-                   : launch_d<128>(q8, k8, v8t, q_scale, k_scale, v_scale, B, H, N, ldv,
-                                   softmax_scale, o, lse, stream);
+                          int64_t ldv, float softmax_scale, int mode, const void* q_hi,
+                          const void* k_hi, void* o, float* lse, hipStream_t stream) {
+    if (mode == JA_FP8_SPLIT)
+        return D == 64 ? launch_d<64, true>(q8, k8, v8t, q_scale, k_scale, v_scale, q_hi, k_hi, B,
+                                            H, N, ldv, softmax_scale, o, lse, stream)
+                       : launch_d<128, true>(q8, k8, v8t, q_scale, k_scale, v_scale, q_hi, k_hi,
+                                             B, H, N, ldv, softmax_scale, o, lse, stream);
+    return D == 64 ? launch_d<64, false>(q8, k8, v8t, q_scale, k_scale, v_scale, nullptr, nullptr,
+                                         B, H, N, ldv, softmax_scale, o, lse, stream)
+                   : launch_d<128, false>(q8, k8, v8t, q_scale, k_scale, v_scale, nullptr, nullptr,
+                                          B, H, N, ldv, softmax_scale, o, lse, stream);
 }
 
 }  // namespace ja

@@ -96,41 +96,51 @@ int joint_attn_fwd_bf16(const void* q, const void* k, const void* vt, int B, int
 }
 
 int joint_attn_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int64_t N,
-                         int D, int64_t ldv, void* q8, void* k8, void* v8t, float* q_scale,
-                         float* k_scale, float* v_scale, void* stream) {
+                         int D, int64_t ldv, int mode, void* q8, void* k8, void* v8t,
+                         float* q_scale, float* k_scale, float* v_scale, void* q_hi, void* k_hi,
+                         int32_t* hi_idx, float* ch_amax, void* stream) {
     const int st = check_shape(B, H, N, D, ldv);
     if (st != JA_OK) return st;
+    if (mode != JA_FP8_PLAIN && mode != JA_FP8_SPLIT) return JA_EUNSUPPORTED;
     if (N == 0) return JA_OK;
     if (!q || !k || !vt || !q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale)
         return JA_EINVAL;
+    if (mode == JA_FP8_SPLIT && (!q_hi || !k_hi || !hi_idx || !ch_amax)) return JA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(q8) || !aligned16(k8) ||
         !aligned16(v8t))
         return JA_EUNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
          reinterpret_cast<uintptr_t>(v_scale)) & 3u)
         return JA_EUNSUPPORTED;
-    return hip_status(ja::launch_quant_fp8(q, k, vt, B, H, (int)N, D, ldv, q8, k8, v8t, q_scale,
-                                           k_scale, v_scale, static_cast<hipStream_t>(stream)));
+    if (mode == JA_FP8_SPLIT &&
+        ((reinterpret_cast<uintptr_t>(q_hi) | reinterpret_cast<uintptr_t>(k_hi)) & 15u ||
+         (reinterpret_cast<uintptr_t>(hi_idx) | reinterpret_cast<uintptr_t>(ch_amax)) & 3u))
+        return JA_EUNSUPPORTED;
+    return hip_status(ja::launch_quant_fp8(q, k, vt, B, H, (int)N, D, ldv, mode, q8, k8, v8t,
+                                           q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
+                                           ch_amax, static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
                        const float* k_scale, const float* v_scale, int B, int H, int64_t N, int D,
-                       int64_t ldv, float softmax_scale, int mode, void* o, float* lse,
-                       void* stream) {
+                       int64_t ldv, float softmax_scale, int mode, const void* q_hi,
+                       const void* k_hi, void* o, float* lse, void* stream) {
     const int st = check_shape(B, H, N, D, ldv);
     if (st != JA_OK) return st;
     if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
-    if (mode != 0) return JA_EUNSUPPORTED;
+    if (mode != JA_FP8_PLAIN && mode != JA_FP8_SPLIT) return JA_EUNSUPPORTED;
     if (N == 0) return JA_OK;
     if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o) return JA_EINVAL;
+    if (mode == JA_FP8_SPLIT && (!q_hi || !k_hi)) return JA_EINVAL;
     if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o))
         return JA_EUNSUPPORTED;
+    if (mode == JA_FP8_SPLIT && (!aligned16(q_hi) || !aligned16(k_hi))) return JA_EUNSUPPORTED;
     if (((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
           reinterpret_cast<uintptr_t>(v_scale)) & 3u) ||
         (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return JA_EUNSUPPORTED;
     return hip_status(ja::launch_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, B, H, (int)N, D,
-                                         ldv, softmax_scale, o, lse,
+                                         ldv, softmax_scale, mode, q_hi, k_hi, o, lse,
                                          static_cast<hipStream_t>(stream)));
 }
 

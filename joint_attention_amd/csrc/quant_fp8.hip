@@ -1,19 +1,24 @@
-// fp8 (OCP E4M3) quantisation of packed Q, K and V with dequantisation scales.
+// fp8 (OCP E4M3) quantisation of packed Q, K and V with power-of-two dequantisation
+// scales, and the channel split of the corrected mode.
 //
 // The VisualGen FLUX 3 article (everytik.com translation, section 量化注意力与稀疏注意力)
-// runs attention with fp8 Q/K and V; the block-wise scale factors follow the
-// kongchang.com English page (section "Reducing Numerical Precision").  Granularity:
-// Q and K one scale per (b, h, 128 packed tokens), V one scale per (b, h, channel).
+// runs attention with fp8 Q/K and V; block-wise scale factors follow the kongchang.com
+// English page (section "Reducing Numerical Precision").  Granularity: Q and K one scale
+// per (b, h, 128 packed tokens), V one scale per (b, h, channel).  Every scale is the
+// smallest power of two s with amax <= 448 s (as the shared scales of the OCP MX
+// formats), so x / s is exact and the e4m3 rounding (nearest, ties to even) is the only
+// rounding: codes are bit-exact by construction.
 //
-// Both kernels are bound by HBM bandwidth.  One workgroup owns one scale segment, which
-// is contiguous in memory in the layouts used here (a 128-token block of a BHND tensor
-// is 128 * D consecutive elements; a V channel is one BHDN row): pass 1 takes the
-// absolute maximum, pass 2 re-reads the segment (now in L2) and writes the codes.
+// Corrected mode: per (b, h) the 16 channels with the largest amax|q_c| * amax|k_c|
+// (ties to the lower index) are kept out of the e4m3 product.  Their e4m3 codes are
+// written as zero and their exact values divided by the block scale are written as bf16
+// (exact: a power-of-two rescale of a bf16 value), to be accumulated by a bf16 MFMA next
+// to the fp8 ones.
 //
-// Codes are bit-exact: scale = amax / 448 and inv = 448 / amax are correctly rounded
-// binary32 quotients, y = x * inv is one binary32 product, and y is clamped to +-448 and
-// rounded to e4m3 (nearest, ties to even) by the integer encoder below, written from
-// the OCP E4M3 definition.
+// All kernels are bound by HBM bandwidth.  One workgroup owns one scale segment, which
+// is contiguous in the layouts used here (a 128-token block of a BHND tensor is
+// 128 * D consecutive elements; a V channel is one BHDN row): pass 1 takes the absolute
+// maximum, pass 2 re-reads the segment (now in L2) and writes the codes.
 #include "ja_device.h"
 #include "ja_launch.h"
 
@@ -22,7 +27,8 @@ namespace {
 
 constexpr int NT = 256;
 
-// binary32 (finite) -> e4m3 code, round to nearest even, saturating at +-448.
+// finite binary32 -> e4m3 code, round to nearest even, saturating at +-448 (written from
+// the OCP E4M3 definition: bias 7, 3 mantissa bits, subnormal step 2^-9)
 __device__ inline uint32_t e4m3_from_f32(float y) {
     const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
     const float a = fminf(fabsf(y), 448.0f);
@@ -36,6 +42,18 @@ __device__ inline uint32_t e4m3_from_f32(float y) {
         code = (uint32_t)rintf(a * 512.0f);            // exact product, ties to even
     }
     return code | sign;
+}
+
+// smallest k >= -126 with amax <= 448 * 2^k (k = 0 for amax == 0).  With
+// amax = (1 + m / 2^23) * 2^(e - 127): 448 * 2^(e-135) = 1.75 * 2^(e-127), so k = e - 135
+// when m <= 0.75 * 2^23 and e - 134 otherwise.
+__device__ inline int pow2_exponent(float amax) {
+    if (amax == 0.f) return 0;
+    const uint32_t u = __float_as_uint(amax);
+    const int e = (int)((u >> 23) & 0xFFu);
+    if (e == 0) return -126;                           // denormal amax
+    const int k = ((u & 0x7FFFFFu) <= 0x600000u) ? e - 135 : e - 134;
+    return k < -126 ? -126 : k;
 }
 
 __device__ inline void bf16x2_to_f32(uint32_t w, float& lo, float& hi) {
@@ -55,26 +73,18 @@ __device__ inline float block_max(float v, float* red) {
     return r;
 }
 
-__device__ inline void scale_pair(float amax, float& scale, float& inv) {
-    if (amax == 0.f) {
-        scale = 1.f;
-        inv = 1.f;
-    } else {
-        scale = __fdiv_rn(amax, 448.0f);
-        inv = __fdiv_rn(448.0f, amax);
-    }
-}
-
-// 8 bf16 (one uint4) -> 8 e4m3 codes (one uint2)
-__device__ inline uint2 quant8(uint4 v, float inv) {
+// 8 bf16 (one uint4) -> 8 e4m3 codes (one uint2); `keep` bit e zeroes code e
+__device__ inline uint2 quant8(uint4 v, float inv, uint32_t keep = 0) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t out[2] = {0, 0};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         float lo, hi;
         bf16x2_to_f32(w[e], lo, hi);
-        const uint32_t c = e4m3_from_f32(lo * inv) | (e4m3_from_f32(hi * inv) << 8);
-        out[e / 2] |= c << (16 * (e % 2));
+        uint32_t c0 = e4m3_from_f32(lo * inv), c1 = e4m3_from_f32(hi * inv);
+        if (keep & (1u << (2 * e))) c0 = 0;
+        if (keep & (2u << (2 * e))) c1 = 0;
+        out[e / 2] |= (c0 | (c1 << 8)) << (16 * (e % 2));
     }
     return make_uint2(out[0], out[1]);
 }
@@ -91,14 +101,116 @@ __device__ inline float amax8(uint4 v) {
     return m;
 }
 
-// grid: (n_blocks, B*H, 2) -- z selects Q (0) or K (1)
+// corrected mode, step 1 -- grid (B*H): per-channel amax of Q and K over all N tokens,
+// then the 16 channels with the largest amax_q * amax_k (ascending order) -> hi_idx.
+template <int D>
+__global__ __launch_bounds__(NT) void select_hi_kernel(const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ k, int N,
+                                                      float* __restrict__ ch_amax,
+                                                      int32_t* __restrict__ hi_idx) {
+    constexpr int CPR = D / 8;                        // 16-byte chunks per token row
+    constexpr int RPP = NT / CPR;                     // rows handled in parallel
+    __shared__ float part[2][RPP][D + 1];
+    __shared__ float amax[2][D];
+    const int bh = blockIdx.x;
+    const int ch = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint4* src = reinterpret_cast<const uint4*>((t ? k : q) + (int64_t)bh * N * D);
+        float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int row = r0; row < N; row += RPP) {
+            const uint4 v = src[(int64_t)row * CPR + ch];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float lo, hi;
+                bf16x2_to_f32(w[e], lo, hi);
+                m[2 * e] = fmaxf(m[2 * e], fabsf(lo));
+                m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(hi));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part[t][r0][ch * 8 + e] = m[e];
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2 * D; i += NT) {
+        const int t = i / D, c = i % D;
+        float m = 0.f;
+        for (int r = 0; r < RPP; ++r) m = fmaxf(m, part[t][r][c]);
+        amax[t][c] = m;
+        ch_amax[((int64_t)bh * 2 + t) * D + c] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        // one wave: 16 rounds of arg-max over the D scores (exact bf16 products); every
+        // lane holds the same `chosen` list
+        const int lane = threadIdx.x;
+        float sc[D / 64];
+        bool taken[D / 64];
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) {
+            sc[j] = amax[0][lane + 64 * j] * amax[1][lane + 64 * j];
+            taken[j] = false;
+        }
+        int chosen[JA_HI_CHANNELS];
+#pragma unroll
+        for (int round = 0; round < JA_HI_CHANNELS; ++round) {
+            float best = -1.f;
+            int bidx = D;
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) {
+                const int c = lane + 64 * j;
+                if (!taken[j] && (sc[j] > best || (sc[j] == best && c < bidx))) {
+                    best = sc[j];
+                    bidx = c;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const float ob = __shfl_xor(best, o);
+                const int oi = __shfl_xor(bidx, o);
+                if (ob > best || (ob == best && oi < bidx)) {
+                    best = ob;
+                    bidx = oi;
+                }
+            }
+            chosen[round] = bidx;
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j)
+                if (lane + 64 * j == bidx) taken[j] = true;
+        }
+        if (lane == 0) {
+            // ascending channel order
+#pragma unroll
+            for (int i = 1; i < JA_HI_CHANNELS; ++i)
+#pragma unroll
+                for (int j = JA_HI_CHANNELS - 1; j >= i; --j)
+                    if (chosen[j - 1] > chosen[j]) {
+                        const int t = chosen[j];
+                        chosen[j] = chosen[j - 1];
+                        chosen[j - 1] = t;
+                    }
+#pragma unroll
+            for (int i = 0; i < JA_HI_CHANNELS; ++i)
+                hi_idx[(int64_t)bh * JA_HI_CHANNELS + i] = chosen[i];
+        }
+    }
+}
+
+// grid: (n_blocks, B*H, 2) -- z selects Q (0) or K (1).  With hi_idx, the selected
+// channels' codes are zero and their values / scale go to hi (bf16 [B, H, N, 16]).
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k, int N, int D,
+                                                     const uint16_t* __restrict__ k, int N,
                                                      uint8_t* __restrict__ q8,
                                                      uint8_t* __restrict__ k8,
                                                      float* __restrict__ qs,
-                                                     float* __restrict__ ks, int nblk) {
+                                                     float* __restrict__ ks, int nblk,
+                                                     const int32_t* __restrict__ hi_idx,
+                                                     uint16_t* __restrict__ q_hi,
+                                                     uint16_t* __restrict__ k_hi) {
     __shared__ float red[NT / 64];
+    __shared__ uint32_t mask[D / 32];
     const uint16_t* x = blockIdx.z ? k : q;
     uint8_t* y = blockIdx.z ? k8 : q8;
     float* sc = blockIdx.z ? ks : qs;
@@ -108,16 +220,40 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
     const int64_t base = ((int64_t)bh * N + t0) * D;
     const int nch = rows * D / 8;                       // 16-byte input chunks in the segment
     const uint4* src = reinterpret_cast<const uint4*>(x + base);
+    if (SPLIT) {
+        if (threadIdx.x < D / 32) mask[threadIdx.x] = 0;
+        __syncthreads();
+        if (threadIdx.x < JA_HI_CHANNELS) {
+            const int c = hi_idx[(int64_t)bh * JA_HI_CHANNELS + threadIdx.x];
+            atomicOr(&mask[c / 32], 1u << (c % 32));
+        }
+    }
 
     float m = 0.f;
     for (int c = threadIdx.x; c < nch; c += NT) m = fmaxf(m, amax8(src[c]));
-    const float amax = block_max(m, red);
-    float scale, inv;
-    scale_pair(amax, scale, inv);
-    if (threadIdx.x == 0) sc[(int64_t)bh * nblk + blk] = scale;
+    const float amax = block_max(m, red);               // (its barrier also publishes mask)
+    const int e = pow2_exponent(amax);
+    const float inv = ldexpf(1.f, -e);
+    if (threadIdx.x == 0) sc[(int64_t)bh * nblk + blk] = ldexpf(1.f, e);
 
     uint2* dst = reinterpret_cast<uint2*>(y + base);
-    for (int c = threadIdx.x; c < nch; c += NT) dst[c] = quant8(src[c], inv);
+    for (int c = threadIdx.x; c < nch; c += NT) {
+        uint32_t keep = 0;
+        if (SPLIT) {
+            const int c0 = (c % (D / 8)) * 8;           // first channel of this chunk
+            keep = (mask[c0 / 32] >> (c0 % 32)) & 0xFFu;
+        }
+        dst[c] = quant8(src[c], inv, keep);
+    }
+    if (SPLIT) {
+        uint16_t* hi = (blockIdx.z ? k_hi : q_hi) + ((int64_t)bh * N + t0) * JA_HI_CHANNELS;
+        const int32_t* sel = hi_idx + (int64_t)bh * JA_HI_CHANNELS;
+        for (int i = threadIdx.x; i < rows * JA_HI_CHANNELS; i += NT) {
+            const int r = i / JA_HI_CHANNELS, j = i % JA_HI_CHANNELS;
+            const float v = __uint_as_float((uint32_t)x[base + (int64_t)r * D + sel[j]] << 16);
+            hi[i] = (uint16_t)(__float_as_uint(v * inv) >> 16);   // exact power-of-two rescale
+        }
+    }
 }
 
 // grid: (D, B*H) -- one V^T row (b, h, channel) per workgroup
@@ -144,9 +280,9 @@ __global__ __launch_bounds__(NT) void quant_v_kernel(const uint16_t* __restrict_
         }
     }
     const float amax = block_max(m, red);
-    float scale, inv;
-    scale_pair(amax, scale, inv);
-    if (threadIdx.x == 0) vs[(int64_t)bh * D + c] = scale;
+    const int e = pow2_exponent(amax);
+    const float inv = ldexpf(1.f, -e);
+    if (threadIdx.x == 0) vs[(int64_t)bh * D + c] = ldexpf(1.f, e);
 
     uint2* dst = reinterpret_cast<uint2*>(v8t + base);
     for (int i = threadIdx.x; i < nch; i += NT) {
@@ -155,35 +291,58 @@ __global__ __launch_bounds__(NT) void quant_v_kernel(const uint16_t* __restrict_
         } else if (i == nfull && rem) {
             uint4 v = src[i];
             uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (int e = 0; e < 4; ++e) {             // zero the elements at or past N
-                if (2 * e >= rem) w[e] = 0;
-                else if (2 * e + 1 >= rem) w[e] &= 0xFFFFu;
+            for (int q = 0; q < 4; ++q) {              // zero the elements at or past N
+                if (2 * q >= rem) w[q] = 0;
+                else if (2 * q + 1 >= rem) w[q] &= 0xFFFFu;
             }
-            uint2 cde = quant8(make_uint4(w[0], w[1], w[2], w[3]), inv);
-            // a zero input encodes as code 0 (positive zero), as padding must be
-            dst[i] = cde;
+            dst[i] = quant8(make_uint4(w[0], w[1], w[2], w[3]), inv);   // zero -> code 0
         } else {
             dst[i] = make_uint2(0, 0);
         }
     }
 }
 
-}  // namespace
-
-hipError_t launch_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int N,
-                            int D, int64_t ldv, void* q8, void* k8, void* v8t, float* q_scale,
-                            float* k_scale, float* v_scale, hipStream_t stream) {
+template <int D>
+hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, int N,
+                    int64_t ldv, int mode, void* q8, void* k8, void* v8t, float* q_scale,
+                    float* k_scale, float* v_scale, void* q_hi, void* k_hi, int32_t* hi_idx,
+                    float* ch_amax, hipStream_t stream) {
     const int nblk = (N + JA_QK_BLOCK - 1) / JA_QK_BLOCK;
-    hipLaunchKernelGGL(quant_qk_kernel, dim3(nblk, B * H, 2), dim3(NT), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), N, D,
-                       static_cast<uint8_t*>(q8), static_cast<uint8_t*>(k8), q_scale, k_scale,
-                       nblk);
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    if (mode == 1) {
+        hipLaunchKernelGGL(select_hi_kernel<D>, dim3(B * H), dim3(NT), 0, stream, qq, kk, N,
+                           ch_amax, hi_idx);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((quant_qk_kernel<D, true>), dim3(nblk, B * H, 2), dim3(NT), 0, stream,
+                           qq, kk, N, static_cast<uint8_t*>(q8), static_cast<uint8_t*>(k8),
+                           q_scale, k_scale, nblk, hi_idx, static_cast<uint16_t*>(q_hi),
+                           static_cast<uint16_t*>(k_hi));
+    } else {
+        hipLaunchKernelGGL((quant_qk_kernel<D, false>), dim3(nblk, B * H, 2), dim3(NT), 0,
+                           stream, qq, kk, N, static_cast<uint8_t*>(q8),
+                           static_cast<uint8_t*>(k8), q_scale, k_scale, nblk, nullptr, nullptr,
+                           nullptr);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(quant_v_kernel, dim3(D, B * H), dim3(NT), 0, stream,
                        static_cast<const uint16_t*>(vt), N, D, ldv, static_cast<uint8_t*>(v8t),
                        v_scale);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int N,
+                            int D, int64_t ldv, int mode, void* q8, void* k8, void* v8t,
+                            float* q_scale, float* k_scale, float* v_scale, void* q_hi,
+                            void* k_hi, int32_t* hi_idx, float* ch_amax, hipStream_t stream) {
+    return D == 64 ? launch_d<64>(q, k, vt, B, H, N, ldv, mode, q8, k8, v8t, q_scale, k_scale,
+                                  v_scale, q_hi, k_hi, hi_idx, ch_amax, stream)
+                   : launch_d<128>(q, k, vt, B, H, N, ldv, mode, q8, k8, v8t, q_scale, k_scale,
+                                   v_scale, q_hi, k_hi, hi_idx, ch_amax, stream);
 }
 
 }  // namespace ja

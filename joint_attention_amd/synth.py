@@ -98,6 +98,7 @@ class Streams:
     q: list = field(default_factory=list)
     k: list = field(default_factory=list)
     v: list = field(default_factory=list)
+    outlier_channels: np.ndarray = field(default_factory=lambda: np.zeros(0, int))
 
 
 def make_streams(w: Workload, seed: int | None = None) -> Streams:
@@ -107,7 +108,7 @@ def make_streams(w: Workload, seed: int | None = None) -> Streams:
     gain_q = rng.normal(1.0, 0.1, size=w.D)
     gain_k = rng.normal(1.0, 0.1, size=w.D)
     outl = rng.choice(w.D, w.outliers, replace=False) if w.outliers else np.zeros(0, int)
-    out = Streams(w)
+    out = Streams(w, outlier_channels=np.sort(outl))
     n_streams = len(w.stream_lens)
     for s, L in enumerate(w.stream_lens):
         shape = (w.B, L, w.H, w.D)

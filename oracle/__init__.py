@@ -15,7 +15,7 @@ from .pack import stream_offsets, pack_tokens, to_bhnd, to_bhdn
 from .attention import attention, attention_rows, all_rows, widen_bf16
 from .fp8 import (E4M3_MAX, QK_BLOCK, P_SCALE_LOG2, HI_CHANNELS, e4m3_encode, e4m3_decode,
                   pow2_scale, quantise_qk, quantise_v, select_hi_channels, quantise_qk_split,
-                  fp8_attention_rows)
+                  fp8_attention_rows, e4m3_midpoint_distance)
 from ._native import build, default_threads
 
 __all__ = [
@@ -23,5 +23,5 @@ __all__ = [
     "attention", "attention_rows", "all_rows", "widen_bf16",
     "E4M3_MAX", "QK_BLOCK", "P_SCALE_LOG2", "HI_CHANNELS", "e4m3_encode", "e4m3_decode",
     "pow2_scale", "quantise_qk", "quantise_v", "select_hi_channels", "quantise_qk_split",
-    "fp8_attention_rows", "build", "default_threads",
+    "fp8_attention_rows", "e4m3_midpoint_distance", "build", "default_threads",
 ]

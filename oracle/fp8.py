@@ -153,8 +153,21 @@ def quantise_qk_split(x_tok: np.ndarray, sel: np.ndarray, block: int = QK_BLOCK)
 
 
 # --------------------------------------------------------------------- fp8 attention
+def e4m3_midpoint_distance(x) -> np.ndarray:
+    """Distance of each x >= 0 (x <= 448) to the nearest point where e4m3 rounding
+    switches between two neighbouring values (the midpoints of the e4m3 grid), and the
+    grid step there.  Returns (distance, step), float64."""
+    a = np.asarray(x, dtype=np.float64)
+    _, E = np.frexp(a)
+    e = E.astype(np.int64) - 1
+    step = np.where(a >= 2.0 ** -6, np.exp2((e - 3).astype(np.float64)), 2.0 ** -9)
+    y = a / step                                  # exact: step is a power of two
+    dist = np.abs(y - np.floor(y) - 0.5) * step
+    return dist, step
+
+
 def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: float, sel,
-                       block: int = QK_BLOCK, q_hi=None, k_hi=None):
+                       block: int = QK_BLOCK, q_hi=None, k_hi=None, rel_window=None):
     """Attention on the fp8 operands, selected rows (b, h, i).
 
     For each row, in float64 with exactly dequantised operands:
@@ -168,11 +181,18 @@ def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: flo
     v_scale [B, H, D].  In the corrected mode q_hi/k_hi [B, N, H, r] hold the kept
     channels divided by their block scale and add (q_hi . k_hi) * qs * ks to the dot
     product.  Returns (O [n, D], lse [n]).
+
+    Rounding P to e4m3 is a decision taken on a floating-point logit: an implementation
+    whose logits differ by rounding alone may round 2**8 * p_j the other way where it
+    lies within a hair of a midpoint of the e4m3 grid.  With rel_window set, a third
+    result [n, D] bounds what that can change: the sum over keys whose 2**8 * p_j lies
+    within rel_window * 2**8 * p_j of a midpoint of step_j * |v_j[c]| / (2**8 * sum p).
     """
     B, N, H, D = q8.shape
     sel = np.asarray(sel, dtype=np.int64).reshape(-1, 3)
     out = np.empty((len(sel), D), dtype=np.float64)
     lse = np.empty((len(sel),), dtype=np.float64)
+    flip = None if rel_window is None else np.empty((len(sel), D), dtype=np.float64)
     blk_of = np.arange(N) // block
     cache = {}
     for r, (b, h, i) in enumerate(sel):
@@ -192,8 +212,13 @@ def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: flo
         t = dots * (softmax_scale / math.log(2.0))
         M = math.ceil(t.max())
         p = np.exp2(t - M)
-        P = e4m3_decode(e4m3_encode(p * 2.0 ** P_SCALE_LOG2))
+        x = p * 2.0 ** P_SCALE_LOG2
+        P = e4m3_decode(e4m3_encode(x))
         l = p.sum()
         out[r] = (P @ vd) / (2.0 ** P_SCALE_LOG2 * l)
         lse[r] = (M + math.log2(l)) * math.log(2.0)
-    return out, lse
+        if flip is not None:
+            dist, step = e4m3_midpoint_distance(x)
+            near = dist <= rel_window * x
+            flip[r] = (step * near) @ np.abs(vd) / (2.0 ** P_SCALE_LOG2 * l)
+    return (out, lse) if flip is None else (out, lse, flip)

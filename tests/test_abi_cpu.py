@@ -80,11 +80,21 @@ def test_attention_validation(lib):
     assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, fake, fake + 2, None) == 2  # lse align
     assert f(None, None, None, 1, 2, 0, 128, 0, 0.1, None, None, None) == 0       # N == 0
     g = lib.joint_attn_fwd_fp8
-    assert g(fake, fake, fake, fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 1, fake, None, None) == 2
-    assert g(fake, fake, fake, None, fake, fake, 1, 2, 64, 128, 64, 0.1, 0, fake, None, None) == 1
+    assert g(fake, fake, fake, fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 7, None, None, fake,
+             None, None) == 2                                                   # mode
+    assert g(fake, fake, fake, None, fake, fake, 1, 2, 64, 128, 64, 0.1, 0, None, None, fake,
+             None, None) == 1                                                   # q_scale
+    assert g(fake, fake, fake, fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 1, None, fake, fake,
+             None, None) == 1                                                   # split: q_hi
     q = lib.joint_attn_quant_fp8
-    assert q(fake, fake, fake, 1, 2, 64, 128, 64, fake, fake, fake, None, fake, fake, None) == 1
-    assert q(fake, fake, fake, 1, 2, 64, 128, 64, fake, fake, fake + 3, fake, fake, fake, None) == 2
+    assert q(fake, fake, fake, 1, 2, 64, 128, 64, 0, fake, fake, fake, None, fake, fake,
+             None, None, None, None, None) == 1                                  # q_scale
+    assert q(fake, fake, fake, 1, 2, 64, 128, 64, 0, fake, fake, fake + 3, fake, fake, fake,
+             None, None, None, None, None) == 2                                  # v8t align
+    assert q(fake, fake, fake, 1, 2, 64, 128, 64, 1, fake, fake, fake, fake, fake, fake,
+             fake, fake, None, fake, None) == 1                                  # split: hi_idx
+    assert q(fake, fake, fake, 1, 2, 64, 128, 64, 2, fake, fake, fake, fake, fake, fake,
+             None, None, None, None, None) == 2                                  # mode
 
 
 def test_python_binding_rejects_cpu_tensors(lib):

@@ -1,11 +1,18 @@
-"""GPU: fp8 quantiser (bit-exact) and fp8 forward (against the fp8 reference) through
-the C ABI.
+"""GPU: fp8 quantiser (bit-exact) and fp8 forward through the C ABI, both modes.
 
-The quantiser's codes and scales must equal the oracle's bit for bit.  The fp8 forward
-is compared with the oracle's fp8 attention (same quantised operands, same P rounding
-rule) at the bf16-output bar, rel_F <= 5e-3 and max |err| <= 2e-2; its distance to the
-fp64 attention on the unquantised inputs is printed and bounded by what the fp8 recipe
-itself loses (the reference's own distance, plus the output rounding).
+Quantiser: codes, scales and, in the split mode, the kept channel indices, their
+scaled bf16 values and the channel amax must equal the oracle's bit for bit.
+
+Forward: compared with the oracle's fp8 attention on the same quantised operands (same
+P rounding rule).  Split mode (1) meets the bf16-output bar there, rel_F <= 5e-3 and
+max |err| <= 2e-2 plus, per element, what rounding a near-midpoint P code the other way
+may change (the oracle's flip bound: P's code is decided on a floating-point logit).
+Plain mode (0) is held to FP8_PLAIN_REL_F instead: the fp8 matrix cores add each group of 8 products at reduced precision relative to the group's largest
+product, and with x8 outlier channels in Q and K that largest product hides the rest
+of its group's low bits; exact fp8 arithmetic on the CPU cannot follow that.  Against
+the fp64 attention on the unquantised inputs the split mode must meet the fp8 bar
+rel_F <= 5e-2; the plain mode cannot on outlier inputs (e4m3's 3 mantissa bits on
+logits dominated by the outlier channels) and is only bounded by its own recipe's loss.
 """
 import math
 
@@ -15,119 +22,203 @@ import pytest
 import oracle
 from joint_attention_amd import synth
 
-from _common import (FP8_MAX_ABS, FP8_REL_F, device_packed, from_device_bf16, gather_rows,
-                     host_streams, max_abs, packed_host, rel_frobenius, widen_bf16)
+from _common import (FP8_MAX_ABS, FP8_PLAIN_MAX_ABS, FP8_PLAIN_REL_F, FP8_REL_F, FP8_VS_FP64,
+                     device_packed, from_device_bf16, gather_rows, host_streams, max_abs,
+                     packed_host, rel_frobenius, widen_bf16)
 
 pytestmark = pytest.mark.gpu
 
+MODES = (0, 1)
+# The kernel's base-2 logits (fp32 matrix-core sums, then the hardware exp2) differ from
+# the oracle's fp64 ones by rounding only, a relative change of 2**8 * p far below 2**-12
+# at these magnitudes; a P code may round the other way only within that window of a
+# midpoint of the e4m3 grid, and the oracle's bound for it widens the max |err| bar.
+P_FLIP_WINDOW = 2.0 ** -12
 
-def _quant_both(w, bh_slices=None):
+
+def _widen_f32(bits):
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _quant_both(w, mode, bh=None):
+    """Quantise on the GPU and fetch the results, restricted to slice (b, h) if given,
+    together with the matching token-major host inputs."""
     import joint_attention_amd as ja
     import torch
     st = host_streams(w)
     q, k, vt, offs = device_packed(st)
-    q8, k8, v8t, qs, ks, vs = ja.joint_attn_quant_fp8(q, k, vt)
+    t = ja.joint_attn_quant_fp8(q, k, vt, mode)
     torch.cuda.synchronize()
     qh, kh, vh, _ = packed_host(st)
-    if bh_slices is not None:                           # compare a few (b, h) slices only
-        b, h = bh_slices
+    if bh is not None:
+        b, h = bh
         qh, kh, vh = qh[b:b + 1, :, h:h + 1], kh[b:b + 1, :, h:h + 1], vh[b:b + 1, :, h:h + 1]
-        pick = lambda t: t[b:b + 1, h:h + 1].cpu().numpy()
+        pick = lambda x: None if x is None else x[b:b + 1, h:h + 1].cpu().numpy()
     else:
-        pick = lambda t: t.cpu().numpy()
-    return dict(dev=(q, k, vt, q8, k8, v8t, qs, ks, vs), st=st,
-                got=tuple(pick(t) for t in (q8, k8, v8t, qs, ks, vs)),
-                host=(qh, kh, vh))
+        pick = lambda x: None if x is None else x.cpu().numpy()
+    got = {n: pick(getattr(t, n)) for n in ("q8", "k8", "v8t", "q_scale", "k_scale", "v_scale",
+                                             "hi_idx", "ch_amax")}
+    for n in ("q_hi", "k_hi"):
+        x = getattr(t, n)
+        got[n] = None if x is None else pick(x.view(torch.int16)).view(np.uint16)
+    return dict(dev=(q, k, vt, t), got=got, host=(qh, kh, vh))
 
 
-def _assert_quant_equal(res, N):
-    q8g, k8g, v8tg, qsg, ksg, vsg = res["got"]
+def _reference_quant(qh, kh, vh, mode):
+    ref = {}
+    if mode == 1:
+        sel = oracle.select_hi_channels(qh, kh)
+        ref["q8"], ref["q_scale"], ref["q_hi"] = oracle.quantise_qk_split(qh, sel)
+        ref["k8"], ref["k_scale"], ref["k_hi"] = oracle.quantise_qk_split(kh, sel)
+        ref["hi_idx"] = sel
+    else:
+        ref["q8"], ref["q_scale"] = oracle.quantise_qk(qh)
+        ref["k8"], ref["k_scale"] = oracle.quantise_qk(kh)
+        ref["q_hi"] = ref["k_hi"] = None
+    ref["v8"], ref["v_scale"] = oracle.quantise_v(vh)
+    return ref
+
+
+def _assert_quant_equal(res, mode):
+    g = res["got"]
     qh, kh, vh = res["host"]
-    q8r, qsr = oracle.quantise_qk(qh)
-    k8r, ksr = oracle.quantise_qk(kh)
-    v8r, vsr = oracle.quantise_v(vh)
-    assert np.array_equal(q8g, oracle.to_bhnd(q8r))
-    assert np.array_equal(k8g, oracle.to_bhnd(k8r))
-    assert np.array_equal(v8tg, oracle.to_bhdn(v8r, v8tg.shape[3]))
-    for g, r in ((qsg, qsr), (ksg, ksr), (vsg, vsr)):
-        assert np.array_equal(g.view(np.uint32), r.view(np.uint32))
+    r = _reference_quant(qh, kh, vh, mode)
+    assert np.array_equal(g["q8"], oracle.to_bhnd(r["q8"]))
+    assert np.array_equal(g["k8"], oracle.to_bhnd(r["k8"]))
+    assert np.array_equal(g["v8t"], oracle.to_bhdn(r["v8"], g["v8t"].shape[3]))
+    for n in ("q_scale", "k_scale", "v_scale"):
+        assert np.array_equal(g[n].view(np.uint32), r[n].view(np.uint32)), n
+    if mode == 1:
+        assert np.array_equal(g["hi_idx"], r["hi_idx"])
+        for n in ("q_hi", "k_hi"):                 # x / 2**k is exact in bf16 here
+            want = np.transpose(r[n], (0, 2, 1, 3))
+            assert np.array_equal(_widen_f32(g[n]).astype(np.float64), want), n
+        amax = np.stack([np.abs(_widen_f32(x)).max(axis=1) for x in (qh, kh)], axis=2)
+        assert np.array_equal(g["ch_amax"], amax)
+    else:
+        assert g["q_hi"] is None and g["hi_idx"] is None
 
 
-@pytest.mark.parametrize("lens,D", [((32, 256), 64), ((1,), 128), ((100, 29), 128),
-                                    ((127, 2, 0, 1), 64), ((129, 64, 66), 128), ((512, 1000), 128)])
-def test_quant_bit_exact_small(lens, D):
+QUANT_CASES = [((32, 256), 64), ((1,), 128), ((100, 29), 128), ((127, 2, 0, 1), 64),
+               ((129, 64, 66), 128), ((512, 1000), 128)]
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("lens,D", QUANT_CASES)
+def test_quant_bit_exact_small(lens, D, mode):
     w = synth.custom("q", B=2, H=3, D=D, stream_lens=lens, outliers=4 if D == 128 else 0,
                      seed=sum(lens))
-    print("quant", lens, D, flush=True)
-    _assert_quant_equal(_quant_both(w), w.N)
+    print("quant mode", mode, lens, D, flush=True)
+    _assert_quant_equal(_quant_both(w, mode), mode)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("b,h", [(0, 0), (1, 23)])
-def test_quant_bit_exact_t2i_2048_slices(b, h):
+def test_quant_bit_exact_t2i_2048_slices(b, h, mode):
     w = synth.WORKLOADS["t2i_2048_fp8"]
-    print("quant t2i_2048 slice", b, h, flush=True)
-    _assert_quant_equal(_quant_both(w, (b, h)), w.N)
+    print("quant t2i_2048 slice", b, h, "mode", mode, flush=True)
+    _assert_quant_equal(_quant_both(w, mode, (b, h)), mode)
 
 
-def _fwd_fp8(w, sel=None):
+def test_quant_split_channels_cover_the_outliers():
+    """With 4 x8 outlier channels shared by Q and K, those 4 are always kept."""
+    w = synth.custom("qo", B=1, H=4, D=128, stream_lens=(64, 448), outliers=4, seed=5)
+    res = _quant_both(w, 1)
+    st = host_streams(w)
+    for b in range(w.B):
+        for h in range(w.H):
+            assert set(st.outlier_channels.tolist()) <= set(res["got"]["hi_idx"][b, h].tolist())
+
+
+def _fwd_fp8(w, mode, sel=None):
     """GPU fp8 forward vs the oracle's fp8 attention and its fp64 attention.  The oracle
     side runs per (b, h) slice (the method is independent per slice), so full-size
     workloads only quantise the slices that the sampled rows touch."""
     import joint_attention_amd as ja
     import torch
-    res = _quant_both(w)
-    q, k, vt, q8, k8, v8t, qs, ks, vs = res["dev"]
+    res = _quant_both(w, mode)
+    t = res["dev"][3]
     scale = 1.0 / math.sqrt(w.D)
-    o, lse = ja.joint_attn_fwd_fp8(q8, k8, v8t, qs, ks, vs, scale, return_lse=True)
+    o, lse = ja.joint_attn_fwd_fp8(t, scale, return_lse=True)
     torch.cuda.synchronize()
     qh, kh, vh = res["host"]
     if sel is None:
         sel = oracle.all_rows(w.B, w.N, w.H)
     ref8 = np.empty((len(sel), w.D))
     lse8 = np.empty(len(sel))
+    flip = np.empty((len(sel), w.D))
     ref64 = np.empty((len(sel), w.D))
     for b, h in sorted(set(map(tuple, sel[:, :2].tolist()))):
         m = (sel[:, 0] == b) & (sel[:, 1] == h)
         sl = lambda x: np.ascontiguousarray(x[b:b + 1, :, h:h + 1])
         qb, kb, vb = sl(qh), sl(kh), sl(vh)
-        q8r, qsr = oracle.quantise_qk(qb)
-        k8r, ksr = oracle.quantise_qk(kb)
-        v8r, vsr = oracle.quantise_v(vb)
+        r = _reference_quant(qb, kb, vb, mode)
         loc = np.stack([np.zeros(m.sum(), np.int64), np.zeros(m.sum(), np.int64), sel[m, 2]], 1)
-        ref8[m], lse8[m] = oracle.fp8_attention_rows(q8r, k8r, v8r, qsr, ksr, vsr, scale, loc)
+        ref8[m], lse8[m], flip[m] = oracle.fp8_attention_rows(
+            r["q8"], r["k8"], r["v8"], r["q_scale"], r["k_scale"], r["v_scale"], scale, loc,
+            q_hi=r["q_hi"], k_hi=r["k_hi"], rel_window=P_FLIP_WINDOW)
         ref64[m], _ = oracle.attention_rows(qb, kb, vb, scale, loc)
     got = gather_rows(widen_bf16(from_device_bf16(o)), sel)
     got_lse = lse.cpu().numpy()[sel[:, 0], sel[:, 1], sel[:, 2]].astype(np.float64)
-    return got, ref8, ref64, got_lse, lse8
+    return got, ref8, ref64, got_lse, lse8, flip
 
 
-def _assert_fp8(tag, got, ref8, ref64, got_lse, lse8):
-    rf, ma = rel_frobenius(got, ref8), max_abs(got, ref8)
+def _assert_fp8(tag, mode, got, ref8, ref64, got_lse, lse8, flip):
+    rf = rel_frobenius(got, ref8)
+    err = np.abs(got - ref8)
+    ma = float(err.max())
+    ma_unflipped = float(np.where(flip > 0, 0.0, err).max())
+    beyond = float((err - flip).max())             # error left after the flip allowance
     recipe = rel_frobenius(ref8, ref64)
     vs64 = rel_frobenius(got, ref64)
     lse_err = float(np.abs(got_lse - lse8).max())
-    print("%s: vs fp8 reference rel_F %.3e max %.3e lse %.2e | vs fp64 unquantised: "
-          "kernel %.3e, reference itself %.3e" % (tag, rf, ma, lse_err, vs64, recipe), flush=True)
-    assert rf <= FP8_REL_F, (tag, rf)
-    assert ma <= FP8_MAX_ABS, (tag, ma)
-    assert vs64 <= recipe + 5e-3, (tag, vs64, recipe)
+    print("%s mode %d: vs fp8 reference rel_F %.3e max %.3e (beyond P-flip bound %.3e, rows "
+          "without a near-midpoint P %.3e) lse %.2e | vs fp64 unquantised: kernel %.3e, "
+          "reference itself %.3e" % (tag, mode, rf, ma, beyond, ma_unflipped, lse_err, vs64,
+                                     recipe), flush=True)
+    if mode == 1:
+        assert rf <= FP8_REL_F, (tag, rf)
+        assert beyond <= FP8_MAX_ABS, (tag, beyond)
+    else:
+        assert rf <= FP8_PLAIN_REL_F, (tag, rf)
+        assert ma <= FP8_PLAIN_MAX_ABS, (tag, ma)
+    bar_f = FP8_REL_F if mode == 1 else FP8_PLAIN_REL_F
+    assert vs64 <= recipe + bar_f, (tag, vs64, recipe)
+    if mode == 1:
+        assert vs64 <= FP8_VS_FP64, (tag, vs64)
     assert lse_err <= 1e-3 * max(1.0, float(np.abs(lse8).max())), (tag, lse_err)
 
 
-def test_fp8_tiny_every_row():
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_tiny_every_row(mode):
     w = synth.custom("fp8tiny", B=1, H=2, D=64, stream_lens=(32, 256))
-    _assert_fp8("fp8 tiny", *_fwd_fp8(w))
+    _assert_fp8("fp8 tiny", mode, *_fwd_fp8(w, mode))
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("lens,D", [((1,), 128), ((63,), 64), ((100, 29), 128),
                                     ((129, 64, 66), 128), ((127, 2, 0, 1), 64)])
-def test_fp8_ragged_every_row(lens, D):
+def test_fp8_ragged_every_row(lens, D, mode):
     w = synth.custom("fp8r", B=2, H=2, D=D, stream_lens=lens, outliers=4 if D == 128 else 0,
                      seed=3 + sum(lens))
-    _assert_fp8("fp8 ragged %s D=%d" % (lens, D), *_fwd_fp8(w))
+    _assert_fp8("fp8 ragged %s D=%d" % (lens, D), mode, *_fwd_fp8(w, mode))
 
 
-def test_fp8_t2i_2048_sampled_rows():
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_t2i_2048_sampled_rows(mode):
     w = synth.WORKLOADS["t2i_2048_fp8"]
     sel = synth.row_sample(w, 256, seed=12, n_pairs=3)
-    _assert_fp8("fp8 t2i_2048", *_fwd_fp8(w, sel))
+    _assert_fp8("fp8 t2i_2048", mode, *_fwd_fp8(w, mode, sel))
+
+
+def test_fp8_deterministic():
+    import joint_attention_amd as ja
+    import torch
+    w = synth.custom("fp8det", B=1, H=3, D=128, stream_lens=(64, 700), outliers=4, seed=9)
+    q, k, vt, _ = device_packed(host_streams(w))
+    for mode in MODES:
+        t = ja.joint_attn_quant_fp8(q, k, vt, mode)
+        a = ja.joint_attn_fwd_fp8(t)
+        b = ja.joint_attn_fwd_fp8(t)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -275,3 +275,46 @@ def test_fp8_split_mode_exact_case_equals_fp64():
     o64, l64 = oracle.attention_rows(q, k, v, math.log(2.0), rows)
     np.testing.assert_allclose(o8, o64, rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(l8, l64, rtol=1e-13)
+
+
+def test_e4m3_midpoint_distance_hand_values():
+    # grid steps: 2**-9 below 2**-6, 0.125 on [1, 2), 16 on [128, 256), 32 on [256, 448]
+    d, st = oracle.e4m3_midpoint_distance(np.array([1.0625, 1.0, 2.0 ** -7, 448.0, 136.0, 130.0]))
+    np.testing.assert_array_equal(st, [0.125, 0.125, 2.0 ** -9, 32.0, 16.0, 16.0])
+    np.testing.assert_array_equal(d, [0.0, 0.0625, 2.0 ** -10, 16.0, 0.0, 6.0])
+    # the midpoints are exactly where the encoder switches
+    for x, step in ((1.0625, 0.125), (136.0, 16.0), (2.0 ** -7 + 2.0 ** -10, 2.0 ** -9)):
+        lo = oracle.e4m3_decode(oracle.e4m3_encode(x - 1e-9))
+        hi = oracle.e4m3_decode(oracle.e4m3_encode(x + 1e-9))
+        assert hi - lo == step
+
+
+def test_fp8_attention_flip_bound_hand_case():
+    # Two keys through one kept channel (exact float64 values), scale ln 2 so t = q_hi.k_hi:
+    # t = [0, log2(136/256)] -> M = 0, 2**8 p = [256, 136]; 136 is the midpoint between the
+    # e4m3 values 128 and 144, so key 1 may round either way.  Bound for every channel:
+    # 16 * |v_1| / (2**8 * (1 + 136/256)) = 2/49 with v_1 = 1.  Key 0 (256, mid-step) adds 0.
+    D = 16
+    q8 = np.zeros((1, 2, 1, D), np.uint8)
+    k8 = np.zeros((1, 2, 1, D), np.uint8)
+    v8 = np.zeros((1, 2, 1, D), np.uint8)
+    v8[0, 1, 0, :] = oracle.e4m3_encode(1.0)
+    v8[0, 0, 0, :] = oracle.e4m3_encode(-2.0)
+    one = np.ones((1, 1, 1), np.float32)
+    vs = np.ones((1, 1, D), np.float32)
+    q_hi = np.zeros((1, 2, 1, 1)); q_hi[0, 0, 0, 0] = 1.0
+    outs = []
+    for nudge in (-1e-9, 0.0, 1e-9):
+        k_hi = np.zeros((1, 2, 1, 1)); k_hi[0, 1, 0, 0] = math.log2(136 / 256) + nudge
+        outs.append(oracle.fp8_attention_rows(q8, k8, v8, one, one, vs, math.log(2.0),
+                                              [[0, 0, 0]], q_hi=q_hi, k_hi=k_hi,
+                                              rel_window=1e-6))
+    np.testing.assert_allclose(outs[1][2], np.full((1, D), 2.0 / 49.0), rtol=1e-12)
+    # the bound is what the flip does: nudging the logit across the midpoint moves O by it
+    jump = outs[2][0] - outs[0][0]
+    np.testing.assert_allclose(jump, np.full((1, D), 2.0 / 49.0), rtol=1e-6)
+    # far from any midpoint the bound vanishes
+    k_hi = np.zeros((1, 2, 1, 1)); k_hi[0, 1, 0, 0] = math.log2(130 / 256)
+    far = oracle.fp8_attention_rows(q8, k8, v8, one, one, vs, math.log(2.0), [[0, 0, 0]],
+                                    q_hi=q_hi, k_hi=k_hi, rel_window=1e-6)
+    assert np.all(far[2] == 0.0)
