@@ -101,99 +101,110 @@ __device__ inline float amax8(uint4 v) {
     return m;
 }
 
-// corrected mode, step 1 -- grid (B*H): per-channel amax of Q and K over all N tokens,
-// then the 16 channels with the largest amax_q * amax_k (ascending order) -> hi_idx.
+// corrected mode, step 0 -- clear ch_amax (a plain fill kernel, also safe under graph
+// capture)
+__global__ __launch_bounds__(NT) void clear_kernel(float* __restrict__ x, int n) {
+    const int i = blockIdx.x * NT + threadIdx.x;
+    if (i < n) x[i] = 0.f;
+}
+
+// corrected mode, step 1 -- grid (n_blocks, B*H, 2): per-channel amax of one 128-token
+// block of Q (z = 0) or K (z = 1), folded into ch_amax [B, H, 2, D] with an atomic max on
+// the bit patterns (non-negative floats order like their bits; max is order-free, so the
+// result is deterministic).
 template <int D>
-__global__ __launch_bounds__(NT) void select_hi_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(NT) void chan_amax_kernel(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ k, int N,
-                                                      float* __restrict__ ch_amax,
-                                                      int32_t* __restrict__ hi_idx) {
+                                                      float* __restrict__ ch_amax) {
     constexpr int CPR = D / 8;                        // 16-byte chunks per token row
     constexpr int RPP = NT / CPR;                     // rows handled in parallel
-    __shared__ float part[2][RPP][D + 1];
-    __shared__ float amax[2][D];
-    const int bh = blockIdx.x;
+    __shared__ float part[RPP][D + 1];
+    const int blk = blockIdx.x, bh = blockIdx.y;
+    const int t0 = blk * JA_QK_BLOCK;
+    const int rows = min(JA_QK_BLOCK, N - t0);
     const int ch = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+    const uint4* src =
+        reinterpret_cast<const uint4*>((blockIdx.z ? k : q) + ((int64_t)bh * N + t0) * D);
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int row = r0; row < rows; row += RPP) {
+        const uint4 v = src[row * CPR + ch];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const uint4* src = reinterpret_cast<const uint4*>((t ? k : q) + (int64_t)bh * N * D);
-        float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int row = r0; row < N; row += RPP) {
-            const uint4 v = src[(int64_t)row * CPR + ch];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float lo, hi;
-                bf16x2_to_f32(w[e], lo, hi);
-                m[2 * e] = fmaxf(m[2 * e], fabsf(lo));
-                m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(hi));
-            }
+        for (int e = 0; e < 4; ++e) {
+            float lo, hi;
+            bf16x2_to_f32(w[e], lo, hi);
+            m[2 * e] = fmaxf(m[2 * e], fabsf(lo));
+            m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(hi));
         }
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part[t][r0][ch * 8 + e] = m[e];
-    }
+    for (int e = 0; e < 8; ++e) part[r0][ch * 8 + e] = m[e];
     __syncthreads();
-    for (int i = threadIdx.x; i < 2 * D; i += NT) {
-        const int t = i / D, c = i % D;
-        float m = 0.f;
-        for (int r = 0; r < RPP; ++r) m = fmaxf(m, part[t][r][c]);
-        amax[t][c] = m;
-        ch_amax[((int64_t)bh * 2 + t) * D + c] = m;
+    if (threadIdx.x < D) {
+        float mx = 0.f;
+        for (int r = 0; r < RPP; ++r) mx = fmaxf(mx, part[r][threadIdx.x]);
+        unsigned int* dst = reinterpret_cast<unsigned int*>(ch_amax) +
+                            ((int64_t)bh * 2 + blockIdx.z) * D + threadIdx.x;
+        atomicMax(dst, __float_as_uint(mx));
     }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        // one wave: 16 rounds of arg-max over the D scores (exact bf16 products); every
-        // lane holds the same `chosen` list
-        const int lane = threadIdx.x;
-        float sc[D / 64];
-        bool taken[D / 64];
+}
+
+// corrected mode, step 2 -- grid (B*H), one wave: the 16 channels with the largest
+// amax_q * amax_k (exact: products of bf16 values), ascending order -> hi_idx.
+template <int D>
+__global__ __launch_bounds__(64) void select_hi_kernel(const float* __restrict__ ch_amax,
+                                                      int32_t* __restrict__ hi_idx) {
+    const int bh = blockIdx.x, lane = threadIdx.x;
+    const float* qa = ch_amax + (int64_t)bh * 2 * D;
+    const float* ka = qa + D;
+    float sc[D / 64];
+    bool taken[D / 64];
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+        sc[j] = qa[lane + 64 * j] * ka[lane + 64 * j];
+        taken[j] = false;
+    }
+    // 16 rounds of arg-max (ties to the lower index); every lane ends with the same list
+    int chosen[JA_HI_CHANNELS];
+#pragma unroll
+    for (int round = 0; round < JA_HI_CHANNELS; ++round) {
+        float best = -1.f;
+        int bidx = D;
 #pragma unroll
         for (int j = 0; j < D / 64; ++j) {
-            sc[j] = amax[0][lane + 64 * j] * amax[1][lane + 64 * j];
-            taken[j] = false;
-        }
-        int chosen[JA_HI_CHANNELS];
-#pragma unroll
-        for (int round = 0; round < JA_HI_CHANNELS; ++round) {
-            float best = -1.f;
-            int bidx = D;
-#pragma unroll
-            for (int j = 0; j < D / 64; ++j) {
-                const int c = lane + 64 * j;
-                if (!taken[j] && (sc[j] > best || (sc[j] == best && c < bidx))) {
-                    best = sc[j];
-                    bidx = c;
-                }
+            const int c = lane + 64 * j;
+            if (!taken[j] && (sc[j] > best || (sc[j] == best && c < bidx))) {
+                best = sc[j];
+                bidx = c;
             }
+        }
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const float ob = __shfl_xor(best, o);
-                const int oi = __shfl_xor(bidx, o);
-                if (ob > best || (ob == best && oi < bidx)) {
-                    best = ob;
-                    bidx = oi;
-                }
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float ob = __shfl_xor(best, o);
+            const int oi = __shfl_xor(bidx, o);
+            if (ob > best || (ob == best && oi < bidx)) {
+                best = ob;
+                bidx = oi;
             }
-            chosen[round] = bidx;
-#pragma unroll
-            for (int j = 0; j < D / 64; ++j)
-                if (lane + 64 * j == bidx) taken[j] = true;
         }
-        if (lane == 0) {
-            // ascending channel order
+        chosen[round] = bidx;
 #pragma unroll
-            for (int i = 1; i < JA_HI_CHANNELS; ++i)
+        for (int j = 0; j < D / 64; ++j)
+            if (lane + 64 * j == bidx) taken[j] = true;
+    }
+    if (lane == 0) {
 #pragma unroll
-                for (int j = JA_HI_CHANNELS - 1; j >= i; --j)
-                    if (chosen[j - 1] > chosen[j]) {
-                        const int t = chosen[j];
-                        chosen[j] = chosen[j - 1];
-                        chosen[j - 1] = t;
-                    }
+        for (int i = 1; i < JA_HI_CHANNELS; ++i)          // ascending channel order
 #pragma unroll
-            for (int i = 0; i < JA_HI_CHANNELS; ++i)
-                hi_idx[(int64_t)bh * JA_HI_CHANNELS + i] = chosen[i];
-        }
+            for (int j = JA_HI_CHANNELS - 1; j >= i; --j)
+                if (chosen[j - 1] > chosen[j]) {
+                    const int t = chosen[j];
+                    chosen[j] = chosen[j - 1];
+                    chosen[j - 1] = t;
+                }
+#pragma unroll
+        for (int i = 0; i < JA_HI_CHANNELS; ++i)
+            hi_idx[(int64_t)bh * JA_HI_CHANNELS + i] = chosen[i];
     }
 }
 
@@ -209,6 +220,7 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
                                                      const int32_t* __restrict__ hi_idx,
                                                      uint16_t* __restrict__ q_hi,
                                                      uint16_t* __restrict__ k_hi) {
+    static_assert(NT % (D / 8) == 0 && (JA_QK_BLOCK * D / 8) % NT == 0, "chunk mapping");
     __shared__ float red[NT / 64];
     __shared__ uint32_t mask[D / 32];
     const uint16_t* x = blockIdx.z ? k : q;
@@ -229,21 +241,32 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
         }
     }
 
+    // the block stays in registers between the amax and the encode pass
+    constexpr int PER = JA_QK_BLOCK * D / 8 / NT;       // 16-byte chunks per thread
+    uint4 reg[PER];
     float m = 0.f;
-    for (int c = threadIdx.x; c < nch; c += NT) m = fmaxf(m, amax8(src[c]));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int c = threadIdx.x + i * NT;
+        reg[i] = c < nch ? src[c] : make_uint4(0, 0, 0, 0);
+        m = fmaxf(m, amax8(reg[i]));
+    }
     const float amax = block_max(m, red);               // (its barrier also publishes mask)
     const int e = pow2_exponent(amax);
     const float inv = ldexpf(1.f, -e);
     if (threadIdx.x == 0) sc[(int64_t)bh * nblk + blk] = ldexpf(1.f, e);
 
+    // NT is a multiple of D / 8, so a thread's chunks all cover the same 8 channels
+    uint32_t keep = 0;
+    if (SPLIT) {
+        const int c0 = (threadIdx.x % (D / 8)) * 8;
+        keep = (mask[c0 / 32] >> (c0 % 32)) & 0xFFu;
+    }
     uint2* dst = reinterpret_cast<uint2*>(y + base);
-    for (int c = threadIdx.x; c < nch; c += NT) {
-        uint32_t keep = 0;
-        if (SPLIT) {
-            const int c0 = (c % (D / 8)) * 8;           // first channel of this chunk
-            keep = (mask[c0 / 32] >> (c0 % 32)) & 0xFFu;
-        }
-        dst[c] = quant8(src[c], inv, keep);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int c = threadIdx.x + i * NT;
+        if (c < nch) dst[c] = quant8(reg[i], inv, keep);
     }
     if (SPLIT) {
         uint16_t* hi = (blockIdx.z ? k_hi : q_hi) + ((int64_t)bh * N + t0) * JA_HI_CHANNELS;
@@ -256,7 +279,25 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
     }
 }
 
-// grid: (D, B*H) -- one V^T row (b, h, channel) per workgroup
+// grid: (D, B*H) -- one V^T row (b, h, channel) per workgroup.  The first VCACHE chunks
+// per thread stay in registers between the two passes; longer rows re-read the rest.
+constexpr int VCACHE = 9;                    // 2048x2048 rows (N = 16896) fit
+
+__device__ inline uint4 v_chunk_masked(const uint4* src, int i, int nfull, int rem) {
+    // chunk i of the row with the elements at or past N zeroed (zero encodes as code 0)
+    uint4 v = src[i];
+    if (i == nfull) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (2 * q >= rem) w[q] = 0;
+            else if (2 * q + 1 >= rem) w[q] &= 0xFFFFu;
+        }
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return v;
+}
+
 __global__ __launch_bounds__(NT) void quant_v_kernel(const uint16_t* __restrict__ vt, int N,
                                                     int D, int64_t ldv,
                                                     uint8_t* __restrict__ v8t,
@@ -267,39 +308,32 @@ __global__ __launch_bounds__(NT) void quant_v_kernel(const uint16_t* __restrict_
     const uint4* src = reinterpret_cast<const uint4*>(vt + base);
     const int nfull = N / 8;                           // chunks entirely inside [0, N)
     const int rem = N - nfull * 8;
+    const int nval = nfull + (rem ? 1 : 0);            // chunks holding data
     const int nch = (int)(ldv / 8);                    // chunks in the padded row
 
+    uint4 reg[VCACHE];
     float m = 0.f;
-    for (int i = threadIdx.x; i < nfull; i += NT) m = fmaxf(m, amax8(src[i]));
-    if (rem && threadIdx.x == 0) {
-        const uint4 v = src[nfull];
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        for (int e = 0; e < rem; ++e) {
-            const uint32_t bits = (e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xFFFFu);
-            m = fmaxf(m, fabsf(__uint_as_float(bits << 16)));
-        }
+#pragma unroll
+    for (int j = 0; j < VCACHE; ++j) {
+        const int i = threadIdx.x + j * NT;
+        reg[j] = i < nval ? v_chunk_masked(src, i, nfull, rem) : make_uint4(0, 0, 0, 0);
+        m = fmaxf(m, amax8(reg[j]));
     }
+    for (int i = threadIdx.x + VCACHE * NT; i < nval; i += NT)
+        m = fmaxf(m, amax8(v_chunk_masked(src, i, nfull, rem)));
     const float amax = block_max(m, red);
     const int e = pow2_exponent(amax);
     const float inv = ldexpf(1.f, -e);
     if (threadIdx.x == 0) vs[(int64_t)bh * D + c] = ldexpf(1.f, e);
 
     uint2* dst = reinterpret_cast<uint2*>(v8t + base);
-    for (int i = threadIdx.x; i < nch; i += NT) {
-        if (i < nfull) {
-            dst[i] = quant8(src[i], inv);
-        } else if (i == nfull && rem) {
-            uint4 v = src[i];
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (int q = 0; q < 4; ++q) {              // zero the elements at or past N
-                if (2 * q >= rem) w[q] = 0;
-                else if (2 * q + 1 >= rem) w[q] &= 0xFFFFu;
-            }
-            dst[i] = quant8(make_uint4(w[0], w[1], w[2], w[3]), inv);   // zero -> code 0
-        } else {
-            dst[i] = make_uint2(0, 0);
-        }
+#pragma unroll
+    for (int j = 0; j < VCACHE; ++j) {
+        const int i = threadIdx.x + j * NT;
+        if (i < nch) dst[i] = i < nval ? quant8(reg[j], inv) : make_uint2(0, 0);
     }
+    for (int i = threadIdx.x + VCACHE * NT; i < nch; i += NT)
+        dst[i] = i < nval ? quant8(v_chunk_masked(src, i, nfull, rem), inv) : make_uint2(0, 0);
 }
 
 template <int D>
@@ -311,8 +345,13 @@ hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, 
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
     if (mode == 1) {
-        hipLaunchKernelGGL(select_hi_kernel<D>, dim3(B * H), dim3(NT), 0, stream, qq, kk, N,
-                           ch_amax, hi_idx);
+        const int n_amax = B * H * 2 * D;
+        hipLaunchKernelGGL(clear_kernel, dim3((n_amax + NT - 1) / NT), dim3(NT), 0, stream,
+                           ch_amax, n_amax);
+        hipLaunchKernelGGL(chan_amax_kernel<D>, dim3(nblk, B * H, 2), dim3(NT), 0, stream, qq,
+                           kk, N, ch_amax);
+        hipLaunchKernelGGL(select_hi_kernel<D>, dim3(B * H), dim3(64), 0, stream, ch_amax,
+                           hi_idx);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((quant_qk_kernel<D, true>), dim3(nblk, B * H, 2), dim3(NT), 0, stream,
