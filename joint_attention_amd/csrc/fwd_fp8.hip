@@ -6,51 +6,74 @@
 // K Q^T with one query per lane, O^T = V^T P^T with P^T taken from the score
 // registers), on v_mfma_f32_32x32x64_f8f6f4 (both operands e4m3).
 //
-// Scales.  A workgroup's 128 query rows are exactly one Q scale block and a 64-key
-// tile lies inside one K scale block, so scale * qs * ks * log2(e) is one factor per
-// tile, applied in the same FMA that subtracts the running maximum.  The running
-// maximum is kept as an integer (base 2), so every rescale of the accumulators is an
-// exact power of two and P's e4m3 rounding does not depend on the order keys arrive
-// in.  P is stored as e4m3(2^8 * p); the 2^8 is folded into the exponent and the row
-// sum is taken over the same 2^8-scaled fp32 values, so it cancels in O = acc / l.
-// The per-channel V scale is applied in the epilogue.
+// Work split.  One workgroup = NW waves of 32 query rows (256 rows for D = 128); keys
+// come in tiles of 64, one k-depth of the fp8 P V product.  A wave's 32 rows lie inside
+// one 128-row Q scale block and a 64-key tile inside one K scale block, so
+// scale * qs * ks * log2(e) is one factor per (lane, tile), applied in the FMA that
+// subtracts the running maximum.
+//
+// Software pipeline (as in the bf16 kernel).  Iteration j runs the softmax of tile j on
+// the vector ALU while the matrix cores run P(j-1) V(j-1) and Q K(j+1)^T, written as an
+// explicit sequence of steps (operand reads a few steps ahead, one MFMA and a slice of
+// the softmax each) separated by scheduling fences.  K, V^T (and the kept channels of
+// the split mode) are staged in registers one iteration ahead and double-buffered in
+// LDS, with one barrier per iteration.  LDS rows are XOR-swizzled so that the operand
+// reads of each lane group hit distinct banks.
+//
+// Softmax.  The running maximum M is an integer (base 2), raised only when some score
+// of the tile exceeds it (a wave-uniform ballot; the two wave halves are combined and O
+// rescaled only then), so every rescale is an exact power of two and P's e4m3 rounding
+// does not depend on the order keys arrive in.  P is stored as e4m3(2^8 * 2^(t - M)),
+// at most 256, with the 2^8 folded into the exponent; the row sum takes the same
+// unrounded fp32 numerators and the 2^8 cancels in O = acc / l.  The per-channel V
+// scale is applied in the epilogue.
 //
 // Split mode (HI): the 16 kept channels of Q and K (bf16, already divided by their
 // power-of-two block scales) add one v_mfma_f32_32x32x16_bf16 per 32x32 score block
 // into the same accumulator, so t = (q8.k8 + q_hi.k_hi) * qs * ks * scale * log2 e.
+#include <type_traits>
+
 #include "ja_device.h"
 #include "ja_launch.h"
 
 namespace ja {
 namespace {
 
-constexpr int BR = 128;          // query rows per workgroup (= one Q scale block)
-constexpr int BC = 64;           // keys per tile (half a K scale block)
-constexpr int NTHREADS = 256;
-static_assert(BR == JA_QK_BLOCK && JA_QK_BLOCK % BC == 0, "scale blocks must align with tiles");
+#ifndef FP8_LEAD
+#define FP8_LEAD 1
+#endif
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 template <int D, bool HI>
-__global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
+__global__ __launch_bounds__(D / 16 * 64, 128 / D) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8T,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     const __bf16* __restrict__ QH, const __bf16* __restrict__ KH,
     int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE,
     int n_qtiles, int total) {
+    constexpr int NW = D / 16;               // waves: one 16-byte K and V^T chunk per thread
+    constexpr int NTHREADS = NW * 64;
+    constexpr int BR = NW * 32;              // query rows per workgroup
+    constexpr int BC = 64;                   // keys per tile
+    constexpr int KB = BC / 32;              // 32-key score blocks per tile
     constexpr int KROWB = D;                 // bytes per K row
     constexpr int DC = D / 16;               // 16-byte chunks per K row
+    constexpr int KRPB = 256 / KROWB;        // K rows per 256-byte line of the 64 LDS banks
     constexpr int NQC = D / 64;              // k-steps of the QK product (64 channels each)
     constexpr int NOB = D / 32;              // 32-channel output blocks
-    constexpr int KCH = BC * DC / NTHREADS;  // K staging chunks per thread
-    constexpr int VCH = D * (BC / 16) / NTHREADS;
-    static_assert(KCH >= 1 && VCH >= 1, "tile too small for the workgroup");
-    __shared__ __attribute__((aligned(16))) uint8_t sk[BC * KROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t sv[D * BC];
-    constexpr int HC = JA_HI_CHANNELS;           // kept channels (bf16), 2 x 16 bytes per key
-    __shared__ __attribute__((aligned(16))) __bf16 skh[HI ? BC * HC : 8];
+    constexpr int VU = BC / 8;               // 8-byte units per V^T row
+    constexpr int VRPB = 256 / BC;           // V^T rows per 256-byte line
+    constexpr int HC = JA_HI_CHANNELS;       // kept channels (bf16), 2 x 16 bytes per key
+    static_assert(BC * DC == NTHREADS && D * (BC / 16) == NTHREADS, "one chunk per thread");
+    static_assert(JA_QK_BLOCK % 32 == 0 && JA_QK_BLOCK % BC == 0,
+                  "a wave's rows and a key tile must each lie in one scale block");
+    __shared__ __attribute__((aligned(16))) uint8_t sk[2][BC * KROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t sv[2][D * BC];
+    __shared__ __attribute__((aligned(16))) __bf16 skh[2][HI ? BC * HC : 8];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, hh = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, total);
     const int bh = wg / n_qtiles, qt = wg - bh * n_qtiles;
@@ -59,13 +82,66 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
     const uint8_t* Qbh = Q8 + (int64_t)bh * N * D;
     const uint8_t* Kbh = K8 + (int64_t)bh * N * D;
     const uint8_t* Vbh = V8T + (int64_t)bh * D * ldv;
-    const float qscale_c2 = QS[(int64_t)bh * nblk + qt] * c2;
+    const __bf16* KHbh = HI ? KH + (int64_t)bh * N * HC : nullptr;
+    const float* KSbh = KS + (int64_t)bh * nblk;
+    const int nkt = (N + BC - 1) / BC;
 
+    // ---- staging: thread t owns K chunk (row t / DC, chunk t % DC), V^T chunk (row
+    //      t / 4, keys 16 (t % 4) ..), and for t < 128 half a kept-channel row
+    const int kr = tid / DC, kc = tid % DC;
+    const int vr = tid / (BC / 16), vj = tid % (BC / 16);
+    uint4 kst, vst, hst = make_uint4(0, 0, 0, 0);
+    auto load_k = [&](int kt) {
+        const int k0 = kt * BC;
+        const int key = min(k0 + kr, N - 1);            // rows past N: any finite row
+        kst = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + kc * 16);
+        if (HI && tid < 2 * BC) {
+            const int hkey = k0 + tid / 2;
+            hst = make_uint4(0, 0, 0, 0);
+            if (hkey < N)
+                hst = *reinterpret_cast<const uint4*>(KHbh + (int64_t)hkey * HC + (tid % 2) * 8);
+        }
+    };
+    auto load_v = [&](int kt) {
+        const int key = kt * BC + 16 * vj;
+        if (key + 16 <= N) {
+            vst = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
+        } else {
+            vst = make_uint4(0, 0, 0, 0);
+            if (key < N) {
+                // key < N, key % 16 == 0 and ldv % 16 == 0 keep the 16 bytes in the row
+                uint4 v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
+                uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    if (key + e >= N) wv[e / 4] &= ~(0xFFu << (8 * (e % 4)));
+                vst = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            }
+        }
+    };
+    auto store_k = [&](int slot) {
+        *reinterpret_cast<uint4*>(&sk[slot][kr * KROWB + ((kc ^ ((kr / KRPB) % DC)) * 16)]) = kst;
+        if (HI && tid < 2 * BC) {
+            const int row = tid / 2, half = (tid % 2) ^ ((row >> 3) & 1);
+            *reinterpret_cast<uint4*>(&skh[slot][row * HC + half * 8]) = hst;
+        }
+    };
+    auto store_v = [&](int slot) {
+        // 16 keys of channel vr as two 8-byte units, so that lane half hh later finds
+        // its keys {16 u + 8 hh + e} as unit 2u + hh of the row
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int unit = (2 * vj + half) ^ ((vr / VRPB) % VU);
+            *reinterpret_cast<uint2*>(&sv[slot][vr * BC + unit * 8]) =
+                half ? make_uint2(vst.z, vst.w) : make_uint2(vst.x, vst.y);
+        }
+    };
+
+    // ---- resident state
     const int q_row = qt * BR + w * 32 + r32;
     const int q_ld = min(q_row, N - 1);
-    const __bf16* KHbh = HI ? KH + (int64_t)bh * N * HC : nullptr;
-    bf16x8 qhf = {};
-    if (HI) qhf = *reinterpret_cast<const bf16x8*>(QH + ((int64_t)bh * N + q_ld) * HC + 8 * hh);
+    // all rows of a wave (clamped ones included) share one Q scale block
+    const float qsc2 = QS[(int64_t)bh * nblk + q_ld / JA_QK_BLOCK] * c2;
     intx8 qf[NQC];
 #pragma unroll
     for (int c = 0; c < NQC; ++c) {
@@ -74,172 +150,250 @@ __global__ __launch_bounds__(NTHREADS, 2) void fwd_fp8_kernel(
         qf[c] = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                       (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
-
+    bf16x8 qhf = {};
+    if (HI) qhf = *reinterpret_cast<const bf16x8*>(QH + ((int64_t)bh * N + q_ld) * HC + 8 * hh);
     floatx16 oacc[NOB];
 #pragma unroll
     for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
         for (int a = 0; a < 16; ++a) oacc[ob][a] = 0.f;
-    float m = -INFINITY, l = 0.f;
+    float m = -INFINITY, l = 0.f;                 // integer running max (base 2); row sum
 
-    const int nkt = (N + BC - 1) / BC;
-    uint4 kreg[KCH], vreg[VCH], khreg = make_uint4(0, 0, 0, 0);
-
-    auto load_tile = [&](int kt) {
-        const int k0 = kt * BC;
-        const bool full = k0 + BC <= N;
+    // ---- MFMA steps.  PV step i (< NOB): A = V^T rows 32 i.. (64 keys), B = P^T.
+    //      QK step i (< NQK): c = i / KB, kb = i % KB: A = K rows kb*32.. (bits 2/3
+    //      swapped), channels 64c..; B = Q.  HI step i (< KB): A = kept channels of
+    //      K rows kb*32.., B = kept channels of Q.
+    constexpr int NPV = NOB;
+    constexpr int NQK = NQC * KB;
+    constexpr int NHI = HI ? KB : 0;
+    constexpr int NQ = NQK + NHI;
+    auto pv_operand = [&](int slot, int i) {
+        const int vrow = i * 32 + r32;
+        intx8 av;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / DC, ch = idx % DC;
-            const int key = k0 + row;
-            kreg[i] = make_uint4(0, 0, 0, 0);
-            if (full || key < N)
-                kreg[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + ch * 16);
+        for (int u = 0; u < 4; ++u) {
+            const int unit = (2 * u + hh) ^ ((vrow / VRPB) % VU);
+            const uint2 x = *reinterpret_cast<const uint2*>(&sv[slot][vrow * BC + unit * 8]);
+            av[2 * u] = (int)x.x;
+            av[2 * u + 1] = (int)x.y;
         }
-        if (HI && tid < BC * 2) {               // 2 chunks of 8 kept channels per key
-            const int key = k0 + tid / 2;
-            khreg = make_uint4(0, 0, 0, 0);
-            if (full || key < N)
-                khreg = *reinterpret_cast<const uint4*>(KHbh + (int64_t)key * HC + (tid % 2) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / (BC / 16), ch = idx % (BC / 16);
-            const int key = k0 + ch * 16;
-            vreg[i] = make_uint4(0, 0, 0, 0);
-            if (full || key < N) {
-                // key < N, key % 16 == 0 and ldv % 16 == 0 keep the 16 bytes in the row
-                uint4 v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)row * ldv + key);
-                if (!full) {
-                    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (key + e >= N) wv[e / 4] &= ~(0xFFu << (8 * (e % 4)));
-                    v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                }
-                vreg[i] = v;
-            }
-        }
+        return av;
     };
-    auto store_tile = [&]() {
-        if (HI && tid < BC * 2) {
-            const int row = tid / 2, half = (tid % 2) ^ ((row >> 3) & 1);
-            *reinterpret_cast<uint4*>(&skh[row * HC + half * 8]) = khreg;
-        }
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int idx = tid + i * NTHREADS, row = idx / DC, ch = idx % DC;
-            *reinterpret_cast<uint4*>(&sk[row * KROWB + ((ch ^ (row % DC)) * 16)]) = kreg[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            // 16 keys (16j .. 16j+15) of channel `row`, stored as two 8-byte units so that
-            // lane half hh later finds its keys {16j + 8hh + e} as 8-byte unit 2j + hh
-            const int idx = tid + i * NTHREADS, row = idx / (BC / 16), j = idx % (BC / 16);
-            const uint4 v = vreg[i];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int unit = (2 * j + half) ^ (row % 8);
-                *reinterpret_cast<uint2*>(&sv[row * BC + unit * 8]) =
-                    half ? make_uint2(v.z, v.w) : make_uint2(v.x, v.y);
-            }
-        }
-    };
-
-    load_tile(0);
-    for (int kt = 0; kt < nkt; ++kt) {
-        store_tile();
-        __syncthreads();
-        if (kt + 1 < nkt) load_tile(kt + 1);
-
-        floatx16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int a = 0; a < 16; ++a) s[kb][a] = 0.f;
+    auto q_operand = [&](int slot, int i) {
+        intx8 av;
+        if (i < NQK) {
+            const int c = i / KB, kb = i % KB;
             const int krow = kb * 32 + swap_bits23(r32);
-#pragma unroll
-            for (int c = 0; c < NQC; ++c) {
-                const int u0 = 4 * c + 2 * hh;       // two 16-byte chunks: channels 64c+32hh..+31
-                const uint4 x0 = *reinterpret_cast<const uint4*>(
-                    &sk[krow * KROWB + ((u0 ^ (krow % DC)) * 16)]);
-                const uint4 x1 = *reinterpret_cast<const uint4*>(
-                    &sk[krow * KROWB + (((u0 + 1) ^ (krow % DC)) * 16)]);
-                const intx8 av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    av, qf[c], s[kb], 0, 0, 0, 0, 0, 0);
-            }
-            if (HI) {
-                const int half = hh ^ ((krow >> 3) & 1);
-                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&skh[krow * HC + half * 8]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qhf, s[kb], 0, 0, 0);
-            }
+            const int kz = (krow / KRPB) % DC;
+            const int u0 = 4 * c + 2 * hh;            // channels 64c + 32hh .. +31
+            const uint4 x0 = *reinterpret_cast<const uint4*>(&sk[slot][krow * KROWB + ((u0 ^ kz) * 16)]);
+            const uint4 x1 =
+                *reinterpret_cast<const uint4*>(&sk[slot][krow * KROWB + (((u0 + 1) ^ kz) * 16)]);
+            av = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                       (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        } else {
+            const int kb = i - NQK;
+            const int krow = kb * 32 + swap_bits23(r32);
+            const int half = hh ^ ((krow >> 3) & 1);
+            const uint4 x = *reinterpret_cast<const uint4*>(&skh[slot][krow * HC + half * 8]);
+            av = intx8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
         }
+        return av;
+    };
 
+    floatx16 sA[KB], sB[KB];                      // score tiles, alternating with parity
+    intx8 pA, pB;                                 // P^T tiles (e4m3), alternating
+
+    auto mfma_pv = [&](int i, const intx8& av, const intx8& pf) {
+        oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pf, oacc[i], 0, 0, 0, 0,
+                                                                 0, 0);
+    };
+    auto mfma_q = [&](int i, const intx8& av, floatx16 (&s)[KB]) {
+        if (i < NQK) {
+            const int c = i / KB, kb = i % KB;
+            if (c == 0) {
+                const floatx16 zero = {};
+                s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf[c], zero, 0, 0, 0,
+                                                                       0, 0, 0);
+            } else {
+                s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf[c], s[kb], 0, 0, 0,
+                                                                       0, 0, 0);
+            }
+        } else {
+            const int kb = i - NQK;
+            const intx4 a4 = {av[0], av[1], av[2], av[3]};
+            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), qhf,
+                                                            s[kb], 0, 0, 0);
+        }
+    };
+    auto pv_all = [&](int slot, const intx8& pf) {
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) mfma_pv(i, pv_operand(slot, i), pf);
+    };
+    auto q_all = [&](int slot, floatx16 (&s)[KB]) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) mfma_q(i, q_operand(slot, i), s);
+    };
+
+    // numerators of 4 scores: k = 4 kb + d covers slots 4d .. 4d + 3 of block kb, which
+    // become word k of the P^T operand (A-operand slot s of the PV product <-> key
+    // kb*32 + 16u + 8hh + e for s = 16kb + 8u + e)
+    constexpr int NQUAD = KB * 4;
+    auto exp_quad = [&](floatx16 (&s)[KB], intx8& pf, int k, float f, float bias, float& sum) {
+        const int kb = k / 4, d = k % 4;
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[kb][4 * d + e], f, bias));
+        sum += (p[0] + p[1]) + (p[2] + p[3]);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+        asm volatile("" : "+v"(word));            // keep at this point of the schedule
+        asm volatile("" : "+v"(sum));
+        pf[k] = word;
+    };
+    auto mask_tail = [&](floatx16 (&s)[KB], int kt) {
         const int k0 = kt * BC;
-        if (k0 + BC > N) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int a = 0; a < 16; ++a) {
-                    const int key = k0 + kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8);
-                    if (key >= N) s[kb][a] = -INFINITY;
-                }
-        }
-
-        // base-2 logits t = s * f; integer running maximum
-        const float f = qscale_c2 * KS[(int64_t)bh * nblk + (k0 / JA_QK_BLOCK)];
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s[kb][a]);
-        mx = wave_halves_max(mx);
-        const float m_new = fmaxf(m, ceilf(mx * f));
-        const float alpha = (m == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m - m_new));
-        m = m_new;
-        l *= alpha;
-#pragma unroll
-        for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-            for (int a = 0; a < 16; ++a) oacc[ob][a] *= alpha;
-
-        // P^T as e4m3 of 2^8 * 2^(t - m), 32 bytes per lane: slot kb*16 + a
-        const float bias = 8.f - m;
-        intx8 pb;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                float p[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    p[e] = fast_exp2(fmaf(s[kb][4 * d + e], f, bias));
-                    l += p[e];
-                }
-                int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-                word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-                pb[4 * kb + d] = word;
+            for (int a = 0; a < 16; ++a) {
+                const int key = k0 + kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8);
+                if (key >= N) s[kb][a] = -INFINITY;
             }
+    };
 
-        // O^T += V^T P^T; A-operand slot s of half hh holds key kb*32 + 16u + 8hh + e
-        // for s = 16kb + 8u + e, i.e. the 8-byte units 2(2kb + u) + hh of the V^T row
-#pragma unroll
-        for (int ob = 0; ob < NOB; ++ob) {
-            const int vrow = ob * 32 + r32;
-            intx8 av;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int unit = (2 * j + hh) ^ (vrow % 8);
-                const uint2 x = *reinterpret_cast<const uint2*>(&sv[vrow * BC + unit * 8]);
-                av[2 * j] = (int)x.x;
-                av[2 * j + 1] = (int)x.y;
-            }
-            oacc[ob] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                av, pb, oacc[ob], 0, 0, 0, 0, 0, 0);
-        }
+    // prologue: K_0, K_1 -> LDS; S_0; stage K_2 and V_0
+    load_k(0);
+    store_k(0);
+    if (nkt > 1) {
+        load_k(1);
+        store_k(1);
+    }
+    __syncthreads();
+    q_all(0, sA);
+    load_k(min(2, nkt - 1));
+    load_v(0);
+
+    // iteration j: softmax(S_j) || P_{j-1} V_{j-1} and Q K_{j+1}^T; loads V_j, K_{j+2}
+    auto iteration = [&](int j, auto parity_tag, auto has_pv_tag, auto has_qk_tag) {
+        constexpr int P = decltype(parity_tag)::value;
+        constexpr bool HAS_PV = decltype(has_pv_tag)::value;
+        constexpr bool HAS_QK = decltype(has_qk_tag)::value;
+        constexpr int MY = P;                     // slot for K_{j+2} and V_j
+        constexpr int RD = 1 - P;                 // slot holding K_{j+1} and V_{j-1}
+        floatx16 (&s_in)[KB] = P ? sB : sA;       // S_j
+        floatx16 (&s_out)[KB] = P ? sA : sB;      // S_{j+1}
+        intx8& p_out = P ? pB : pA;               // P_j
+        intx8& p_in = P ? pA : pB;                // P_{j-1}
+        if (!HAS_QK && (N % BC) != 0) mask_tail(s_in, j);
         __syncthreads();
+        if (HAS_QK) store_k(MY);
+        store_v(MY);
+        if (HAS_QK) load_k(min(j + 3, nkt - 1));
+        load_v(min(j + 1, nkt - 1));
+
+        const float f = qsc2 * KSbh[(j * BC) / JA_QK_BLOCK];
+        float bias = 0.f, alpha = 1.f;
+        bool grow = false;
+        // raise M only if some score of the tile exceeds it (a wave-uniform branch)
+        auto check = [&]() {
+            float mx = s_in[0][0];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s_in[kb][a]);
+            const float tmax = mx * f;
+            grow = __ballot(tmax > m) != 0;
+            if (grow) {
+                asm volatile("");
+                const float m_new = fmaxf(m, ceilf(wave_halves_max(tmax)));
+                alpha = (m == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m - m_new));
+                m = m_new;
+                l *= alpha;
+            }
+            bias = 8.f - m;
+        };
+
+        constexpr int S0 = HAS_PV ? 0 : NPV;
+        constexpr int S1 = HAS_QK ? NPV + NQ : NPV;
+        constexpr int NST = S1 - S0;
+        constexpr int LEAD = FP8_LEAD;
+        constexpr int FIRST = 1;                  // steps before the numerators start
+        // step order: PV and QK steps alternate while both remain
+        auto step_id = [&](int k) -> int {
+            if constexpr (HAS_PV && HAS_QK) {
+                constexpr int PAIRS = NPV < NQ ? NPV : NQ;
+                if (k < 2 * PAIRS) return (k & 1) ? NPV + (k >> 1) : (k >> 1);
+                return NPV > NQ ? k - PAIRS : NPV + (k - PAIRS);
+            }
+            return S0 + k;
+        };
+        auto load_op = [&](int st) -> intx8 {
+            return st < NPV ? pv_operand(RD, st) : q_operand(RD, st - NPV);
+        };
+        if constexpr (NST <= FIRST) {
+            check();
+#pragma unroll
+            for (int e = 0; e < NQUAD; ++e) exp_quad(s_in, p_out, e, f, bias, l);
+            if constexpr (HAS_PV) pv_all(RD, p_in);
+            if constexpr (HAS_QK) q_all(RD, s_out);
+        } else {
+            intx8 opnd[LEAD + 1];
+#pragma unroll
+            for (int k = 0; k < LEAD; ++k) opnd[k] = load_op(step_id(k));
+#pragma unroll
+            for (int k = 0; k < NST; ++k) {
+                const int st = step_id(k);
+                if (k + LEAD < NST) opnd[(k + LEAD) % (LEAD + 1)] = load_op(step_id(k + LEAD));
+                if (st < NPV) mfma_pv(st, opnd[k % (LEAD + 1)], p_in);
+                else mfma_q(st - NPV, opnd[k % (LEAD + 1)], s_out);
+                if (k == 0) check();
+                if (k >= FIRST) {
+                    const int lo = (k - FIRST) * NQUAD / (NST - FIRST);
+                    const int hi = (k - FIRST + 1) * NQUAD / (NST - FIRST);
+#pragma unroll
+                    for (int e = lo; e < hi; ++e) exp_quad(s_in, p_out, e, f, bias, l);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // O holds P_{j-1} V_{j-1} in the old scale: rescale after those products
+        if (grow) {
+            asm volatile("");
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int a = 0; a < 16; ++a) oacc[ob][a] *= alpha;
+        }
+    };
+
+    using F = std::false_type;
+    using T = std::true_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    if (nkt == 1) {
+        iteration(0, P0{}, F{}, F{});
+    } else {
+        iteration(0, P0{}, F{}, T{});
+        int j = 1;
+        for (; j + 2 <= nkt - 1; j += 2) {
+            iteration(j, P1{}, T{}, T{});
+            iteration(j + 1, P0{}, T{}, T{});
+        }
+        if (j < nkt - 1) {
+            iteration(j, P1{}, T{}, T{});
+            ++j;
+        }
+        if (j & 1) iteration(j, P1{}, T{}, F{});
+        else iteration(j, P0{}, T{}, F{});
+    }
+
+    // epilogue: P_last V_last (V_last was stored in the last iteration)
+    {
+        const int jl = nkt - 1;
+        __syncthreads();
+        if (jl & 1) pv_all(1, pB);
+        else pv_all(0, pA);
     }
 
     const float l_tot = wave_halves_sum(l);
@@ -268,9 +422,11 @@ hipError_t launch_d(const void* q8, const void* k8, const void* v8t, const float
                     const float* ks, const float* vs, const void* qh, const void* kh, int B,
                     int H, int N, int64_t ldv, float softmax_scale, void* o, float* lse,
                     hipStream_t stream) {
+    constexpr int NW = D / 16;
+    constexpr int BR = NW * 32;
     const int n_qtiles = (N + BR - 1) / BR;
     const int total = n_qtiles * B * H;
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, HI>), dim3(total), dim3(NTHREADS), 0, stream,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, HI>), dim3(total), dim3(NW * 64), 0, stream,
                        static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
                        static_cast<const uint8_t*>(v8t), qs, ks, vs,
                        static_cast<const __bf16*>(qh), static_cast<const __bf16*>(kh), H, N, ldv,
