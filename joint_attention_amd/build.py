@@ -26,7 +26,8 @@ SOURCES = ["joint_attn.cpp", "pack.hip", "fwd_bf16.hip", "quant_fp8.hip", "fwd_f
 # two score tiles and two P tiles fit without spilling
 # (and, no NaN ever being an operand there, skips the NaN canonicalisation in front of
 # every v_max; infinities keep their meaning)
-EXTRA_FLAGS = {"fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"]}
+EXTRA_FLAGS = {"fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+               "fwd_fp8.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

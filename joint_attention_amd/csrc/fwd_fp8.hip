@@ -42,17 +42,19 @@ namespace {
 #ifndef FP8_LEAD
 #define FP8_LEAD 1
 #endif
+#ifndef FP8_NW128
+#define FP8_NW128 8
+#endif
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-template <int D, bool HI>
-__global__ __launch_bounds__(D / 16 * 64, 128 / D) void fwd_fp8_kernel(
+template <int D, int NW, bool HI>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8T,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     const __bf16* __restrict__ QH, const __bf16* __restrict__ KH,
     int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE,
     int n_qtiles, int total) {
-    constexpr int NW = D / 16;               // waves: one 16-byte K and V^T chunk per thread
     constexpr int NTHREADS = NW * 64;
     constexpr int BR = NW * 32;              // query rows per workgroup
     constexpr int BC = 64;                   // keys per tile
@@ -65,7 +67,10 @@ __global__ __launch_bounds__(D / 16 * 64, 128 / D) void fwd_fp8_kernel(
     constexpr int VU = BC / 8;               // 8-byte units per V^T row
     constexpr int VRPB = 256 / BC;           // V^T rows per 256-byte line
     constexpr int HC = JA_HI_CHANNELS;       // kept channels (bf16), 2 x 16 bytes per key
-    static_assert(BC * DC == NTHREADS && D * (BC / 16) == NTHREADS, "one chunk per thread");
+    constexpr int KCH = BC * DC / NTHREADS;  // 16-byte K chunks per thread and tile
+    constexpr int VCH = D * (BC / 16) / NTHREADS;
+    static_assert(KCH >= 1 && VCH >= 1 && KCH * NTHREADS == BC * DC &&
+                  VCH * NTHREADS == D * (BC / 16) && NTHREADS >= 2 * BC, "chunk mapping");
     static_assert(JA_QK_BLOCK % 32 == 0 && JA_QK_BLOCK % BC == 0,
                   "a wave's rows and a key tile must each lie in one scale block");
     __shared__ __attribute__((aligned(16))) uint8_t sk[2][BC * KROWB];
@@ -86,15 +91,18 @@ __global__ __launch_bounds__(D / 16 * 64, 128 / D) void fwd_fp8_kernel(
     const float* KSbh = KS + (int64_t)bh * nblk;
     const int nkt = (N + BC - 1) / BC;
 
-    // ---- staging: thread t owns K chunk (row t / DC, chunk t % DC), V^T chunk (row
-    //      t / 4, keys 16 (t % 4) ..), and for t < 128 half a kept-channel row
-    const int kr = tid / DC, kc = tid % DC;
-    const int vr = tid / (BC / 16), vj = tid % (BC / 16);
-    uint4 kst, vst, hst = make_uint4(0, 0, 0, 0);
+    // ---- staging: chunk x = tid + i * NTHREADS of a tile is K row x / DC, 16-byte
+    //      chunk x % DC, and V^T row x / 4, keys 16 (x % 4) ..; threads t < 128 also
+    //      own half a kept-channel row
+    uint4 kst[KCH], vst[VCH], hst = make_uint4(0, 0, 0, 0);
     auto load_k = [&](int kt) {
         const int k0 = kt * BC;
-        const int key = min(k0 + kr, N - 1);            // rows past N: any finite row
-        kst = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + kc * 16);
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int x = tid + i * NTHREADS, kr = x / DC, kc = x % DC;
+            const int key = min(k0 + kr, N - 1);        // rows past N: any finite row
+            kst[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + kc * 16);
+        }
         if (HI && tid < 2 * BC) {
             const int hkey = k0 + tid / 2;
             hst = make_uint4(0, 0, 0, 0);
@@ -103,24 +111,33 @@ __global__ __launch_bounds__(D / 16 * 64, 128 / D) void fwd_fp8_kernel(
         }
     };
     auto load_v = [&](int kt) {
-        const int key = kt * BC + 16 * vj;
-        if (key + 16 <= N) {
-            vst = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
-        } else {
-            vst = make_uint4(0, 0, 0, 0);
-            if (key < N) {
-                // key < N, key % 16 == 0 and ldv % 16 == 0 keep the 16 bytes in the row
-                uint4 v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
-                uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (key + e >= N) wv[e / 4] &= ~(0xFFu << (8 * (e % 4)));
-                vst = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        for (int i = 0; i < VCH; ++i) {
+            const int x = tid + i * NTHREADS, vr = x / (BC / 16), vj = x % (BC / 16);
+            const int key = kt * BC + 16 * vj;
+            if (key + 16 <= N) {
+                vst[i] = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
+            } else {
+                vst[i] = make_uint4(0, 0, 0, 0);
+                if (key < N) {
+                    // key < N, key % 16 == 0 and ldv % 16 == 0 keep the 16 bytes in the row
+                    uint4 v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
+                    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (key + e >= N) wv[e / 4] &= ~(0xFFu << (8 * (e % 4)));
+                    vst[i] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                }
             }
         }
     };
     auto store_k = [&](int slot) {
-        *reinterpret_cast<uint4*>(&sk[slot][kr * KROWB + ((kc ^ ((kr / KRPB) % DC)) * 16)]) = kst;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int x = tid + i * NTHREADS, kr = x / DC, kc = x % DC;
+            *reinterpret_cast<uint4*>(&sk[slot][kr * KROWB + ((kc ^ ((kr / KRPB) % DC)) * 16)]) =
+                kst[i];
+        }
         if (HI && tid < 2 * BC) {
             const int row = tid / 2, half = (tid % 2) ^ ((row >> 3) & 1);
             *reinterpret_cast<uint4*>(&skh[slot][row * HC + half * 8]) = hst;
@@ -130,10 +147,14 @@ __global__ __launch_bounds__(D / 16 * 64, 128 / D) void fwd_fp8_kernel(
         // 16 keys of channel vr as two 8-byte units, so that lane half hh later finds
         // its keys {16 u + 8 hh + e} as unit 2u + hh of the row
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int unit = (2 * vj + half) ^ ((vr / VRPB) % VU);
-            *reinterpret_cast<uint2*>(&sv[slot][vr * BC + unit * 8]) =
-                half ? make_uint2(vst.z, vst.w) : make_uint2(vst.x, vst.y);
+        for (int i = 0; i < VCH; ++i) {
+            const int x = tid + i * NTHREADS, vr = x / (BC / 16), vj = x % (BC / 16);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int unit = (2 * vj + half) ^ ((vr / VRPB) % VU);
+                *reinterpret_cast<uint2*>(&sv[slot][vr * BC + unit * 8]) =
+                    half ? make_uint2(vst[i].z, vst[i].w) : make_uint2(vst[i].x, vst[i].y);
+            }
         }
     };
 
@@ -245,7 +266,8 @@ __global__ __launch_bounds__(D / 16 * 64, 128 / D) void fwd_fp8_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[kb][4 * d + e], f, bias));
         sum += (p[0] + p[1]) + (p[2] + p[3]);
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        // both halves of the word are written; its old contents only save a move
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[k], false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
         asm volatile("" : "+v"(word));            // keep at this point of the schedule
         asm volatile("" : "+v"(sum));
@@ -422,11 +444,11 @@ hipError_t launch_d(const void* q8, const void* k8, const void* v8t, const float
                     const float* ks, const float* vs, const void* qh, const void* kh, int B,
                     int H, int N, int64_t ldv, float softmax_scale, void* o, float* lse,
                     hipStream_t stream) {
-    constexpr int NW = D / 16;
+    constexpr int NW = D == 128 ? FP8_NW128 : 4;
     constexpr int BR = NW * 32;
     const int n_qtiles = (N + BR - 1) / BR;
     const int total = n_qtiles * B * H;
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, HI>), dim3(total), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, HI>), dim3(total), dim3(NW * 64), 0, stream,
                        static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
                        static_cast<const uint8_t*>(v8t), qs, ks, vs,
                        static_cast<const __bf16*>(qh), static_cast<const __bf16*>(kh), H, N, ldv,
