@@ -12,6 +12,10 @@ The fp8 path (pack x3 -> joint_attn_quant_fp8 -> joint_attn_fwd_fp8) on the same
 inputs is timed the same way in its own loop and reported under "fp8".
 value = algorithmic attention flops (4 B H N^2 D) per bf16 step / step time.
 
+Under "shapes", the forward alone is timed on the other shapes: 1024^2 T2I and 2048^2 I2I
+(same generator) and one GPU's share of a Ulysses head split of 2048^2 T2I (batch 0 with
+6 or 3 of the 24 heads).
+
 Per-kernel durations come from HIP events recorded on the launch stream around every
 launch inside the timed loops.  The CPU baseline times the fp64 oracle on a bounded
 sample of query rows of the same workload on this host's cores.
@@ -73,6 +77,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
     ap.add_argument("--skip-fp8", action="store_true")
+    ap.add_argument("--skip-shapes", action="store_true",
+                    help="skip the forward-only timing of the other shapes")
     return ap.parse_args()
 
 
@@ -191,6 +197,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name), "kernel": "fwd_bf16_kernel<128>",
                      "avg_launch_ms": round(float(fwd_ms), 4),
+                     "median_launch_ms": round(float(np.median(durs[:, 1])), 4),
                      "min_launch_ms": round(float(durs[:, 1].min()), 4)},
         "kernels_ms": {"pack_qkv": round(float(pack_ms), 4), "fwd_bf16": round(float(fwd_ms), 4)},
         "pct_of_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
@@ -236,6 +243,52 @@ def main():
                 "frac_of_bf16_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
             }
             del t8
+
+    if not args.skip_shapes:
+        # forward-only throughput of the other shapes: 1024^2 T2I and 2048^2 I2I from the
+        # same generator, and one GPU's share of a Ulysses head split of 2048^2 T2I
+        # (batch element 0, the first 6 or 3 of the 24 heads: what a rank would hold)
+        def time_fwd(qq, kk, vv, steps, warmup):
+            oo = torch.empty((qq.shape[0], qq.shape[2], qq.shape[1], qq.shape[3]),
+                             dtype=torch.bfloat16, device="cuda")
+            for _ in range(warmup):
+                ja.joint_attn_fwd_bf16(qq, kk, vv, scale, out=oo)
+            evs = [(ev(), ev()) for _ in range(steps)]
+            for a, b2 in evs:
+                a.record(stream)
+                ja.joint_attn_fwd_bf16(qq, kk, vv, scale, out=oo)
+                b2.record(stream)
+            torch.cuda.synchronize()
+            return np.asarray([a.elapsed_time(b2) for a, b2 in evs])
+
+        def shape_row(wl, qq, kk, vv, steps):
+            d = time_fwd(qq, kk, vv, steps, 2)
+            fl = 4.0 * qq.shape[0] * qq.shape[1] * qq.shape[2] ** 2 * qq.shape[3]
+            tf = fl / (d.mean() * 1e-3) / 1e12
+            return {"B": int(qq.shape[0]), "H": int(qq.shape[1]), "N": int(qq.shape[2]),
+                    "stream_lens": list(wl), "fwd_bf16_ms_mean": round(float(d.mean()), 4),
+                    "fwd_bf16_ms_median": round(float(np.median(d)), 4),
+                    "fwd_bf16_ms_min": round(float(d.min()), 4),
+                    "fwd_bf16_tflops": round(tf, 2),
+                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+        shapes = {}
+        for hs, name in ((6, "ulysses4_share_t2i_2048"), (3, "ulysses8_share_t2i_2048")):
+            log("timing %s" % name)
+            shapes[name] = shape_row(w.stream_lens, q[:1, :hs].contiguous(),
+                                     k[:1, :hs].contiguous(), vt[:1, :hs].contiguous(),
+                                     args.steps)
+        for name in ("t2i_1024_bf16", "i2i_2048_bf16"):
+            w2 = synth.WORKLOADS[name]
+            log("generating and timing %s (N=%d)" % (name, w2.N))
+            st2 = synth.make_streams(w2)
+            q2, _ = ja.joint_attn_pack([dev(x) for x in st2.q], "bhnd")
+            k2, _ = ja.joint_attn_pack([dev(x) for x in st2.k], "bhnd")
+            v2, _ = ja.joint_attn_pack([dev(x) for x in st2.v], "bhdn")
+            del st2
+            shapes[name] = shape_row(w2.stream_lens, q2, k2, v2, args.steps)
+            del q2, k2, v2
+        out["shapes"] = shapes
 
     if not args.no_cpu_baseline:
         import oracle
