@@ -12,9 +12,9 @@ The fp8 path (pack x3 -> joint_attn_quant_fp8 -> joint_attn_fwd_fp8) on the same
 inputs is timed the same way in its own loop and reported under "fp8".
 value = algorithmic attention flops (4 B H N^2 D) per bf16 step / step time.
 
-Under "shapes", the forward alone is timed on the other shapes: 1024^2 T2I and 2048^2 I2I
-(same generator) and one GPU's share of a Ulysses head split of 2048^2 T2I (batch 0 with
-6 or 3 of the 24 heads).
+Under "shapes", the forward alone is timed on the other shapes: 1024^2 T2I, 2048^2 I2I and
+I2I with one or three reference images (same generator), and one GPU's share of a Ulysses
+head split of 2048^2 T2I (batch 0 with 6 or 3 of the 24 heads).
 
 Per-kernel durations come from HIP events recorded on the launch stream around every
 launch inside the timed loops.  The CPU baseline times the fp64 oracle on a bounded
@@ -278,7 +278,8 @@ def main():
             shapes[name] = shape_row(w.stream_lens, q[:1, :hs].contiguous(),
                                      k[:1, :hs].contiguous(), vt[:1, :hs].contiguous(),
                                      args.steps)
-        for name in ("t2i_1024_bf16", "i2i_2048_bf16"):
+        for name in ("t2i_1024_bf16", "i2i_2048_bf16", "i2i_1024_r1_bf16", "i2i_1024_r3_bf16",
+                     "i2i_2048_r3_bf16"):
             w2 = synth.WORKLOADS[name]
             log("generating and timing %s (N=%d)" % (name, w2.N))
             st2 = synth.make_streams(w2)

@@ -62,6 +62,13 @@ WORKLOADS = {
                  n_reference=1, outliers=4),
         Workload("t2i_2048_fp8", B=2, H=24, D=128, stream_lens=(512, 16384), outliers=4,
                  precision="fp8"),
+        # several reference images: text + target + r references of the target's size
+        Workload("i2i_1024_r1_bf16", B=2, H=24, D=128, stream_lens=(512, 4096, 4096),
+                 n_reference=1, outliers=4),
+        Workload("i2i_1024_r3_bf16", B=2, H=24, D=128,
+                 stream_lens=(512, 4096, 4096, 4096, 4096), n_reference=3, outliers=4),
+        Workload("i2i_2048_r3_bf16", B=2, H=24, D=128,
+                 stream_lens=(512, 16384, 16384, 16384, 16384), n_reference=3, outliers=4),
     ]
 }
 
