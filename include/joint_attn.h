@@ -11,7 +11,8 @@
  * This library computes it as unmasked scaled-dot-product attention,
  *     O = softmax(Q K^T * softmax_scale) V        (per batch b and head h),
  * in four calls: pack the streams, then either the bf16 forward, or the fp8 quantiser
- * followed by the fp8 forward.
+ * followed by the fp8 forward; joint_attn_fwd_bf16_streams does pack and bf16 forward in
+ * one call, reading the streams in place.
  *
  * Conventions for every call.
  *   - Tensor pointers are DEVICE pointers (HBM) owned by the caller; the library never
@@ -105,6 +106,30 @@ int joint_attn_pack(int n_streams, const void *const *src, const int64_t *lens,
 int joint_attn_fwd_bf16(const void *q, const void *k, const void *vt,
                         int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
                         void *o, float *lse, void *stream);
+
+/*
+ * joint_attn_fwd_bf16_streams -- the same attention as joint_attn_fwd_bf16, reading Q, K
+ * and V in place from the per-stream tensors instead of packed copies: the joint
+ * sequence of the VisualGen FLUX 3 article (everytik.com translation, section
+ * 使用 TensorRT LLM VisualGen 进行 FLUX 3 推理: text, noisy target and reference streams
+ * processed apart and joined only in attention) is formed by the kernel's own loads, so
+ * no pack step is needed.  Results are bit-identical to joint_attn_pack (x3) followed
+ * by joint_attn_fwd_bf16 on the same streams.
+ *
+ *   n_streams   1..JA_MAX_STREAMS, in joint-sequence order (text, target, references)
+ *   q, k, v     host arrays of n_streams device pointers; stream s is bf16 BNHD
+ *               [B][lens[s]][H][D] (a zero-length stream may pass NULL); 16-byte aligned
+ *   lens        host array of n_streams token counts (>= 0); N = sum of lens
+ *   o           bf16 BNHD [B][N][H][D] (stream s's output is rows offsets[s] ..
+ *               offsets[s+1]-1 of every batch)
+ *   lse         fp32 [B][H][N] natural-log log-sum-exp per query row, or NULL
+ *   offsets     host output, n_streams + 1 entries as in joint_attn_pack, or NULL;
+ *               written whenever the arguments are valid, also for N == 0
+ */
+int joint_attn_fwd_bf16_streams(int n_streams, const void *const *q, const void *const *k,
+                                const void *const *v, const int64_t *lens,
+                                int B, int H, int D, float softmax_scale,
+                                void *o, float *lse, int64_t *offsets, void *stream);
 
 /*
  * joint_attn_quant_fp8 -- quantise packed bf16 Q, K, V to e4m3 with dequantisation

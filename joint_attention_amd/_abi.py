@@ -24,7 +24,8 @@ JA_HI_CHANNELS = 16
 JA_FP8_PLAIN, JA_FP8_SPLIT = 0, 1
 
 EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
-           "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_quant_fp8",
+           "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_streams",
+           "joint_attn_quant_fp8",
            "joint_attn_fwd_fp8")
 
 _lock = threading.Lock()
@@ -61,6 +62,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_pack.argtypes = [I, P, P, I, I, I, I, I64, P, P, P]
         h.joint_attn_fwd_bf16.restype = I
         h.joint_attn_fwd_bf16.argtypes = [P, P, P, I, I, I64, I, I64, F, P, P, P]
+        h.joint_attn_fwd_bf16_streams.restype = I
+        h.joint_attn_fwd_bf16_streams.argtypes = [I, P, P, P, P, I, I, I, F,
+                                                  P, P, P, P]
         h.joint_attn_quant_fp8.restype = I
         h.joint_attn_quant_fp8.argtypes = [P, P, P, I, I, I64, I, I64, I, P, P, P, P, P, P,
                                            P, P, P, P, P]
@@ -161,6 +165,41 @@ def joint_attn_fwd_bf16(q, k, vt, softmax_scale: float | None = None, out=None,
                                     lse.data_ptr() if lse is not None else None, _stream(q))
     _check("joint_attn_fwd_bf16", st)
     return (out, lse) if return_lse else out
+
+
+def joint_attn_fwd_bf16_streams(q_streams, k_streams, v_streams,
+                                softmax_scale: float | None = None, out=None,
+                                return_lse: bool = False):
+    """Attention over the concatenation of per-stream bf16 [B, L_s, H, D] tensors, read in
+    place.  Returns (O [B, N, H, D], offsets) (and lse [B, H, N] if asked)."""
+    torch = _torch()
+    qs, ks, vs = list(q_streams), list(k_streams), list(v_streams)
+    n = len(qs)
+    if not 1 <= n <= JA_MAX_STREAMS or len(ks) != n or len(vs) != n:
+        raise ValueError("need 1..%d streams, the same number for q, k and v" % JA_MAX_STREAMS)
+    B, _, H, D = qs[0].shape
+    dev = qs[0].device
+    for i in range(n):
+        for t, nm in ((qs[i], "q"), (ks[i], "k"), (vs[i], "v")):
+            _need(t, torch.bfloat16, "%s stream %d" % (nm, i), 4)
+            if (t.shape[0], t.shape[2], t.shape[3]) != (B, H, D) or t.shape[1] != qs[i].shape[1] \
+                    or t.device != dev:
+                raise ValueError("streams must share B, H, D, lengths per stream and device")
+    N = sum(int(x.shape[1]) for x in qs)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", 4)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
+    ptr = lambda lst: (ctypes.c_void_p * n)(*[x.data_ptr() if x.numel() else None for x in lst])
+    lens = (ctypes.c_int64 * n)(*[int(x.shape[1]) for x in qs])
+    offs = (ctypes.c_int64 * (n + 1))()
+    st = load().joint_attn_fwd_bf16_streams(n, ptr(qs), ptr(ks), ptr(vs), lens, B, H, D, scale,
+                                            out.data_ptr() if out.numel() else None,
+                                            lse.data_ptr() if lse is not None else None, offs,
+                                            _stream(out))
+    _check("joint_attn_fwd_bf16_streams", st)
+    return (out, list(offs), lse) if return_lse else (out, list(offs))
 
 
 class Fp8Tensors:

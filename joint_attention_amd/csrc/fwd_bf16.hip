@@ -59,17 +59,23 @@ namespace {
 #ifndef FWD_LEAD
 #define FWD_LEAD 3
 #endif
+#ifndef FWD_TW
+#define FWD_TW 3
+#endif
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 // NW: waves per workgroup (each owns QB 32-row query blocks); BC: keys per tile.  With
 // NW * QB = 8 one workgroup covers 256 query rows, so every K/V tile loaded into LDS
 // serves 256 rows, and two waves share each SIMD.
-template <int D, int NW, int QB, int BC>
+// GATHER: Q, K and V are read in place from the per-stream tensors of `st` (token-major
+// [B][L_s][H][D]) instead of the packed Q, K (BHND) and V^T (BHDN); V tiles are then kept
+// token-major in LDS and read with transposing LDS loads.
+template <int D, int NW, int QB, int BC, bool GATHER>
 __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ VT,
-    int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE,
-    int n_qtiles, int total) {
+    const StreamTable st, int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O,
+    float* __restrict__ LSE, int n_qtiles, int total) {
     constexpr int NTHREADS = NW * 64;
     constexpr int BR = NW * QB * 32;             // query rows per workgroup
     constexpr int KB = BC / 32;                  // 32-key blocks per tile
@@ -82,10 +88,15 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     constexpr int LOADS = TILE_ELEMS * 2 / 1024 / (NTHREADS / 64);   // 1 KB loads per wave
     static_assert(LOADS >= 1, "tile smaller than one load per wave");
     constexpr float kLazy = 16.f;
+    constexpr int GSEG = D / 32;                 // 64-byte segments per token-major V row
+    constexpr int GRPL = 128 / D;                // token-major V rows per 256-byte line
     __shared__ __attribute__((aligned(1024))) __bf16 sk0[TILE_ELEMS];
     __shared__ __attribute__((aligned(1024))) __bf16 sk1[TILE_ELEMS];
     __shared__ __attribute__((aligned(1024))) __bf16 sv0[TILE_ELEMS];
     __shared__ __attribute__((aligned(1024))) __bf16 sv1[TILE_ELEMS];
+    // GATHER: token-major V tiles, transposed into sv0 / sv1 one iteration later
+    __shared__ __attribute__((aligned(1024))) __bf16 st0[GATHER ? TILE_ELEMS : 8];
+    __shared__ __attribute__((aligned(1024))) __bf16 st1[GATHER ? TILE_ELEMS : 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
@@ -98,6 +109,41 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const __bf16* Vbh = VT + (int64_t)bh * D * ldv;
     const int nkt = (N + BC - 1) / BC;
 
+    // GATHER: packed token n -> its row (b, n - off[s], h) of stream s's tensor
+    auto stream_of = [&](int n) {
+        int s = 0;
+        for (int i = 1; i < st.n; ++i)
+            if (n >= st.off[i]) s = i;           // zero-length streams share the next start
+        return s;
+    };
+    auto stream_row = [&](const void* const* src, int s, int n) -> const __bf16* {
+        const int64_t L = st.off[s + 1] - st.off[s];
+        return static_cast<const __bf16*>(src[s]) +
+               (((int64_t)b * L + (n - st.off[s])) * H + h) * (int64_t)D;
+    };
+    const int64_t row_pitch = GATHER ? (int64_t)H * D : D;   // elements between tokens
+    // GATHER: tiles are visited in order, so each tensor keeps a cursor on the stream that
+    // holds its current tile; the stream table is read only when a tile crosses into the
+    // next stream (reads of it inside the loop would also stall the LDS-operand waits)
+    struct Cursor {
+        int s, start, end;               // stream s holds packed tokens [start, end)
+        const __bf16* row0;              // its row for packed token `start`
+    };
+    auto cursor_init = [&](const void* const* src) {
+        Cursor c{0, 0, (int)st.off[1], nullptr};
+        if (GATHER) c.row0 = stream_row(src, 0, 0);
+        return c;
+    };
+    auto advance = [&](Cursor& c, const void* const* src, int key) {   // key >= c.start
+        while (key >= c.end && c.s + 1 < st.n) {
+            ++c.s;
+            c.start = c.end;
+            c.end = (int)st.off[c.s + 1];
+            c.row0 = stream_row(src, c.s, c.start);
+        }
+    };
+    Cursor kcur = cursor_init(st.k), vcur = cursor_init(st.v);
+
     // ---- K / V^T tile loads, staged through registers: lane `lane` of wave w owns
     //      tile bytes (w*LOADS + i) * 1024 + 16 * lane; the swizzle is inverted on the
     //      global side, so the LDS store is one linear 16-byte write per chunk
@@ -106,20 +152,47 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         const int off = (w * LOADS + i) * 1024 + lane * 16;
         return ((off % (2 * D)) / 16) ^ ((off / (2 * D)) % DC);
     };
-    auto v_row = [&](int i) { return ((w * LOADS + i) * 1024 + lane * 16) / (2 * BC); };
+    auto v_row = [&](int i) {
+        const int off = (w * LOADS + i) * 1024 + lane * 16;
+        return GATHER ? off / (2 * D) : off / (2 * BC);
+    };
     auto v_chunk = [&](int i) {
         const int off = (w * LOADS + i) * 1024 + lane * 16;
+        if constexpr (GATHER) {
+            // token-major V tile: the 64-byte segments of each key row are rotated by
+            // (key / GRPL) % GSEG (conflict-free for the transposing reads)
+            return ((off % (2 * D)) / 16) ^ ((((off / (2 * D)) / GRPL) % GSEG) * 4);
+        }
         return ((off % (2 * BC)) / 16) ^ (((off / (2 * BC)) / VRPB) % VCPR);
     };
     uint32_t k_off[LOADS], v_off[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-        k_off[i] = (uint32_t)(k_row(i) * D + k_chunk(i) * 8) * 2u;
-        v_off[i] = (uint32_t)(v_row(i) * (int)ldv + v_chunk(i) * 8) * 2u;
+        k_off[i] = (uint32_t)(k_row(i) * row_pitch + k_chunk(i) * 8) * 2u;
+        v_off[i] = GATHER ? (uint32_t)(v_row(i) * row_pitch + v_chunk(i) * 8) * 2u
+                          : (uint32_t)(v_row(i) * (int)ldv + v_chunk(i) * 8) * 2u;
     }
     uint4 kst[LOADS], vst[LOADS];                 // staged tiles (global -> registers)
     auto load_k = [&](int kt) {
         const int k0 = kt * BC;
+        if constexpr (GATHER) {
+            advance(kcur, st.k, k0);                            // wave-uniform
+            if (k0 + BC <= kcur.end) {                          // the tile lies in one stream
+                const char* base = reinterpret_cast<const char*>(
+                    kcur.row0 + (int64_t)(k0 - kcur.start) * row_pitch);
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i)
+                    kst[i] = *reinterpret_cast<const uint4*>(base + k_off[i]);
+            } else {                                            // straddles streams or N
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    const int key = min(k0 + k_row(i), N - 1);  // rows past N: any finite row
+                    kst[i] = *reinterpret_cast<const uint4*>(
+                        stream_row(st.k, stream_of(key), key) + k_chunk(i) * 8);
+                }
+            }
+            return;
+        }
         if (k0 + BC <= N) {
             const char* base = reinterpret_cast<const char*>(Kbh + (int64_t)k0 * D);
 #pragma unroll
@@ -135,6 +208,26 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     };
     auto load_v = [&](int kt) {
         const int k0 = kt * BC;
+        if constexpr (GATHER) {
+            // token-major rows as for K; rows past N repeat row N-1 (finite, and their
+            // probabilities are exactly zero)
+            advance(vcur, st.v, k0);
+            if (k0 + BC <= vcur.end) {
+                const char* base = reinterpret_cast<const char*>(
+                    vcur.row0 + (int64_t)(k0 - vcur.start) * row_pitch);
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i)
+                    vst[i] = *reinterpret_cast<const uint4*>(base + v_off[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    const int key = min(k0 + v_row(i), N - 1);
+                    vst[i] = *reinterpret_cast<const uint4*>(
+                        stream_row(st.v, stream_of(key), key) + v_chunk(i) * 8);
+                }
+            }
+            return;
+        }
         if (k0 + BC <= N) {
             const char* base = reinterpret_cast<const char*>(Vbh + k0);
 #pragma unroll
@@ -166,6 +259,33 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         for (int i = 0; i < LOADS; ++i)
             *reinterpret_cast<uint4*>(slot + (w * LOADS + i) * 512 + lane * 8) = kst[i];
     };
+    // GATHER: V^T chunk (row c, keys 8u .. 8u + 7) of a token-major tile in `ts`, one per
+    // thread: in each 16-lane group, lane k points at key 8u + 4 half + (k >> 2), channels
+    // 4 (k & 3) .. + 3 of the group's 16 channels; the transposing read hands lane r the 4
+    // keys of channel c0 + r.  Written later to `vs` in the V^T layout of the operand reads
+    // (the write waits for the reads, so it is placed a few MFMA steps after them).
+    auto transpose_read = [&](const __bf16* ts) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const int grp = tid >> 4, i16 = tid & 15;
+        const int c0 = (grp % (D / 16)) * 16, u = grp / (D / 16);
+        const int a = i16 & 3, jj = i16 >> 2;
+        v4s r[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int key = 8 * u + 4 * half + jj;               // (key / GRPL) % GSEG
+            const int byte = key * (2 * D) + (((c0 + 4 * a) * 2) ^ (((jj / GRPL) % GSEG) * 64));
+            r[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(reinterpret_cast<const char*>(ts) +
+                                                         byte));
+        }
+        return uint4{__builtin_bit_cast(uint2, r[0]).x, __builtin_bit_cast(uint2, r[0]).y,
+                     __builtin_bit_cast(uint2, r[1]).x, __builtin_bit_cast(uint2, r[1]).y};
+    };
+    auto transpose_write = [&](const uint4& x, __bf16* vs) {
+        const int grp = tid >> 4, i16 = tid & 15;
+        const int row = (grp % (D / 16)) * 16 + i16, u = grp / (D / 16);
+        *reinterpret_cast<uint4*>(vs + row * BC + ((u ^ ((row / VRPB) % VCPR)) * 8)) = x;
+    };
     auto store_v = [&](__bf16* slot) {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
@@ -178,10 +298,11 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int q_ld = min(q_base + 32 * qb, N - 1);
+        const __bf16* qrow = GATHER ? stream_row(st.q, stream_of(q_ld), q_ld)
+                                    : Qbh + (int64_t)q_ld * D;
 #pragma unroll
         for (int c = 0; c < NQC; ++c)
-            qf[qb][c] =
-                *reinterpret_cast<const bf16x8*>(Qbh + (int64_t)q_ld * D + 16 * c + 8 * hh);
+            qf[qb][c] = *reinterpret_cast<const bf16x8*>(qrow + 16 * c + 8 * hh);
     }
     floatx16 oacc[QB][NOB];
 #pragma unroll
@@ -303,7 +424,14 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     __syncthreads();
     qk_all(sk0, sA);
     load_k(min(2, nkt - 1));
-    load_v(0);
+    if constexpr (GATHER) {
+        // V_0 token-major before the first barrier; V_1 staged for iteration 0
+        load_v(0);
+        store_v(st0);
+        load_v(min(1, nkt - 1));
+    } else {
+        load_v(0);
+    }
 
     // iteration j: softmax(S_j) || P_{j-1} V_{j-1} and Q K_{j+1}^T; loads V_j, K_{j+2}
     auto iteration = [&](int j, auto parity_tag, auto has_pv_tag, auto has_qk_tag) {
@@ -323,9 +451,17 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         // the staged K_{j+2} and V_j go to the slots freed by the barrier; then stage
         // K_{j+3} and V_{j+1} (indices past the end reload the last tile, unused)
         if (HAS_QK) store_k(my_k);
-        store_v(my_v);
+        // GATHER: V_{j+1} token-major into the free staging slot; V_j (staged last
+        // iteration) read transposed now, written to the V^T slot during the steps
+        uint4 vtr = {};
+        if constexpr (GATHER) {
+            store_v(P ? st0 : st1);
+            vtr = transpose_read(P ? st1 : st0);
+        } else {
+            store_v(my_v);
+        }
         if (HAS_QK) load_k(min(j + 3, nkt - 1));
-        load_v(min(j + 1, nkt - 1));
+        load_v(min(j + (GATHER ? 2 : 1), nkt - 1));
 
         constexpr int S0 = HAS_PV ? 0 : NPV;           // first MFMA step
         constexpr int S1 = HAS_QK ? NPV + NQK : NPV;   // one past the last step
@@ -374,6 +510,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
             for (int e = 0; e < NEXP; ++e) exp_pair(s_in, p_out, e, nm, l);
             if constexpr (HAS_PV) pv_all(rd_v, p_in);
             if constexpr (HAS_QK) qk_all(rd_k, s_out);
+            if constexpr (GATHER) transpose_write(vtr, my_v);
         } else {
             bf16x8 opnd[LEAD + 1];
 #pragma unroll
@@ -384,6 +521,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                 if (k + LEAD < NST) opnd[(k + LEAD) % (LEAD + 1)] = load_op(step_id(k + LEAD));
                 if (st < NPV) mfma_pv(st, opnd[k % (LEAD + 1)], p_in);
                 else mfma_qk(st - NPV, opnd[k % (LEAD + 1)], s_out);
+                if (GATHER && k == (NST > FWD_TW ? FWD_TW : NST - 1)) transpose_write(vtr, my_v);
                 // softmax slice: offset check first, then numerators
                 if (k < QB) check(k);
                 if (k >= FIRST) {
@@ -459,15 +597,16 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     }
 }
 
-template <int D, int NW, int QB, int BC>
-hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, int N,
-                    int64_t ldv, float softmax_scale, void* o, float* lse, hipStream_t stream) {
+template <int D, int NW, int QB, int BC, bool GATHER>
+hipError_t launch_d(const void* q, const void* k, const void* vt, const StreamTable& st, int B,
+                    int H, int N, int64_t ldv, float softmax_scale, void* o, float* lse,
+                    hipStream_t stream) {
     constexpr int BR = NW * QB * 32;
     const int n_qtiles = (N + BR - 1) / BR;
     const int total = n_qtiles * B * H;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BC>), dim3(total), dim3(NW * 64), 0, stream,
-                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                       static_cast<const __bf16*>(vt), H, N, ldv, softmax_scale * kLog2e,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BC, GATHER>), dim3(total), dim3(NW * 64), 0,
+                       stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                       static_cast<const __bf16*>(vt), st, H, N, ldv, softmax_scale * kLog2e,
                        static_cast<__bf16*>(o), lse, n_qtiles, total);
     return hipGetLastError();
 }
@@ -478,10 +617,21 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, 
                            int D, int64_t ldv, float softmax_scale, void* o, float* lse,
                            hipStream_t stream) {
     // head size 64 (4 KB tiles) keeps 4 waves so that each wave still moves whole 1 KB loads
-    return D == 64
-        ? launch_d<64, 4, FWD_QB, FWD_BC>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse, stream)
-        : launch_d<128, FWD_NW, FWD_QB, FWD_BC>(q, k, vt, B, H, N, ldv, softmax_scale, o, lse,
-                                                stream);
+    const StreamTable none{};
+    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, false>(q, k, vt, none, B, H, N, ldv,
+                                                            softmax_scale, o, lse, stream)
+                   : launch_d<128, FWD_NW, FWD_QB, FWD_BC, false>(q, k, vt, none, B, H, N, ldv,
+                                                                  softmax_scale, o, lse, stream);
+}
+
+hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,
+                                   float softmax_scale, void* o, float* lse,
+                                   hipStream_t stream) {
+    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, true>(nullptr, nullptr, nullptr, st, B, H, N,
+                                                           0, softmax_scale, o, lse, stream)
+                   : launch_d<128, FWD_NW, FWD_QB, FWD_BC, true>(nullptr, nullptr, nullptr, st, B,
+                                                                 H, N, 0, softmax_scale, o, lse,
+                                                                 stream);
 }
 
 }  // namespace ja

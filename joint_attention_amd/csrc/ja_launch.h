@@ -5,7 +5,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "joint_attn.h"
+
 namespace ja {
+
+// Per-stream source tensors of one joint sequence (Q, K and V, each bf16 [B][L_s][H][D])
+// with the packed offsets: stream s holds packed tokens off[s] .. off[s+1]-1.  Passed to
+// kernels by value.
+struct StreamTable {
+    const void* q[JA_MAX_STREAMS];
+    const void* k[JA_MAX_STREAMS];
+    const void* v[JA_MAX_STREAMS];
+    int64_t off[JA_MAX_STREAMS + 1];
+    int n;
+};
 
 hipError_t launch_pack(int n_streams, const void* const* src, const int64_t* offsets, int B,
                        int H, int D, int layout, int64_t ld, void* dst, hipStream_t stream);
@@ -13,6 +26,10 @@ hipError_t launch_pack(int n_streams, const void* const* src, const int64_t* off
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, int H, int N,
                            int D, int64_t ldv, float softmax_scale, void* o, float* lse,
                            hipStream_t stream);
+
+hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,
+                                   float softmax_scale, void* o, float* lse,
+                                   hipStream_t stream);
 
 hipError_t launch_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int N,
                             int D, int64_t ldv, int mode, void* q8, void* k8, void* v8t,

@@ -95,6 +95,40 @@ int joint_attn_fwd_bf16(const void* q, const void* k, const void* vt, int B, int
                                           static_cast<hipStream_t>(stream)));
 }
 
+int joint_attn_fwd_bf16_streams(int n_streams, const void* const* q, const void* const* k,
+                                const void* const* v, const int64_t* lens, int B, int H, int D,
+                                float softmax_scale, void* o, float* lse, int64_t* offsets,
+                                void* stream) {
+    if (n_streams <= 0 || !q || !k || !v || !lens) return JA_EINVAL;
+    if (n_streams > JA_MAX_STREAMS) return JA_EUNSUPPORTED;
+    ja::StreamTable st{};
+    st.n = n_streams;
+    st.off[0] = 0;
+    for (int s = 0; s < n_streams; ++s) {
+        if (lens[s] < 0 || lens[s] > kMaxInt) return JA_EINVAL;
+        if (lens[s] > 0) {
+            if (!q[s] || !k[s] || !v[s]) return JA_EINVAL;
+            if (!aligned16(q[s]) || !aligned16(k[s]) || !aligned16(v[s])) return JA_EUNSUPPORTED;
+            st.q[s] = q[s];
+            st.k[s] = k[s];
+            st.v[s] = v[s];
+        }
+        st.off[s + 1] = st.off[s] + lens[s];
+    }
+    const int64_t N = st.off[n_streams];
+    const int sh = check_shape(B, H, N, D, joint_attn_vt_ld(N));
+    if (sh != JA_OK) return sh;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (offsets)
+        for (int s = 0; s <= n_streams; ++s) offsets[s] = st.off[s];
+    if (N == 0) return JA_OK;
+    if (!o) return JA_EINVAL;
+    if (!aligned16(o)) return JA_EUNSUPPORTED;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
+    return hip_status(ja::launch_fwd_bf16_streams(st, B, H, (int)N, D, softmax_scale, o, lse,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int joint_attn_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int64_t N,
                          int D, int64_t ldv, int mode, void* q8, void* k8, void* v8t,
                          float* q_scale, float* k_scale, float* v_scale, void* q_hi, void* k_hi,

@@ -102,3 +102,31 @@ def test_python_binding_rejects_cpu_tensors(lib):
     x = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ja.joint_attn_pack([x])
+
+
+def test_fwd_streams_validation(lib):
+    fake = 0x10000
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+
+    def call(n, q, k, v, lens, B=1, H=2, D=128, scale=0.1, o=fake, lse=None):
+        arr = lambda xs: (P * max(n, 1))(*xs) if xs is not None else None
+        ln = (I64 * max(n, 1))(*lens) if lens is not None else None
+        offs = (I64 * (max(n, 1) + 1))()
+        st = lib.joint_attn_fwd_bf16_streams(n, arr(q), arr(k), arr(v), ln, B, H, D, scale, o,
+                                             lse, offs, None)
+        return st, list(offs)
+
+    two = [fake, fake]
+    assert call(0, [], [], [], [])[0] == 1
+    assert call(17, [fake] * 17, [fake] * 17, [fake] * 17, [1] * 17)[0] == 2
+    assert call(2, two, two, two, [4, 4], D=96)[0] == 2
+    assert call(2, two, two, two, [4, -1])[0] == 1
+    assert call(2, two, [fake, None], two, [4, 4])[0] == 1                # NULL non-empty k
+    assert call(2, two, two, [fake, fake + 8], [4, 4])[0] == 2            # misaligned v
+    assert call(2, two, two, two, [4, 4], o=None)[0] == 1
+    assert call(2, two, two, two, [4, 4], o=fake + 2)[0] == 2
+    assert call(2, two, two, two, [4, 4], scale=float("inf"))[0] == 1
+    assert call(2, two, two, two, [4, 4], B=0)[0] == 1
+    # empty streams are a successful no-op that still reports the offsets
+    st, offs = call(3, [None] * 3, [None] * 3, [None] * 3, [0, 0, 0], o=None)
+    assert st == 0 and offs == [0, 0, 0, 0]
