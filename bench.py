@@ -269,6 +269,34 @@ def main():
             }
             del t8
 
+            # the same fp8 step with the quantiser reading the streams in place (no pack)
+            t8s, _ = ja.joint_attn_quant_fp8_streams(qs_d, ks_d, vs_d, mode)
+
+            def step_fp8s(rec, mode=mode, t8s=t8s):
+                e = [ev() for _ in range(3)] if rec else None
+                if rec:
+                    e[0].record(stream)
+                ja.joint_attn_quant_fp8_streams(qs_d, ks_d, vs_d, mode, out=t8s)
+                if rec:
+                    e[1].record(stream)
+                ja.joint_attn_fwd_fp8(t8s, scale, out=o)
+                if rec:
+                    e[2].record(stream)
+                return e
+
+            log("timing fp8 path from the streams, mode %d (%s)" % (mode, name))
+            wall8s, durs8s = timed(step_fp8s, args.steps, args.warmup)
+            ms8s = wall8s * 1e3 / args.steps
+            qn8s, f8s = durs8s.mean(axis=0)
+            out["fp8"][name + "_streams"] = {
+                "mode": mode, "step": "quant_fp8_streams + fwd_fp8 (no pack)",
+                "value": round(flops / (ms8s * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(ms8s, 4),
+                "kernels_ms": {"quant_fp8_streams": round(float(qn8s), 4),
+                               "fwd_fp8": round(float(f8s), 4)},
+            }
+            del t8s
+
     if not args.skip_shapes:
         # forward-only throughput of the other shapes: 1024^2 T2I and 2048^2 I2I from the
         # same generator, and one GPU's share of a Ulysses head split of 2048^2 T2I

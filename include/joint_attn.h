@@ -172,6 +172,22 @@ int joint_attn_quant_fp8(const void *q, const void *k, const void *vt,
                          void *stream);
 
 /*
+ * joint_attn_quant_fp8_streams -- joint_attn_quant_fp8 reading Q, K and V in place from
+ * the per-stream tensors (laid out and passed as for joint_attn_fwd_bf16_streams), so the
+ * fp8 path needs no bf16 pack step either.  The outputs (packed e4m3 codes, V^T codes with
+ * pitch ldv, scales, and in mode 1 the kept channels) are bit-identical to those of
+ * joint_attn_pack followed by joint_attn_quant_fp8 on the same streams.  `offsets` (host,
+ * n_streams + 1 entries, or NULL) receives the stream offsets as in joint_attn_pack.
+ */
+int joint_attn_quant_fp8_streams(int n_streams, const void *const *q, const void *const *k,
+                                 const void *const *v, const int64_t *lens,
+                                 int B, int H, int D, int64_t ldv, int mode,
+                                 void *q8, void *k8, void *v8t,
+                                 float *q_scale, float *k_scale, float *v_scale,
+                                 void *q_hi, void *k_hi, int32_t *hi_idx, float *ch_amax,
+                                 int64_t *offsets, void *stream);
+
+/*
  * joint_attn_fwd_fp8 -- attention on the e4m3 operands of joint_attn_quant_fp8.
  *   QK^T on fp8 matrix cores with fp32 accumulation (mode 1 adds the kept channels on a
  *   bf16 MFMA into the same accumulator); per-block Q/K scales and softmax_scale are

@@ -25,7 +25,7 @@ JA_FP8_PLAIN, JA_FP8_SPLIT = 0, 1
 
 EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
            "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_streams",
-           "joint_attn_quant_fp8",
+           "joint_attn_quant_fp8", "joint_attn_quant_fp8_streams",
            "joint_attn_fwd_fp8")
 
 _lock = threading.Lock()
@@ -68,6 +68,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_quant_fp8.restype = I
         h.joint_attn_quant_fp8.argtypes = [P, P, P, I, I, I64, I, I64, I, P, P, P, P, P, P,
                                            P, P, P, P, P]
+        h.joint_attn_quant_fp8_streams.restype = I
+        h.joint_attn_quant_fp8_streams.argtypes = [I, P, P, P, P, I, I, I, I64, I, P, P, P, P, P,
+                                                   P, P, P, P, P, P, P]
         h.joint_attn_fwd_fp8.restype = I
         h.joint_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, I, I64, I, I64, F, I, P, P, P, P,
                                          P]
@@ -242,6 +245,43 @@ def joint_attn_quant_fp8(q, k, vt, mode: int = JA_FP8_PLAIN, out: Fp8Tensors | N
         _ptr(out.hi_idx), _ptr(out.ch_amax), _stream(q))
     _check("joint_attn_quant_fp8", st)
     return out
+
+
+def joint_attn_quant_fp8_streams(q_streams, k_streams, v_streams, mode: int = JA_FP8_PLAIN,
+                                 out: Fp8Tensors | None = None):
+    """joint_attn_quant_fp8 on the concatenation of per-stream bf16 [B, L_s, H, D] tensors,
+    read in place.  Returns (Fp8Tensors, offsets)."""
+    torch = _torch()
+    qs, ks, vs = list(q_streams), list(k_streams), list(v_streams)
+    n = len(qs)
+    if not 1 <= n <= JA_MAX_STREAMS or len(ks) != n or len(vs) != n:
+        raise ValueError("need 1..%d streams, the same number for q, k and v" % JA_MAX_STREAMS)
+    B, _, H, D = qs[0].shape
+    dev = qs[0].device
+    for i in range(n):
+        for t, nm in ((qs[i], "q"), (ks[i], "k"), (vs[i], "v")):
+            _need(t, torch.bfloat16, "%s stream %d" % (nm, i), 4)
+            if (t.shape[0], t.shape[2], t.shape[3]) != (B, H, D) or t.shape[1] != qs[i].shape[1] \
+                    or t.device != dev:
+                raise ValueError("streams must share B, H, D, lengths per stream and device")
+    N = sum(int(x.shape[1]) for x in qs)
+    ldv = joint_attn_vt_ld(N)
+    nblk = -(-N // JA_QK_BLOCK)
+    if out is not None:
+        if out.mode != mode or tuple(out.q8.shape) != (B, H, N, D) \
+                or tuple(out.v8t.shape) != (B, H, D, ldv):
+            raise ValueError("joint_attn_quant_fp8_streams: `out` does not match the inputs or mode")
+    else:
+        out = _alloc_fp8(mode, B, H, N, D, ldv, nblk, dev)
+    ptr = lambda lst: (ctypes.c_void_p * n)(*[x.data_ptr() if x.numel() else None for x in lst])
+    lens = (ctypes.c_int64 * n)(*[int(x.shape[1]) for x in qs])
+    offs = (ctypes.c_int64 * (n + 1))()
+    st = load().joint_attn_quant_fp8_streams(
+        n, ptr(qs), ptr(ks), ptr(vs), lens, B, H, D, ldv, int(mode), _ptr(out.q8), _ptr(out.k8),
+        _ptr(out.v8t), _ptr(out.q_scale), _ptr(out.k_scale), _ptr(out.v_scale), _ptr(out.q_hi),
+        _ptr(out.k_hi), _ptr(out.hi_idx), _ptr(out.ch_amax), offs, _stream(qs[0]))
+    _check("joint_attn_quant_fp8_streams", st)
+    return out, list(offs)
 
 
 def _alloc_fp8(mode, B, H, N, D, ldv, nblk, dev) -> Fp8Tensors:

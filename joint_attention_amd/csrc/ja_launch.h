@@ -36,6 +36,12 @@ hipError_t launch_quant_fp8(const void* q, const void* k, const void* vt, int B,
                             float* q_scale, float* k_scale, float* v_scale, void* q_hi,
                             void* k_hi, int32_t* hi_idx, float* ch_amax, hipStream_t stream);
 
+hipError_t launch_quant_fp8_streams(const StreamTable& st, int B, int H, int N, int D,
+                                    int64_t ldv, int mode, void* q8, void* k8, void* v8t,
+                                    float* q_scale, float* k_scale, float* v_scale, void* q_hi,
+                                    void* k_hi, int32_t* hi_idx, float* ch_amax,
+                                    hipStream_t stream);
+
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
                           const float* k_scale, const float* v_scale, int B, int H, int N, int D,
                           int64_t ldv, float softmax_scale, int mode, const void* q_hi,

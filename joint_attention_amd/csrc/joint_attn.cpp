@@ -36,6 +36,46 @@ int check_shape(int B, int H, int64_t N, int D, int64_t ldv) {
     return JA_OK;
 }
 
+// The stream table of the *_streams calls: lengths, non-NULL and 16-byte aligned
+// pointers for every non-empty stream, offsets.
+int stream_table(int n_streams, const void* const* q, const void* const* k,
+                 const void* const* v, const int64_t* lens, ja::StreamTable& st) {
+    if (n_streams <= 0 || !q || !k || !v || !lens) return JA_EINVAL;
+    if (n_streams > JA_MAX_STREAMS) return JA_EUNSUPPORTED;
+    st.n = n_streams;
+    st.off[0] = 0;
+    for (int s = 0; s < n_streams; ++s) {
+        if (lens[s] < 0 || lens[s] > kMaxInt) return JA_EINVAL;
+        if (lens[s] > 0) {
+            if (!q[s] || !k[s] || !v[s]) return JA_EINVAL;
+            if (!aligned16(q[s]) || !aligned16(k[s]) || !aligned16(v[s])) return JA_EUNSUPPORTED;
+            st.q[s] = q[s];
+            st.k[s] = k[s];
+            st.v[s] = v[s];
+        }
+        st.off[s + 1] = st.off[s] + lens[s];
+    }
+    return JA_OK;
+}
+
+// Output checks of the fp8 quantiser (shared by the packed and the streams call).
+int check_quant_outputs(int mode, const void* q8, const void* k8, const void* v8t,
+                        const float* q_scale, const float* k_scale, const float* v_scale,
+                        const void* q_hi, const void* k_hi, const int32_t* hi_idx,
+                        const float* ch_amax) {
+    if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale) return JA_EINVAL;
+    if (mode == JA_FP8_SPLIT && (!q_hi || !k_hi || !hi_idx || !ch_amax)) return JA_EINVAL;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t)) return JA_EUNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+         reinterpret_cast<uintptr_t>(v_scale)) & 3u)
+        return JA_EUNSUPPORTED;
+    if (mode == JA_FP8_SPLIT &&
+        ((reinterpret_cast<uintptr_t>(q_hi) | reinterpret_cast<uintptr_t>(k_hi)) & 15u ||
+         (reinterpret_cast<uintptr_t>(hi_idx) | reinterpret_cast<uintptr_t>(ch_amax)) & 3u))
+        return JA_EUNSUPPORTED;
+    return JA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,22 +139,9 @@ int joint_attn_fwd_bf16_streams(int n_streams, const void* const* q, const void*
                                 const void* const* v, const int64_t* lens, int B, int H, int D,
                                 float softmax_scale, void* o, float* lse, int64_t* offsets,
                                 void* stream) {
-    if (n_streams <= 0 || !q || !k || !v || !lens) return JA_EINVAL;
-    if (n_streams > JA_MAX_STREAMS) return JA_EUNSUPPORTED;
     ja::StreamTable st{};
-    st.n = n_streams;
-    st.off[0] = 0;
-    for (int s = 0; s < n_streams; ++s) {
-        if (lens[s] < 0 || lens[s] > kMaxInt) return JA_EINVAL;
-        if (lens[s] > 0) {
-            if (!q[s] || !k[s] || !v[s]) return JA_EINVAL;
-            if (!aligned16(q[s]) || !aligned16(k[s]) || !aligned16(v[s])) return JA_EUNSUPPORTED;
-            st.q[s] = q[s];
-            st.k[s] = k[s];
-            st.v[s] = v[s];
-        }
-        st.off[s + 1] = st.off[s] + lens[s];
-    }
+    const int tst = stream_table(n_streams, q, k, v, lens, st);
+    if (tst != JA_OK) return tst;
     const int64_t N = st.off[n_streams];
     const int sh = check_shape(B, H, N, D, joint_attn_vt_ld(N));
     if (sh != JA_OK) return sh;
@@ -137,22 +164,38 @@ int joint_attn_quant_fp8(const void* q, const void* k, const void* vt, int B, in
     if (st != JA_OK) return st;
     if (mode != JA_FP8_PLAIN && mode != JA_FP8_SPLIT) return JA_EUNSUPPORTED;
     if (N == 0) return JA_OK;
-    if (!q || !k || !vt || !q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale)
-        return JA_EINVAL;
-    if (mode == JA_FP8_SPLIT && (!q_hi || !k_hi || !hi_idx || !ch_amax)) return JA_EINVAL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(q8) || !aligned16(k8) ||
-        !aligned16(v8t))
-        return JA_EUNSUPPORTED;
-    if ((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
-         reinterpret_cast<uintptr_t>(v_scale)) & 3u)
-        return JA_EUNSUPPORTED;
-    if (mode == JA_FP8_SPLIT &&
-        ((reinterpret_cast<uintptr_t>(q_hi) | reinterpret_cast<uintptr_t>(k_hi)) & 15u ||
-         (reinterpret_cast<uintptr_t>(hi_idx) | reinterpret_cast<uintptr_t>(ch_amax)) & 3u))
-        return JA_EUNSUPPORTED;
+    if (!q || !k || !vt) return JA_EINVAL;
+    const int ost = check_quant_outputs(mode, q8, k8, v8t, q_scale, k_scale, v_scale, q_hi, k_hi,
+                                        hi_idx, ch_amax);
+    if (ost != JA_OK) return ost;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt)) return JA_EUNSUPPORTED;
     return hip_status(ja::launch_quant_fp8(q, k, vt, B, H, (int)N, D, ldv, mode, q8, k8, v8t,
                                            q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
                                            ch_amax, static_cast<hipStream_t>(stream)));
+}
+
+int joint_attn_quant_fp8_streams(int n_streams, const void* const* q, const void* const* k,
+                                 const void* const* v, const int64_t* lens, int B, int H, int D,
+                                 int64_t ldv, int mode, void* q8, void* k8, void* v8t,
+                                 float* q_scale, float* k_scale, float* v_scale, void* q_hi,
+                                 void* k_hi, int32_t* hi_idx, float* ch_amax, int64_t* offsets,
+                                 void* stream) {
+    ja::StreamTable st{};
+    const int tst = stream_table(n_streams, q, k, v, lens, st);
+    if (tst != JA_OK) return tst;
+    const int64_t N = st.off[n_streams];
+    const int sh = check_shape(B, H, N, D, ldv);
+    if (sh != JA_OK) return sh;
+    if (mode != JA_FP8_PLAIN && mode != JA_FP8_SPLIT) return JA_EUNSUPPORTED;
+    if (offsets)
+        for (int s = 0; s <= n_streams; ++s) offsets[s] = st.off[s];
+    if (N == 0) return JA_OK;
+    const int ost = check_quant_outputs(mode, q8, k8, v8t, q_scale, k_scale, v_scale, q_hi, k_hi,
+                                        hi_idx, ch_amax);
+    if (ost != JA_OK) return ost;
+    return hip_status(ja::launch_quant_fp8_streams(st, B, H, (int)N, D, ldv, mode, q8, k8, v8t,
+                                                   q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
+                                                   ch_amax, static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,

@@ -101,6 +101,46 @@ __device__ inline float amax8(uint4 v) {
     return m;
 }
 
+// ---- where the rows of packed tokens come from: the packed tensor [B][H][N][D], or
+//      (GATHER) the per-stream tensors [B][L_s][H][D] of a StreamTable
+__device__ inline int stream_index(const StreamTable& st, int t) {
+    int s = 0;
+    for (int i = 1; i < st.n; ++i)
+        if (t >= st.off[i]) s = i;                   // zero-length streams share the next start
+    return s;
+}
+
+__device__ inline const uint16_t* stream_token_row(const StreamTable& st, const void* const* src,
+                                                   int b, int h, int H, int D, int t) {
+    const int s = stream_index(st, t);
+    const int64_t L = st.off[s + 1] - st.off[s];
+    return static_cast<const uint16_t*>(src[s]) +
+           (((int64_t)b * L + (t - st.off[s])) * H + h) * (int64_t)D;
+}
+
+// rows of tokens t0 .. t0 + rows - 1 of one (b, h): one strided run (packed, or inside a
+// single stream), else looked up row by row
+struct RowMap {
+    const uint16_t* run;     // row of t0, or nullptr
+    int64_t pitch;           // elements between consecutive rows of the run
+};
+
+template <bool GATHER>
+__device__ inline RowMap row_map(const uint16_t* packed_bh, const StreamTable& st,
+                                 const void* const* src, int b, int h, int H, int D, int t0,
+                                 int rows) {
+    if (!GATHER) return {packed_bh + (int64_t)t0 * D, D};
+    const int s = stream_index(st, t0);
+    if (t0 + rows <= st.off[s + 1]) return {stream_token_row(st, src, b, h, H, D, t0), (int64_t)H * D};
+    return {nullptr, 0};
+}
+
+__device__ inline const uint16_t* row_ptr(const RowMap& m, const StreamTable& st,
+                                          const void* const* src, int b, int h, int H, int D,
+                                          int t0, int r) {
+    return m.run ? m.run + r * m.pitch : stream_token_row(st, src, b, h, H, D, t0 + r);
+}
+
 // corrected mode, step 0 -- clear ch_amax (a plain fill kernel, also safe under graph
 // capture)
 __global__ __launch_bounds__(NT) void clear_kernel(float* __restrict__ x, int n) {
@@ -112,22 +152,26 @@ __global__ __launch_bounds__(NT) void clear_kernel(float* __restrict__ x, int n)
 // block of Q (z = 0) or K (z = 1), folded into ch_amax [B, H, 2, D] with an atomic max on
 // the bit patterns (non-negative floats order like their bits; max is order-free, so the
 // result is deterministic).
-template <int D>
+template <int D, bool GATHER>
 __global__ __launch_bounds__(NT) void chan_amax_kernel(const uint16_t* __restrict__ q,
-                                                      const uint16_t* __restrict__ k, int N,
+                                                      const uint16_t* __restrict__ k,
+                                                      const StreamTable st, int H, int N,
                                                       float* __restrict__ ch_amax) {
     constexpr int CPR = D / 8;                        // 16-byte chunks per token row
     constexpr int RPP = NT / CPR;                     // rows handled in parallel
     __shared__ float part[RPP][D + 1];
     const int blk = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / H, h = bh - b * H;
     const int t0 = blk * JA_QK_BLOCK;
     const int rows = min(JA_QK_BLOCK, N - t0);
     const int ch = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
-    const uint4* src =
-        reinterpret_cast<const uint4*>((blockIdx.z ? k : q) + ((int64_t)bh * N + t0) * D);
+    const void* const* xs = blockIdx.z ? st.k : st.q;
+    const RowMap rm = row_map<GATHER>((blockIdx.z ? k : q) + (int64_t)bh * N * D, st, xs, b, h,
+                                      H, D, t0, rows);
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int row = r0; row < rows; row += RPP) {
-        const uint4 v = src[row * CPR + ch];
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(row_ptr(rm, st, xs, b, h, H, D, t0, row) + ch * 8);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -210,9 +254,10 @@ __global__ __launch_bounds__(64) void select_hi_kernel(const float* __restrict__
 
 // grid: (n_blocks, B*H, 2) -- z selects Q (0) or K (1).  With hi_idx, the selected
 // channels' codes are zero and their values / scale go to hi (bf16 [B, H, N, 16]).
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool GATHER>
 __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k, int N,
+                                                     const uint16_t* __restrict__ k,
+                                                     const StreamTable st, int H, int N,
                                                      uint8_t* __restrict__ q8,
                                                      uint8_t* __restrict__ k8,
                                                      float* __restrict__ qs,
@@ -229,9 +274,15 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
     const int blk = blockIdx.x, bh = blockIdx.y;
     const int t0 = blk * JA_QK_BLOCK;
     const int rows = min(JA_QK_BLOCK, N - t0);
-    const int64_t base = ((int64_t)bh * N + t0) * D;
+    const int64_t base = ((int64_t)bh * N + t0) * D;    // of the packed output block
     const int nch = rows * D / 8;                       // 16-byte input chunks in the segment
-    const uint4* src = reinterpret_cast<const uint4*>(x + base);
+    const int b = bh / H, h = bh - b * H;
+    const void* const* xs = blockIdx.z ? st.k : st.q;
+    const RowMap rm = row_map<GATHER>(x + (int64_t)bh * N * D, st, xs, b, h, H, D, t0, rows);
+    auto chunk = [&](int c) {                           // input chunk c of the block
+        return *reinterpret_cast<const uint4*>(
+            row_ptr(rm, st, xs, b, h, H, D, t0, c / (D / 8)) + (c % (D / 8)) * 8);
+    };
     if (SPLIT) {
         if (threadIdx.x < D / 32) mask[threadIdx.x] = 0;
         __syncthreads();
@@ -248,7 +299,7 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int c = threadIdx.x + i * NT;
-        reg[i] = c < nch ? src[c] : make_uint4(0, 0, 0, 0);
+        reg[i] = c < nch ? chunk(c) : make_uint4(0, 0, 0, 0);
         m = fmaxf(m, amax8(reg[i]));
     }
     const float amax = block_max(m, red);               // (its barrier also publishes mask)
@@ -273,7 +324,8 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
         const int32_t* sel = hi_idx + (int64_t)bh * JA_HI_CHANNELS;
         for (int i = threadIdx.x; i < rows * JA_HI_CHANNELS; i += NT) {
             const int r = i / JA_HI_CHANNELS, j = i % JA_HI_CHANNELS;
-            const float v = __uint_as_float((uint32_t)x[base + (int64_t)r * D + sel[j]] << 16);
+            const float v =
+                __uint_as_float((uint32_t)row_ptr(rm, st, xs, b, h, H, D, t0, r)[sel[j]] << 16);
             hi[i] = (uint16_t)(__float_as_uint(v * inv) >> 16);   // exact power-of-two rescale
         }
     }
@@ -336,11 +388,97 @@ __global__ __launch_bounds__(NT) void quant_v_kernel(const uint16_t* __restrict_
         dst[i] = i < nval ? quant8(v_chunk_masked(src, i, nfull, rem), inv) : make_uint2(0, 0);
 }
 
+// GATHER V, pass 1 -- grid (ceil(N / 256), B*H): per-channel amax of 256 tokens, folded
+// into vmax [B][H][D] (the v_scale buffer, cleared first) with an atomic max on the bits.
 template <int D>
-hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, int N,
-                    int64_t ldv, int mode, void* q8, void* k8, void* v8t, float* q_scale,
-                    float* k_scale, float* v_scale, void* q_hi, void* k_hi, int32_t* hi_idx,
-                    float* ch_amax, hipStream_t stream) {
+__global__ __launch_bounds__(NT) void v_amax_kernel(const StreamTable st, int H, int N,
+                                                   float* __restrict__ vmax) {
+    constexpr int CPR = D / 8, RPP = NT / CPR, TT = 256;
+    __shared__ float part[RPP][D + 1];
+    const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+    const int t0 = blockIdx.x * TT, rows = min(TT, N - t0);
+    const int ch = threadIdx.x % CPR, r0 = threadIdx.x / CPR;
+    const RowMap rm = row_map<true>(nullptr, st, st.v, b, h, H, D, t0, rows);
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = r0; r < rows; r += RPP) {
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(row_ptr(rm, st, st.v, b, h, H, D, t0, r) + ch * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float lo, hi;
+            bf16x2_to_f32(w[e], lo, hi);
+            m[2 * e] = fmaxf(m[2 * e], fabsf(lo));
+            m[2 * e + 1] = fmaxf(m[2 * e + 1], fabsf(hi));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[r0][ch * 8 + e] = m[e];
+    __syncthreads();
+    if (threadIdx.x < D) {
+        float mx = 0.f;
+        for (int r = 0; r < RPP; ++r) mx = fmaxf(mx, part[r][threadIdx.x]);
+        atomicMax(reinterpret_cast<unsigned int*>(vmax) + (int64_t)bh * D + threadIdx.x,
+                  __float_as_uint(mx));
+    }
+}
+
+// GATHER V, pass 2 -- grid (ceil(ldv / 64), B*H): a 64-token tile quantised with the
+// per-channel scales of pass 1 and transposed through LDS into 64-byte runs of the V^T
+// code rows; tokens at or past N (the padding up to ldv) are written as code 0.
+template <int D>
+__global__ __launch_bounds__(NT) void quant_vt_kernel(const StreamTable st, int H, int N,
+                                                     int64_t ldv, const float* __restrict__ vmax,
+                                                     uint8_t* __restrict__ v8t) {
+    constexpr int T = 64, CPR = D / 8, PITCH = T + 4;   // codes, channel-major
+    __shared__ __attribute__((aligned(16))) uint8_t tile[D * PITCH];
+    __shared__ float inv_s[D];
+    const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+    const int t0 = blockIdx.x * T;
+    const int rows = max(0, min(T, N - t0));
+    for (int c = threadIdx.x; c < D; c += NT)
+        inv_s[c] = ldexpf(1.f, -pow2_exponent(vmax[(int64_t)bh * D + c]));
+    __syncthreads();
+    const RowMap rm = row_map<true>(nullptr, st, st.v, b, h, H, D, t0, max(rows, 1));
+    for (int x = threadIdx.x; x < T * CPR; x += NT) {
+        const int r = x / CPR, col = x % CPR;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < rows)
+            v = *reinterpret_cast<const uint4*>(row_ptr(rm, st, st.v, b, h, H, D, t0, r) +
+                                                col * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float lo, hi;
+            bf16x2_to_f32(w[e], lo, hi);
+            const int c = col * 8 + 2 * e;
+            tile[c * PITCH + r] = (uint8_t)e4m3_from_f32(lo * inv_s[c]);
+            tile[(c + 1) * PITCH + r] = (uint8_t)e4m3_from_f32(hi * inv_s[c + 1]);
+        }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < D * (T / 16); x += NT) {
+        const int c = x / (T / 16), seg = x % (T / 16);
+        const int64_t col0 = t0 + seg * 16;
+        if (col0 < ldv) {                                // ldv % 16 == 0: whole 16-byte runs
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(&tile[c * PITCH + seg * 16]);
+            *reinterpret_cast<uint4*>(v8t + ((int64_t)bh * D + c) * ldv + col0) =
+                make_uint4(src[0], src[1], src[2], src[3]);
+        }
+    }
+}
+
+// GATHER V, pass 3: amax -> power-of-two scale, in place
+__global__ __launch_bounds__(NT) void v_scale_final_kernel(float* __restrict__ vs, int n) {
+    const int i = blockIdx.x * NT + threadIdx.x;
+    if (i < n) vs[i] = ldexpf(1.f, pow2_exponent(vs[i]));
+}
+
+template <int D, bool GATHER>
+hipError_t launch_d(const void* q, const void* k, const void* vt, const StreamTable& st, int B,
+                    int H, int N, int64_t ldv, int mode, void* q8, void* k8, void* v8t,
+                    float* q_scale, float* k_scale, float* v_scale, void* q_hi, void* k_hi,
+                    int32_t* hi_idx, float* ch_amax, hipStream_t stream) {
     const int nblk = (N + JA_QK_BLOCK - 1) / JA_QK_BLOCK;
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     const uint16_t* kk = static_cast<const uint16_t*>(k);
@@ -348,27 +486,39 @@ hipError_t launch_d(const void* q, const void* k, const void* vt, int B, int H, 
         const int n_amax = B * H * 2 * D;
         hipLaunchKernelGGL(clear_kernel, dim3((n_amax + NT - 1) / NT), dim3(NT), 0, stream,
                            ch_amax, n_amax);
-        hipLaunchKernelGGL(chan_amax_kernel<D>, dim3(nblk, B * H, 2), dim3(NT), 0, stream, qq,
-                           kk, N, ch_amax);
+        hipLaunchKernelGGL((chan_amax_kernel<D, GATHER>), dim3(nblk, B * H, 2), dim3(NT), 0,
+                           stream, qq, kk, st, H, N, ch_amax);
         hipLaunchKernelGGL(select_hi_kernel<D>, dim3(B * H), dim3(64), 0, stream, ch_amax,
                            hi_idx);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((quant_qk_kernel<D, true>), dim3(nblk, B * H, 2), dim3(NT), 0, stream,
-                           qq, kk, N, static_cast<uint8_t*>(q8), static_cast<uint8_t*>(k8),
-                           q_scale, k_scale, nblk, hi_idx, static_cast<uint16_t*>(q_hi),
-                           static_cast<uint16_t*>(k_hi));
+        hipLaunchKernelGGL((quant_qk_kernel<D, true, GATHER>), dim3(nblk, B * H, 2), dim3(NT), 0,
+                           stream, qq, kk, st, H, N, static_cast<uint8_t*>(q8),
+                           static_cast<uint8_t*>(k8), q_scale, k_scale, nblk, hi_idx,
+                           static_cast<uint16_t*>(q_hi), static_cast<uint16_t*>(k_hi));
     } else {
-        hipLaunchKernelGGL((quant_qk_kernel<D, false>), dim3(nblk, B * H, 2), dim3(NT), 0,
-                           stream, qq, kk, N, static_cast<uint8_t*>(q8),
+        hipLaunchKernelGGL((quant_qk_kernel<D, false, GATHER>), dim3(nblk, B * H, 2), dim3(NT),
+                           0, stream, qq, kk, st, H, N, static_cast<uint8_t*>(q8),
                            static_cast<uint8_t*>(k8), q_scale, k_scale, nblk, nullptr, nullptr,
                            nullptr);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(quant_v_kernel, dim3(D, B * H), dim3(NT), 0, stream,
-                       static_cast<const uint16_t*>(vt), N, D, ldv, static_cast<uint8_t*>(v8t),
-                       v_scale);
+    if (GATHER) {
+        const int n_vs = B * H * D;
+        hipLaunchKernelGGL(clear_kernel, dim3((n_vs + NT - 1) / NT), dim3(NT), 0, stream,
+                           v_scale, n_vs);
+        hipLaunchKernelGGL(v_amax_kernel<D>, dim3((N + 255) / 256, B * H), dim3(NT), 0, stream,
+                           st, H, N, v_scale);
+        hipLaunchKernelGGL(quant_vt_kernel<D>, dim3((int)((ldv + 63) / 64), B * H), dim3(NT), 0,
+                           stream, st, H, N, ldv, v_scale, static_cast<uint8_t*>(v8t));
+        hipLaunchKernelGGL(v_scale_final_kernel, dim3((n_vs + NT - 1) / NT), dim3(NT), 0,
+                           stream, v_scale, n_vs);
+    } else {
+        hipLaunchKernelGGL(quant_v_kernel, dim3(D, B * H), dim3(NT), 0, stream,
+                           static_cast<const uint16_t*>(vt), N, D, ldv,
+                           static_cast<uint8_t*>(v8t), v_scale);
+    }
     return hipGetLastError();
 }
 
@@ -378,10 +528,26 @@ hipError_t launch_quant_fp8(const void* q, const void* k, const void* vt, int B,
                             int D, int64_t ldv, int mode, void* q8, void* k8, void* v8t,
                             float* q_scale, float* k_scale, float* v_scale, void* q_hi,
                             void* k_hi, int32_t* hi_idx, float* ch_amax, hipStream_t stream) {
-    return D == 64 ? launch_d<64>(q, k, vt, B, H, N, ldv, mode, q8, k8, v8t, q_scale, k_scale,
-                                  v_scale, q_hi, k_hi, hi_idx, ch_amax, stream)
-                   : launch_d<128>(q, k, vt, B, H, N, ldv, mode, q8, k8, v8t, q_scale, k_scale,
-                                   v_scale, q_hi, k_hi, hi_idx, ch_amax, stream);
+    const StreamTable none{};
+    return D == 64 ? launch_d<64, false>(q, k, vt, none, B, H, N, ldv, mode, q8, k8, v8t,
+                                         q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx, ch_amax,
+                                         stream)
+                   : launch_d<128, false>(q, k, vt, none, B, H, N, ldv, mode, q8, k8, v8t,
+                                          q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx, ch_amax,
+                                          stream);
+}
+
+hipError_t launch_quant_fp8_streams(const StreamTable& st, int B, int H, int N, int D,
+                                    int64_t ldv, int mode, void* q8, void* k8, void* v8t,
+                                    float* q_scale, float* k_scale, float* v_scale, void* q_hi,
+                                    void* k_hi, int32_t* hi_idx, float* ch_amax,
+                                    hipStream_t stream) {
+    return D == 64 ? launch_d<64, true>(nullptr, nullptr, nullptr, st, B, H, N, ldv, mode, q8, k8,
+                                        v8t, q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
+                                        ch_amax, stream)
+                   : launch_d<128, true>(nullptr, nullptr, nullptr, st, B, H, N, ldv, mode, q8,
+                                         k8, v8t, q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
+                                         ch_amax, stream);
 }
 
 }  // namespace ja

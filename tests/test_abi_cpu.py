@@ -130,3 +130,25 @@ def test_fwd_streams_validation(lib):
     # empty streams are a successful no-op that still reports the offsets
     st, offs = call(3, [None] * 3, [None] * 3, [None] * 3, [0, 0, 0], o=None)
     assert st == 0 and offs == [0, 0, 0, 0]
+
+
+def test_quant_streams_validation(lib):
+    fake = 0x10000
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+
+    def call(n, ptrs, lens, mode=0, ldv=16, D=128, q8=fake, hi=None):
+        arr = (P * max(n, 1))(*ptrs)
+        ln = (I64 * max(n, 1))(*lens)
+        offs = (I64 * (max(n, 1) + 1))()
+        st = lib.joint_attn_quant_fp8_streams(n, arr, arr, arr, ln, 1, 2, D, ldv, mode, q8, fake,
+                                              fake, fake, fake, fake, hi, hi, hi, hi, offs, None)
+        return st, list(offs)
+
+    assert call(2, [fake, fake], [4, 4], ldv=8)[0] == 1       # ldv < N
+    assert call(2, [fake, fake], [4, 4], mode=3)[0] == 2
+    assert call(2, [fake, fake], [4, 4], mode=1)[0] == 1      # split without its buffers
+    assert call(2, [fake, fake], [4, 4], q8=None)[0] == 1
+    assert call(2, [fake, fake], [4, 4], q8=fake + 4)[0] == 2
+    assert call(2, [fake, fake], [4, 4], D=80)[0] == 2
+    st, offs = call(2, [None, None], [0, 0], ldv=0)
+    assert st == 0 and offs == [0, 0, 0]

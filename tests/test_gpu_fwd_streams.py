@@ -64,3 +64,57 @@ def test_streams_small_every_row(D, lens):
 def test_streams_full_size(name):
     w = synth.WORKLOADS[name]
     _check(w, sel=synth.row_sample(w, 256, seed=21, n_pairs=4), tag=name)
+
+
+def _quant_both(w, mode):
+    import joint_attention_amd as ja
+    import torch
+    st = host_streams(w)
+    qd = [to_device(x) for x in st.q]
+    kd = [to_device(x) for x in st.k]
+    vd = [to_device(x) for x in st.v]
+    t_s, offs_s = ja.joint_attn_quant_fp8_streams(qd, kd, vd, mode)
+    q, k, vt, offs = device_packed(st)
+    t_p = ja.joint_attn_quant_fp8(q, k, vt, mode)
+    torch.cuda.synchronize()
+    return t_s, offs_s, t_p, offs
+
+
+def _assert_same_fp8(t_s, t_p, mode, tag):
+    import torch
+    names = ["q8", "k8", "v8t", "q_scale", "k_scale", "v_scale"]
+    if mode == 1:
+        names += ["q_hi", "k_hi", "hi_idx", "ch_amax"]
+    for n in names:
+        a, b = getattr(t_s, n), getattr(t_p, n)
+        assert a.shape == b.shape, (tag, n)
+        va = a.view(torch.uint8) if a.dtype == torch.uint8 else a.contiguous().view(torch.int8)
+        vb = b.view(torch.uint8) if b.dtype == torch.uint8 else b.contiguous().view(torch.int8)
+        assert torch.equal(va, vb), (tag, n)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("lens", [(1,), (31,), (100, 29), (127, 2, 0, 1), (0, 45, 0, 300),
+                                  (129, 64, 66), (300, 17, 0)])
+def test_quant_streams_equals_packed(lens, D, mode):
+    w = synth.custom("qs", B=2, H=3, D=D, stream_lens=lens, n_reference=max(0, len(lens) - 2),
+                     outliers=4 if D == 128 else 0, seed=11 + sum(lens))
+    print("quant streams", lens, D, mode, flush=True)
+    t_s, offs_s, t_p, offs = _quant_both(w, mode)
+    assert offs_s == offs
+    _assert_same_fp8(t_s, t_p, mode, (lens, D, mode))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_quant_streams_t2i_2048_equals_packed_and_forward(mode):
+    import joint_attention_amd as ja
+    import torch
+    w = synth.WORKLOADS["t2i_2048_fp8"]
+    t_s, offs_s, t_p, offs = _quant_both(w, mode)
+    assert offs_s == offs
+    _assert_same_fp8(t_s, t_p, mode, ("t2i_2048", mode))
+    o_s = ja.joint_attn_fwd_fp8(t_s)
+    o_p = ja.joint_attn_fwd_fp8(t_p)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s.view(torch.int16), o_p.view(torch.int16))
