@@ -6,6 +6,7 @@ FLUX 3 article (everytik.com translation) and the mathematics of softmax attenti
   pack       -- token concatenation of text / target / reference streams + offsets
   attention  -- fp64 two-pass softmax attention (C, OpenMP over rows)
   fp8        -- OCP e4m3 codec, the block/channel quantiser, fp8 attention
+  sparse     -- block-sparse attention with an input block mask
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this
 package.  The product path (joint_attention_amd) never imports it, and this package
@@ -16,6 +17,7 @@ from .attention import attention, attention_rows, all_rows, widen_bf16
 from .fp8 import (E4M3_MAX, QK_BLOCK, P_SCALE_LOG2, HI_CHANNELS, e4m3_encode, e4m3_decode,
                   pow2_scale, quantise_qk, quantise_v, select_hi_channels, quantise_qk_split,
                   fp8_attention_rows, e4m3_midpoint_distance)
+from .sparse import SPARSE_BQ, SPARSE_BK, mask_shape, sparse_attention_rows
 from ._native import build, default_threads
 
 __all__ = [
@@ -23,5 +25,6 @@ __all__ = [
     "attention", "attention_rows", "all_rows", "widen_bf16",
     "E4M3_MAX", "QK_BLOCK", "P_SCALE_LOG2", "HI_CHANNELS", "e4m3_encode", "e4m3_decode",
     "pow2_scale", "quantise_qk", "quantise_v", "select_hi_channels", "quantise_qk_split",
-    "fp8_attention_rows", "e4m3_midpoint_distance", "build", "default_threads",
+    "fp8_attention_rows", "e4m3_midpoint_distance",
+    "SPARSE_BQ", "SPARSE_BK", "mask_shape", "sparse_attention_rows", "build", "default_threads",
 ]
