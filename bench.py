@@ -9,7 +9,8 @@ before timing starts.
 
 One timed step of the bf16 path = pack(Q), pack(K), pack(V^T) -> joint_attn_fwd_bf16.
 The same attention through joint_attn_fwd_bf16_streams (streams read in place, no pack)
-is timed in its own loop and reported under "fused_bf16".
+is timed in its own loop and reported under "fused_bf16"; the block-sparse forward with a
+structured block mask under "sparse_bf16".
 The fp8 path (pack x3 -> joint_attn_quant_fp8 -> joint_attn_fwd_fp8) on the same
 inputs is timed the same way in its own loop and reported under "fp8".
 value = algorithmic attention flops (4 B H N^2 D) per bf16 step / step time.
@@ -226,6 +227,31 @@ def main():
         "kernel_tflops": round(flops / (float(durs_f.mean()) * 1e-3) / 1e12, 2),
         "frac_of_bf16_peak": round(flops / (float(durs_f.mean()) * 1e-3) / 1e12
                                    / PEAK_BF16_TFLOPS, 4),
+    }
+
+    # block-sparse forward with a structured 128x128 block mask (text rows and columns,
+    # a band of 2 blocks around the diagonal, 15 % of the other image blocks)
+    mask = synth.block_mask(w, "structured", 0.15, band=2, seed=4)
+    frac = float(mask.mean())
+    m_dev = torch.from_numpy(mask).cuda()
+
+    def step_sparse(rec):
+        e0, e1 = (ev(), ev()) if rec else (None, None)
+        if rec:
+            e0.record(stream)
+        ja.joint_attn_fwd_bf16_sparse(q, k, vt, m_dev, scale, out=o)
+        if rec:
+            e1.record(stream)
+        return (e0, e1)
+
+    log("timing block-sparse bf16 forward (%.1f %% of blocks)" % (100 * frac))
+    _, durs_s = timed(step_sparse, args.steps, args.warmup)
+    sp_ms = float(durs_s.mean())
+    out["sparse_bf16"] = {
+        "mask": "structured: text rows/columns, band 2, 15 % random", "block": 128,
+        "attended_fraction": round(frac, 4), "kernel_ms": round(sp_ms, 4),
+        "effective_tflops": round(flops * frac / (sp_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": round(float(fwd_ms) / sp_ms, 3),
     }
 
     if not args.skip_fp8:

@@ -56,6 +56,9 @@ extern "C" {
 #define JA_QK_BLOCK 128     /* tokens per fp8 scale block of Q and K */
 #define JA_HI_CHANNELS 16   /* Q/K channels per (b, h) kept out of e4m3 in fp8 mode 1 */
 
+#define JA_SPARSE_BLOCK 128       /* query rows and keys per block of the sparse mask */
+#define JA_SPARSE_MAX_N 131072    /* longest sequence of joint_attn_fwd_bf16_sparse */
+
 #define JA_FP8_PLAIN 0      /* fp8 mode 0: every Q/K channel in e4m3 */
 #define JA_FP8_SPLIT 1      /* fp8 mode 1: JA_HI_CHANNELS outlier channels in bf16 */
 
@@ -106,6 +109,24 @@ int joint_attn_pack(int n_streams, const void *const *src, const int64_t *lens,
 int joint_attn_fwd_bf16(const void *q, const void *k, const void *vt,
                         int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
                         void *o, float *lse, void *stream);
+
+/*
+ * joint_attn_fwd_bf16_sparse -- block-sparse variant of joint_attn_fwd_bf16: the sparse
+ * attention option of the VisualGen FLUX 3 article (section 量化注意力与稀疏注意力), which
+ * runs on a general block-sparse attention kernel; the rule that picks the blocks is not
+ * part of this library, the mask is an input.  Query row i of (b, h) attends key j only if
+ *     block_mask[b][h][i / JA_SPARSE_BLOCK][j / JA_SPARSE_BLOCK] != 0;
+ * a row that attends no key gets O = 0 and lse = -inf.  Key blocks that no query row of a
+ * workgroup attends are skipped (the work saved scales with the zero blocks).
+ *
+ *   q, k, vt, o, lse  as for joint_attn_fwd_bf16
+ *   block_mask        device uint8 [B][H][nb][nb], nb = ceil(N / JA_SPARSE_BLOCK)
+ *   N                 at most JA_SPARSE_MAX_N
+ */
+int joint_attn_fwd_bf16_sparse(const void *q, const void *k, const void *vt,
+                               int B, int H, int64_t N, int D, int64_t ldv,
+                               const uint8_t *block_mask, float softmax_scale,
+                               void *o, float *lse, void *stream);
 
 /*
  * joint_attn_fwd_bf16_streams -- the same attention as joint_attn_fwd_bf16, reading Q, K

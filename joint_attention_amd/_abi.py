@@ -21,10 +21,12 @@ JA_LAYOUT_BHND, JA_LAYOUT_BHDN = 0, 1
 JA_MAX_STREAMS = 16
 JA_QK_BLOCK = 128
 JA_HI_CHANNELS = 16
+JA_SPARSE_BLOCK, JA_SPARSE_MAX_N = 128, 131072
 JA_FP8_PLAIN, JA_FP8_SPLIT = 0, 1
 
 EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
-           "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_streams",
+           "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse",
+           "joint_attn_fwd_bf16_streams",
            "joint_attn_quant_fp8", "joint_attn_quant_fp8_streams",
            "joint_attn_fwd_fp8")
 
@@ -62,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_pack.argtypes = [I, P, P, I, I, I, I, I64, P, P, P]
         h.joint_attn_fwd_bf16.restype = I
         h.joint_attn_fwd_bf16.argtypes = [P, P, P, I, I, I64, I, I64, F, P, P, P]
+        h.joint_attn_fwd_bf16_sparse.restype = I
+        h.joint_attn_fwd_bf16_sparse.argtypes = [P, P, P, I, I, I64, I, I64, P, F, P, P, P]
         h.joint_attn_fwd_bf16_streams.restype = I
         h.joint_attn_fwd_bf16_streams.argtypes = [I, P, P, P, P, I, I, I, F,
                                                   P, P, P, P]
@@ -167,6 +171,33 @@ def joint_attn_fwd_bf16(q, k, vt, softmax_scale: float | None = None, out=None,
                                     scale, out.data_ptr(),
                                     lse.data_ptr() if lse is not None else None, _stream(q))
     _check("joint_attn_fwd_bf16", st)
+    return (out, lse) if return_lse else out
+
+
+def joint_attn_fwd_bf16_sparse(q, k, vt, block_mask, softmax_scale: float | None = None,
+                               out=None, return_lse: bool = False):
+    """Block-sparse attention: q, k bf16 [B, H, N, D]; vt bf16 [B, H, D, ldv]; block_mask
+    uint8 [B, H, nb, nb] with nb = ceil(N / JA_SPARSE_BLOCK), nonzero = attended.  Returns
+    O [B, N, H, D] (and lse [B, H, N])."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, N, D = q.shape
+    nb = -(-N // JA_SPARSE_BLOCK)
+    _need(block_mask, torch.uint8, "block_mask", 4)
+    if tuple(block_mask.shape) != (B, H, nb, nb):
+        raise ValueError("block_mask must be [B, H, %d, %d]" % (nb, nb))
+    if tuple(k.shape) != (B, H, N, D) or vt.shape[:3] != (B, H, D):
+        raise ValueError("k must match q; vt must be [B, H, D, ldv]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out", 4)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    st = load().joint_attn_fwd_bf16_sparse(q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D,
+                                           int(vt.shape[3]), block_mask.data_ptr(), scale,
+                                           out.data_ptr(), _ptr(lse), _stream(q))
+    _check("joint_attn_fwd_bf16_sparse", st)
     return (out, lse) if return_lse else out
 
 

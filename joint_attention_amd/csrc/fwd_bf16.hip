@@ -71,11 +71,15 @@ __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | (
 // GATHER: Q, K and V are read in place from the per-stream tensors of `st` (token-major
 // [B][L_s][H][D]) instead of the packed Q, K (BHND) and V^T (BHDN); V tiles are then kept
 // token-major in LDS and read with transposing LDS loads.
-template <int D, int NW, int QB, int BC, bool GATHER>
+// SPARSE: only the key blocks that a block mask (uint8 [B][H][nqb][nkb], 128 x 128 blocks)
+// allows for at least one of the workgroup's query blocks are visited; a wave whose own
+// query block does not see a visited block gives it zero weight.
+template <int D, int NW, int QB, int BC, bool GATHER, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ VT,
-    const StreamTable st, int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O,
-    float* __restrict__ LSE, int n_qtiles, int total) {
+    const StreamTable st, const uint8_t* __restrict__ MASK, int H, int N, int64_t ldv, float c2,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int n_qtiles, int total) {
+    static_assert(!(GATHER && SPARSE), "one variant at a time");
     constexpr int NTHREADS = NW * 64;
     constexpr int BR = NW * QB * 32;             // query rows per workgroup
     constexpr int KB = BC / 32;                  // 32-key blocks per tile
@@ -107,7 +111,76 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const __bf16* Qbh = Q + (int64_t)bh * N * D;
     const __bf16* Kbh = K + (int64_t)bh * N * D;
     const __bf16* Vbh = VT + (int64_t)bh * D * ldv;
-    const int nkt = (N + BC - 1) / BC;
+    int nkt = (N + BC - 1) / BC;
+
+    // ---- SPARSE: table of the active 128-key blocks (block index | flags << 16, one flag
+    //      per query block of the workgroup), compacted by wave 0 with ballots
+    constexpr int TPB = JA_SPARSE_BLOCK / BC;    // key tiles per mask block
+    __shared__ int ktab[SPARSE ? JA_SPARSE_MAX_N / JA_SPARSE_BLOCK : 1];
+    __shared__ int ktab_n;
+    int sp_group = 0;                            // this wave's query block in the workgroup
+    if constexpr (SPARSE) {
+        constexpr int QBW = BR / JA_SPARSE_BLOCK;
+        static_assert(QBW >= 1 && QBW * JA_SPARSE_BLOCK == BR, "workgroup rows per mask block");
+        const int nb = (N + JA_SPARSE_BLOCK - 1) / JA_SPARSE_BLOCK;
+        const int qb0 = qt * QBW;
+        sp_group = (w * QB * 32) / JA_SPARSE_BLOCK;
+        if (w == 0) {
+            int count = 0;
+            for (int base = 0; base < nb; base += 64) {
+                const int kb = base + lane;
+                int flags = 0;
+                if (kb < nb) {
+#pragma unroll
+                    for (int g = 0; g < QBW; ++g)
+                        if (qb0 + g < nb && MASK[((int64_t)bh * nb + qb0 + g) * nb + kb] != 0)
+                            flags |= 1 << g;
+                }
+                const uint64_t bal = __ballot(flags != 0);
+                if (flags) {
+                    const int below = __builtin_amdgcn_mbcnt_hi(
+                        (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                    ktab[count + below] = kb | (flags << 16);
+                }
+                count += __popcll(bal);
+            }
+            if (lane == 0) ktab_n = count;
+        }
+        __syncthreads();
+        const int nact = ktab_n;
+        nkt = nact * TPB;
+        if (nact > 0) {
+            // only the last mask block runs past N: drop its tiles that start at or past N
+            const int last = (ktab[nact - 1] & 0xFFFF) * JA_SPARSE_BLOCK;
+            nkt -= TPB - min(TPB, (N - last + BC - 1) / BC);
+        }
+        if (nkt == 0) {
+            // no row of this workgroup sees any key: O = 0, lse = -inf
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int q_row = qt * BR + w * (QB * 32) + r32 + 32 * qb;
+                if (q_row < N) {
+                    __bf16* orow = O + (((int64_t)b * N + q_row) * H + h) * D;
+#pragma unroll
+                    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            *reinterpret_cast<uint2*>(orow + ob * 32 + j * 8 + hh * 4) =
+                                make_uint2(0, 0);
+                    if (LSE != nullptr && hh == 0) LSE[(int64_t)bh * N + q_row] = -INFINITY;
+                }
+            }
+            return;
+        }
+    }
+    auto tile_k0 = [&](int t) -> int {           // first key of (visited) key tile t
+        if constexpr (SPARSE) return (ktab[t / TPB] & 0xFFFF) * JA_SPARSE_BLOCK + (t % TPB) * BC;
+        return t * BC;
+    };
+    auto tile_on = [&](int t) -> bool {          // SPARSE: this wave's query block sees tile t
+        if constexpr (SPARSE) return ((ktab[t / TPB] >> (16 + sp_group)) & 1) != 0;
+        return true;
+    };
 
     // GATHER: packed token n -> its row (b, n - off[s], h) of stream s's tensor
     auto stream_of = [&](int n) {
@@ -174,7 +247,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     }
     uint4 kst[LOADS], vst[LOADS];                 // staged tiles (global -> registers)
     auto load_k = [&](int kt) {
-        const int k0 = kt * BC;
+        const int k0 = tile_k0(kt);
         if constexpr (GATHER) {
             advance(kcur, st.k, k0);                            // wave-uniform
             if (k0 + BC <= kcur.end) {                          // the tile lies in one stream
@@ -207,7 +280,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         }
     };
     auto load_v = [&](int kt) {
-        const int k0 = kt * BC;
+        const int k0 = tile_k0(kt);
         if constexpr (GATHER) {
             // token-major rows as for K; rows past N repeat row N-1 (finite, and their
             // probabilities are exactly zero)
@@ -402,7 +475,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         pf[qb][2 * kb + u][2 * e + 1] = pb[1];
     };
     auto mask_tail = [&](floatx16 (&s)[QB][KB], int kt) {
-        const int k0 = kt * BC;
+        const int k0 = tile_k0(kt);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -475,6 +548,14 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         float nm[QB], alpha[QB];
         bool grow[QB];
         auto check = [&](int qb) {
+            if constexpr (SPARSE) {
+                if (!tile_on(j)) {                     // wave-uniform: zero weight
+                    grow[qb] = false;
+                    alpha[qb] = 1.f;
+                    nm[qb] = -INFINITY;
+                    return;
+                }
+            }
             float mx = s_in[qb][0][0];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -578,7 +659,8 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float l_tot = wave_halves_sum(l[qb]);
-        const float inv = 1.f / l_tot;
+        // (SPARSE rows that see no key: l = 0, O = 0, lse = -inf)
+        const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
         const int q_row = q_base + 32 * qb;
         if (q_row < N) {
             __bf16* orow = O + (((int64_t)b * N + q_row) * H + h) * D;
@@ -592,22 +674,24 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                         __builtin_convertvector(v, bf16x4);
                 }
             if (LSE != nullptr && hh == 0)
-                LSE[(int64_t)bh * N + q_row] = (m[qb] + log2f(l_tot)) * kLn2;
+                LSE[(int64_t)bh * N + q_row] =
+                    (SPARSE && l_tot == 0.f) ? -INFINITY : (m[qb] + log2f(l_tot)) * kLn2;
         }
     }
 }
 
-template <int D, int NW, int QB, int BC, bool GATHER>
+template <int D, int NW, int QB, int BC, bool GATHER, bool SPARSE = false>
 hipError_t launch_d(const void* q, const void* k, const void* vt, const StreamTable& st, int B,
                     int H, int N, int64_t ldv, float softmax_scale, void* o, float* lse,
-                    hipStream_t stream) {
+                    hipStream_t stream, const uint8_t* mask = nullptr) {
     constexpr int BR = NW * QB * 32;
     const int n_qtiles = (N + BR - 1) / BR;
     const int total = n_qtiles * B * H;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BC, GATHER>), dim3(total), dim3(NW * 64), 0,
-                       stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                       static_cast<const __bf16*>(vt), st, H, N, ldv, softmax_scale * kLog2e,
-                       static_cast<__bf16*>(o), lse, n_qtiles, total);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, BC, GATHER, SPARSE>), dim3(total),
+                       dim3(NW * 64), 0, stream, static_cast<const __bf16*>(q),
+                       static_cast<const __bf16*>(k), static_cast<const __bf16*>(vt), st, mask, H,
+                       N, ldv, softmax_scale * kLog2e, static_cast<__bf16*>(o), lse, n_qtiles,
+                       total);
     return hipGetLastError();
 }
 
@@ -622,6 +706,18 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, 
                                                             softmax_scale, o, lse, stream)
                    : launch_d<128, FWD_NW, FWD_QB, FWD_BC, false>(q, k, vt, none, B, H, N, ldv,
                                                                   softmax_scale, o, lse, stream);
+}
+
+hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
+                                  const uint8_t* mask, int B, int H, int N, int D, int64_t ldv,
+                                  float softmax_scale, void* o, float* lse, hipStream_t stream) {
+    const StreamTable none{};
+    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, false, true>(q, k, vt, none, B, H, N, ldv,
+                                                                  softmax_scale, o, lse, stream,
+                                                                  mask)
+                   : launch_d<128, FWD_NW, FWD_QB, FWD_BC, false, true>(q, k, vt, none, B, H, N,
+                                                                        ldv, softmax_scale, o,
+                                                                        lse, stream, mask);
 }
 
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,

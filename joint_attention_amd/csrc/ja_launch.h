@@ -27,6 +27,10 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, 
                            int D, int64_t ldv, float softmax_scale, void* o, float* lse,
                            hipStream_t stream);
 
+hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
+                                  const uint8_t* mask, int B, int H, int N, int D, int64_t ldv,
+                                  float softmax_scale, void* o, float* lse, hipStream_t stream);
+
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,
                                    float softmax_scale, void* o, float* lse,
                                    hipStream_t stream);

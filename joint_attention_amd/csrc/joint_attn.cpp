@@ -135,6 +135,22 @@ int joint_attn_fwd_bf16(const void* q, const void* k, const void* vt, int B, int
                                           static_cast<hipStream_t>(stream)));
 }
 
+int joint_attn_fwd_bf16_sparse(const void* q, const void* k, const void* vt, int B, int H,
+                               int64_t N, int D, int64_t ldv, const uint8_t* block_mask,
+                               float softmax_scale, void* o, float* lse, void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (N > JA_SPARSE_MAX_N) return JA_EUNSUPPORTED;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (N == 0) return JA_OK;
+    if (!q || !k || !vt || !o || !block_mask) return JA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return JA_EUNSUPPORTED;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
+    return hip_status(ja::launch_fwd_bf16_sparse(q, k, vt, block_mask, B, H, (int)N, D, ldv,
+                                                 softmax_scale, o, lse,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int joint_attn_fwd_bf16_streams(int n_streams, const void* const* q, const void* const* k,
                                 const void* const* v, const int64_t* lens, int B, int H, int D,
                                 float softmax_scale, void* o, float* lse, int64_t* offsets,

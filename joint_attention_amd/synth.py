@@ -158,3 +158,27 @@ def row_sample(w: Workload, n_rows: int, seed: int = 1234, n_pairs: int | None =
         b, h = pairs[int(rng.integers(len(pairs)))]
         rows.add((b, h, int(rng.integers(w.N))))
     return np.asarray(sorted(rows), dtype=np.int64)
+
+
+def block_mask(w: Workload, kind: str = "structured", density: float = 0.25, band: int = 2,
+               seed: int = 0, block: int = 128) -> np.ndarray:
+    """Seeded uint8 block mask [B, H, nb, nb] (nb = ceil(N / block)) for block-sparse runs.
+
+    "random": every (query block, key block) on with probability `density`.
+    "structured": the text blocks (those holding stream 0's tokens) on in whole rows and
+    columns, the key blocks within `band` of each query block's diagonal on, and the other
+    image-image blocks on with probability `density`: a stand-in for the per-block selection
+    of a sparse-attention method, whose rule is not given.
+    """
+    rng = np.random.default_rng(seed)
+    nb = -(-w.N // block)
+    m = (rng.random((w.B, w.H, nb, nb)) < density).astype(np.uint8)
+    if kind == "structured":
+        n_text = -(-w.stream_lens[0] // block) if w.stream_lens[0] > 0 else 0
+        m[:, :, :n_text, :] = 1
+        m[:, :, :, :n_text] = 1
+        qb, kb = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+        m[:, :, np.abs(qb - kb) <= band] = 1
+    elif kind != "random":
+        raise ValueError("kind must be 'random' or 'structured'")
+    return m

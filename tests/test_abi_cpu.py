@@ -152,3 +152,13 @@ def test_quant_streams_validation(lib):
     assert call(2, [fake, fake], [4, 4], D=80)[0] == 2
     st, offs = call(2, [None, None], [0, 0], ldv=0)
     assert st == 0 and offs == [0, 0, 0]
+
+
+def test_sparse_validation(lib):
+    fake = 0x10000
+    f = lib.joint_attn_fwd_bf16_sparse
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, None, 0.1, fake, None, None) == 1   # mask
+    assert f(fake, fake, fake, 1, 2, 64, 96, 64, fake, 0.1, fake, None, None) == 2    # D
+    assert f(fake, fake, fake, 1, 2, 131073, 128, 131088, fake, 0.1, fake, None, None) == 2
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, fake, -1.0, fake, None, None) == 1
+    assert f(None, None, None, 1, 2, 0, 128, 0, None, 0.1, None, None, None) == 0      # N == 0
