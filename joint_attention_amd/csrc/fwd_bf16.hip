@@ -536,6 +536,11 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         if (HAS_QK) load_k(min(j + 3, nkt - 1));
         load_v(min(j + (GATHER ? 2 : 1), nkt - 1));
 
+        // SPARSE: a wave skips the products and numerators of tiles its query block does not
+        // see (their weights are zero; scores left stale are never read: see check)
+        const bool pv_on = !SPARSE || !HAS_PV || tile_on(j - 1);
+        const bool qk_on = !SPARSE || !HAS_QK || tile_on(j + 1);
+        const bool sm_on = !SPARSE || tile_on(j);
         constexpr int S0 = HAS_PV ? 0 : NPV;           // first MFMA step
         constexpr int S1 = HAS_QK ? NPV + NQK : NPV;   // one past the last step
         constexpr int NST = S1 - S0;
@@ -600,12 +605,15 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
             for (int k = 0; k < NST; ++k) {
                 const int st = step_id(k);
                 if (k + LEAD < NST) opnd[(k + LEAD) % (LEAD + 1)] = load_op(step_id(k + LEAD));
-                if (st < NPV) mfma_pv(st, opnd[k % (LEAD + 1)], p_in);
-                else mfma_qk(st - NPV, opnd[k % (LEAD + 1)], s_out);
+                if (st < NPV) {
+                    if (pv_on) mfma_pv(st, opnd[k % (LEAD + 1)], p_in);
+                } else {
+                    if (qk_on) mfma_qk(st - NPV, opnd[k % (LEAD + 1)], s_out);
+                }
                 if (GATHER && k == (NST > FWD_TW ? FWD_TW : NST - 1)) transpose_write(vtr, my_v);
                 // softmax slice: offset check first, then numerators
                 if (k < QB) check(k);
-                if (k >= FIRST) {
+                if (k >= FIRST && sm_on) {
                     const int lo = (k - FIRST) * NEXP / (NST - FIRST);
                     const int hi = (k - FIRST + 1) * NEXP / (NST - FIRST);
 #pragma unroll
@@ -652,8 +660,10 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         const int jl = nkt - 1;
         __bf16* const vs = (jl & 1) ? sv1 : sv0;
         __syncthreads();
-        if (jl & 1) pv_all(vs, pB);
-        else pv_all(vs, pA);
+        if (!SPARSE || tile_on(jl)) {              // (SPARSE: skipped tiles left P stale)
+            if (jl & 1) pv_all(vs, pB);
+            else pv_all(vs, pA);
+        }
     }
 
 #pragma unroll
