@@ -4,11 +4,14 @@
 // (VisualGen FLUX 3 article, everytik.com translation, sections
 // 使用 TensorRT LLM VisualGen 进行 FLUX 3 推理 and 量化注意力与稀疏注意力).
 //
-// Work split.  One workgroup = 4 waves = 256 query rows of one (b, h); each wave owns
-// two 32-row query blocks for the whole key loop (one wave per SIMD, with the whole
-// 512-entry register file: Q, O, two score tiles and two P tiles stay resident).
-// Keys are consumed in tiles of BC = 32; every K or V^T operand read from LDS feeds
-// two MFMAs, one per query block.
+// Work split.  One workgroup = 8 waves = 256 query rows of one (b, h) (head size 64: 4
+// waves, 128 rows); each wave owns one 32-row query block for the whole key loop, two
+// waves share a SIMD, and Q, O, two score tiles and two P tiles stay in its 256 VGPRs.
+// Keys are consumed in tiles of BC = 32, loaded once per workgroup into LDS.
+//
+// Variants of the same kernel: GATHER reads Q, K and V in place from the per-stream
+// tensors (no pack step); SPARSE visits only the key blocks that an input block mask
+// allows.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64).  The wave computes the
 // transposed scores S^T = K Q^T: operand A = 32 keys (from LDS), operand B = the

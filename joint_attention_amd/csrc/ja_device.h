@@ -53,17 +53,4 @@ __device__ inline float wave_halves_sum(float x) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16-byte direct global->LDS load: lane l of the wave writes lds_base + 16 * l
-// (lds_base must be wave-uniform).  The builtin only exists for the device; keeping it
-// out of the host pass also keeps clang from dropping the host stubs of kernel
-// templates that use it.
-__device__ inline void global_load_lds16(const void* gptr, void* lds_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
-#else
-    (void)gptr;
-    (void)lds_base;
-#endif
-}
-
 }  // namespace ja

@@ -15,6 +15,11 @@
 // (exact: a power-of-two rescale of a bf16 value), to be accumulated by a bf16 MFMA next
 // to the fp8 ones.
 //
+// The streams variant (GATHER) reads Q, K and V in place from the per-stream tensors: Q/K
+// blocks as above (row by row where a block straddles two streams); V, whose scale spans
+// all tokens and whose output is channel-major, through a block-parallel channel amax and
+// a 64-token tile kernel that quantises and transposes through LDS.
+//
 // All kernels are bound by HBM bandwidth.  One workgroup owns one scale segment, which
 // is contiguous in the layouts used here (a 128-token block of a BHND tensor is
 // 128 * D consecutive elements; a V channel is one BHDN row): pass 1 takes the absolute
