@@ -17,7 +17,8 @@ value = algorithmic attention flops (4 B H N^2 D) per bf16 step / step time.
 
 Under "shapes", the forward alone is timed on the other shapes: 1024^2 T2I, 2048^2 I2I and
 I2I with one or three reference images (same generator), and one GPU's share of a Ulysses
-head split of 2048^2 T2I (batch 0 with 6 or 3 of the 24 heads).
+head split of 2048^2 T2I (batch 0 with 6 or 3 of the 24 heads).  Where such a grid holds
+fewer than about four workgroups per compute unit, the split-KV forward is timed beside it.
 
 Per-kernel durations come from HIP events recorded on the launch stream around every
 launch inside the timed loops.  The CPU baseline times the fp64 oracle on a bounded
@@ -327,29 +328,44 @@ def main():
         # forward-only throughput of the other shapes: 1024^2 T2I and 2048^2 I2I from the
         # same generator, and one GPU's share of a Ulysses head split of 2048^2 T2I
         # (batch element 0, the first 6 or 3 of the 24 heads: what a rank would hold)
-        def time_fwd(qq, kk, vv, steps, warmup):
-            oo = torch.empty((qq.shape[0], qq.shape[2], qq.shape[1], qq.shape[3]),
-                             dtype=torch.bfloat16, device="cuda")
+        def time_fwd(call, steps, warmup):
             for _ in range(warmup):
-                ja.joint_attn_fwd_bf16(qq, kk, vv, scale, out=oo)
+                call()
             evs = [(ev(), ev()) for _ in range(steps)]
             for a, b2 in evs:
                 a.record(stream)
-                ja.joint_attn_fwd_bf16(qq, kk, vv, scale, out=oo)
+                call()
                 b2.record(stream)
             torch.cuda.synchronize()
             return np.asarray([a.elapsed_time(b2) for a, b2 in evs])
 
         def shape_row(wl, qq, kk, vv, steps):
-            d = time_fwd(qq, kk, vv, steps, 2)
-            fl = 4.0 * qq.shape[0] * qq.shape[1] * qq.shape[2] ** 2 * qq.shape[3]
+            Bq, Hq, Nq, Dq = (int(x) for x in qq.shape)
+            oo = torch.empty((Bq, Nq, Hq, Dq), dtype=torch.bfloat16, device="cuda")
+            d = time_fwd(lambda: ja.joint_attn_fwd_bf16(qq, kk, vv, scale, out=oo), steps, 2)
+            fl = 4.0 * Bq * Hq * Nq ** 2 * Dq
             tf = fl / (d.mean() * 1e-3) / 1e12
-            return {"B": int(qq.shape[0]), "H": int(qq.shape[1]), "N": int(qq.shape[2]),
-                    "stream_lens": list(wl), "fwd_bf16_ms_mean": round(float(d.mean()), 4),
-                    "fwd_bf16_ms_median": round(float(np.median(d)), 4),
-                    "fwd_bf16_ms_min": round(float(d.min()), 4),
-                    "fwd_bf16_tflops": round(tf, 2),
-                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            row = {"B": Bq, "H": Hq, "N": Nq,
+                   "stream_lens": list(wl), "fwd_bf16_ms_mean": round(float(d.mean()), 4),
+                   "fwd_bf16_ms_median": round(float(np.median(d)), 4),
+                   "fwd_bf16_ms_min": round(float(d.min()), 4),
+                   "fwd_bf16_tflops": round(tf, 2),
+                   "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            # grids of fewer than ~4 workgroups per CU: the split-KV forward (key ranges
+            # in parallel + a log-sum-exp merge), workspace allocated outside the timing
+            ns = int(ja.load().joint_attn_fwd_bf16_splitkv_suggest(Bq, Hq, Nq, Dq))
+            if ns > 1:
+                wsb = int(ja.load().joint_attn_fwd_bf16_splitkv_workspace(Bq, Hq, Nq, Dq, ns))
+                wsp = torch.empty((wsb,), dtype=torch.uint8, device="cuda")
+                ds = time_fwd(lambda: ja.joint_attn_fwd_bf16_splitkv(
+                    qq, kk, vv, scale, n_split=ns, workspace=wsp, out=oo), steps, 2)
+                tfs = fl / (ds.mean() * 1e-3) / 1e12
+                row.update({"splitkv_n_split": ns,
+                            "fwd_bf16_splitkv_ms_mean": round(float(ds.mean()), 4),
+                            "fwd_bf16_splitkv_tflops": round(tfs, 2),
+                            "splitkv_frac_of_bf16_peak": round(tfs / PEAK_BF16_TFLOPS, 4)})
+                del wsp
+            return row
 
         shapes = {}
         for hs, name in ((6, "ulysses4_share_t2i_2048"), (3, "ulysses8_share_t2i_2048")):

@@ -129,6 +129,29 @@ int joint_attn_fwd_bf16_sparse(const void *q, const void *k, const void *vt,
                                void *o, float *lse, void *stream);
 
 /*
+ * joint_attn_fwd_bf16_splitkv -- joint_attn_fwd_bf16 with the keys cut into n_split
+ * ranges, one workgroup per (query tile, range), so that short sequences and small head
+ * counts (a 1024x1024 image; one GPU's share of a head split) still fill the GPU.  The
+ * partial results are merged with the log-sum-exp rule: for key sets S_1 .. S_n,
+ *     O = sum_s exp(lse_s - lse) O_s,   lse = ln sum_s exp(lse_s).
+ * Same operation, layouts and arguments as joint_attn_fwd_bf16, plus:
+ *   n_split          1 .. 64 (clamped to the number of 32-key tiles);
+ *                    joint_attn_fwd_bf16_splitkv_suggest() gives one that fills the GPU
+ *   workspace        device scratch owned by the caller, 16-byte aligned, at least
+ *                    joint_attn_fwd_bf16_splitkv_workspace() bytes (fp32 partial outputs
+ *                    and log-sum-exps); its contents on entry do not matter
+ * Results are deterministic but not bit-identical to joint_attn_fwd_bf16 (the sums are
+ * split differently).
+ */
+int64_t joint_attn_fwd_bf16_splitkv_workspace(int B, int H, int64_t N, int D, int n_split);
+int joint_attn_fwd_bf16_splitkv_suggest(int B, int H, int64_t N, int D);
+int joint_attn_fwd_bf16_splitkv(const void *q, const void *k, const void *vt,
+                                int B, int H, int64_t N, int D, int64_t ldv,
+                                float softmax_scale, int n_split,
+                                void *workspace, int64_t workspace_bytes,
+                                void *o, float *lse, void *stream);
+
+/*
  * joint_attn_fwd_bf16_streams -- the same attention as joint_attn_fwd_bf16, reading Q, K
  * and V in place from the per-stream tensors instead of packed copies: the joint
  * sequence of the VisualGen FLUX 3 article (everytik.com translation, section

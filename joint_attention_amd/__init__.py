@@ -5,13 +5,15 @@ include/joint_attn.h); this package is its thin Python binding plus the seeded
 synthetic-input generator used by the tests and the benchmark.
 """
 from ._abi import (JointAttnError, Fp8Tensors, load, joint_attn_vt_ld, joint_attn_pack,
-                   joint_attn_fwd_bf16, joint_attn_fwd_bf16_sparse, joint_attn_fwd_bf16_streams,
+                   joint_attn_fwd_bf16, joint_attn_fwd_bf16_sparse, joint_attn_fwd_bf16_splitkv,
+                   joint_attn_fwd_bf16_streams,
                    joint_attn_quant_fp8,
                    joint_attn_quant_fp8_streams, joint_attn_fwd_fp8, EXPORTS, LIB_PATH, JA_QK_BLOCK, JA_HI_CHANNELS, JA_FP8_PLAIN, JA_FP8_SPLIT,
                    JA_SPARSE_BLOCK, JA_SPARSE_MAX_N)
 
 __all__ = ["JointAttnError", "Fp8Tensors", "load", "joint_attn_vt_ld", "joint_attn_pack",
-           "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse", "joint_attn_fwd_bf16_streams",
+           "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse", "joint_attn_fwd_bf16_splitkv",
+           "joint_attn_fwd_bf16_streams",
            "joint_attn_quant_fp8",
            "joint_attn_quant_fp8_streams", "joint_attn_fwd_fp8",
            "EXPORTS", "LIB_PATH", "JA_QK_BLOCK", "JA_HI_CHANNELS", "JA_FP8_PLAIN",

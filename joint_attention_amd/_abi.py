@@ -26,6 +26,8 @@ JA_FP8_PLAIN, JA_FP8_SPLIT = 0, 1
 
 EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
            "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse",
+           "joint_attn_fwd_bf16_splitkv", "joint_attn_fwd_bf16_splitkv_workspace",
+           "joint_attn_fwd_bf16_splitkv_suggest",
            "joint_attn_fwd_bf16_streams",
            "joint_attn_quant_fp8", "joint_attn_quant_fp8_streams",
            "joint_attn_fwd_fp8")
@@ -66,6 +68,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_fwd_bf16.argtypes = [P, P, P, I, I, I64, I, I64, F, P, P, P]
         h.joint_attn_fwd_bf16_sparse.restype = I
         h.joint_attn_fwd_bf16_sparse.argtypes = [P, P, P, I, I, I64, I, I64, P, F, P, P, P]
+        h.joint_attn_fwd_bf16_splitkv_workspace.restype = I64
+        h.joint_attn_fwd_bf16_splitkv_workspace.argtypes = [I, I, I64, I, I]
+        h.joint_attn_fwd_bf16_splitkv_suggest.restype = I
+        h.joint_attn_fwd_bf16_splitkv_suggest.argtypes = [I, I, I64, I]
+        h.joint_attn_fwd_bf16_splitkv.restype = I
+        h.joint_attn_fwd_bf16_splitkv.argtypes = [P, P, P, I, I, I64, I, I64, F, I, P, I64, P, P,
+                                                  P]
         h.joint_attn_fwd_bf16_streams.restype = I
         h.joint_attn_fwd_bf16_streams.argtypes = [I, P, P, P, P, I, I, I, F,
                                                   P, P, P, P]
@@ -198,6 +207,40 @@ def joint_attn_fwd_bf16_sparse(q, k, vt, block_mask, softmax_scale: float | None
                                            int(vt.shape[3]), block_mask.data_ptr(), scale,
                                            out.data_ptr(), _ptr(lse), _stream(q))
     _check("joint_attn_fwd_bf16_sparse", st)
+    return (out, lse) if return_lse else out
+
+
+def joint_attn_fwd_bf16_splitkv(q, k, vt, softmax_scale: float | None = None,
+                                n_split: int | None = None, workspace=None, out=None,
+                                return_lse: bool = False):
+    """joint_attn_fwd_bf16 with split keys (for grids too small to fill the GPU).  n_split
+    defaults to the library's suggestion; workspace (a device tensor of at least the
+    required bytes) is allocated here if not given."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, N, D = q.shape
+    if tuple(k.shape) != (B, H, N, D) or vt.shape[:3] != (B, H, D):
+        raise ValueError("k must match q; vt must be [B, H, D, ldv]")
+    lib = load()
+    if n_split is None:
+        n_split = lib.joint_attn_fwd_bf16_splitkv_suggest(B, H, N, D)
+    need = int(lib.joint_attn_fwd_bf16_splitkv_workspace(B, H, N, D, int(n_split)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out", 4)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib.joint_attn_fwd_bf16_splitkv(q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D,
+                                         int(vt.shape[3]), scale, int(n_split),
+                                         workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(),
+                                         out.data_ptr(), _ptr(lse), _stream(q))
+    _check("joint_attn_fwd_bf16_splitkv", st)
     return (out, lse) if return_lse else out
 
 

@@ -77,12 +77,16 @@ __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | (
 // SPARSE: only the key blocks that a block mask (uint8 [B][H][nqb][nkb], 128 x 128 blocks)
 // allows for at least one of the workgroup's query blocks are visited; a wave whose own
 // query block does not see a visited block gives it zero weight.
-template <int D, int NW, int QB, int BC, bool GATHER, bool SPARSE>
+// PARTIAL (split-KV): the keys are cut into n_split ranges of whole tiles, one workgroup
+// per (query tile, range); each writes its normalised fp32 partial output and lse to
+// OP / LP ([n_split][B*H][N][D] and [n_split][B*H][N]) for the merge kernel below.
+template <int D, int NW, int QB, int BC, bool GATHER, bool SPARSE, bool PARTIAL = false>
 __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ VT,
     const StreamTable st, const uint8_t* __restrict__ MASK, int H, int N, int64_t ldv, float c2,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int n_qtiles, int total) {
-    static_assert(!(GATHER && SPARSE), "one variant at a time");
+    __bf16* __restrict__ O, float* __restrict__ LSE, int n_qtiles, int total,
+    int n_split = 1, float* __restrict__ OP = nullptr, float* __restrict__ LP = nullptr) {
+    static_assert(int(GATHER) + int(SPARSE) + int(PARTIAL) <= 1, "one variant at a time");
     constexpr int NTHREADS = NW * 64;
     constexpr int BR = NW * QB * 32;             // query rows per workgroup
     constexpr int KB = BC / 32;                  // 32-key blocks per tile
@@ -109,12 +113,22 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
     const int r32 = lane & 31, hh = lane >> 5;
     const int wg = xcd_remap(blockIdx.x, total);
-    const int bh = wg / n_qtiles, qt = wg - bh * n_qtiles;
+    // consecutive workgroups share (b, h) and, in PARTIAL, the key range
+    const int bhs = wg / n_qtiles, qt = wg - bhs * n_qtiles;
+    const int bh = PARTIAL ? bhs / n_split : bhs;
+    const int split = PARTIAL ? bhs - bh * n_split : 0;
     const int b = bh / H, h = bh - b * H;
     const __bf16* Qbh = Q + (int64_t)bh * N * D;
     const __bf16* Kbh = K + (int64_t)bh * N * D;
     const __bf16* Vbh = VT + (int64_t)bh * D * ldv;
     int nkt = (N + BC - 1) / BC;
+    int t_begin = 0;                             // PARTIAL: first key tile of this range
+    if constexpr (PARTIAL) {
+        // n_split <= the number of key tiles (the launcher clamps it): no range is empty
+        const int all = nkt;
+        t_begin = (int)((int64_t)split * all / n_split);
+        nkt = (int)((int64_t)(split + 1) * all / n_split) - t_begin;
+    }
 
     // ---- SPARSE: table of the active 128-key blocks (block index | flags << 16, one flag
     //      per query block of the workgroup), compacted by wave 0 with ballots
@@ -178,7 +192,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     }
     auto tile_k0 = [&](int t) -> int {           // first key of (visited) key tile t
         if constexpr (SPARSE) return (ktab[t / TPB] & 0xFFFF) * JA_SPARSE_BLOCK + (t % TPB) * BC;
-        return t * BC;
+        return (t_begin + t) * BC;
     };
     auto tile_on = [&](int t) -> bool {          // SPARSE: this wave's query block sees tile t
         if constexpr (SPARSE) return ((ktab[t / TPB] >> (16 + sp_group)) & 1) != 0;
@@ -675,6 +689,21 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         // (SPARSE rows that see no key: l = 0, O = 0, lse = -inf)
         const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
         const int q_row = q_base + 32 * qb;
+        if constexpr (PARTIAL) {
+            if (q_row < N) {
+                const int64_t part = (int64_t)split * (total / (n_qtiles * n_split)) + bh;
+                float* orow = OP + (part * N + q_row) * D;
+#pragma unroll
+                for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<floatx4*>(orow + ob * 32 + j * 8 + hh * 4) =
+                            floatx4{oacc[qb][ob][4 * j] * inv, oacc[qb][ob][4 * j + 1] * inv,
+                                    oacc[qb][ob][4 * j + 2] * inv, oacc[qb][ob][4 * j + 3] * inv};
+                if (hh == 0) LP[part * N + q_row] = (m[qb] + log2f(l_tot)) * kLn2;
+            }
+            continue;
+        }
         if (q_row < N) {
             __bf16* orow = O + (((int64_t)b * N + q_row) * H + h) * D;
 #pragma unroll
@@ -691,6 +720,37 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                     (SPARSE && l_tot == 0.f) ? -INFINITY : (m[qb] + log2f(l_tot)) * kLn2;
         }
     }
+}
+
+// split-KV merge -- grid (ceil(N / 8), B*H), 256 threads: 8 rows x (D / 4) channel quads.
+// O = sum_s w_s O_s / sum_s w_s, w_s = exp(lse_s - max lse), lse = max + ln sum_s w_s (the
+// log-sum-exp rule for attention over a union of key sets).
+template <int D>
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ OP,
+                                                           const float* __restrict__ LP,
+                                                           int n_split, int BH, int H, int N,
+                                                           __bf16* __restrict__ O,
+                                                           float* __restrict__ LSE) {
+    constexpr int TPR = D / 4;                    // threads per row
+    constexpr int RPB = 256 / TPR;                // rows per block
+    const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
+    const int row = blockIdx.x * RPB + threadIdx.x / TPR, c = (threadIdx.x % TPR) * 4;
+    if (row >= N) return;
+    float mx = -INFINITY;
+    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, LP[((int64_t)s * BH + bh) * N + row]);
+    float den = 0.f;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_split; ++s) {
+        const int64_t part = (int64_t)s * BH + bh;
+        const float wgt = expf(LP[part * N + row] - mx);
+        const floatx4 o = *reinterpret_cast<const floatx4*>(OP + (part * N + row) * D + c);
+        den += wgt;
+        acc += o * wgt;
+    }
+    const float inv = 1.f / den;
+    *reinterpret_cast<bf16x4*>(O + (((int64_t)b * N + row) * H + h) * D + c) =
+        __builtin_convertvector(acc * inv, bf16x4);
+    if (LSE != nullptr && c == 0) LSE[(int64_t)bh * N + row] = mx + logf(den);
 }
 
 template <int D, int NW, int QB, int BC, bool GATHER, bool SPARSE = false>
@@ -731,6 +791,37 @@ hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
                    : launch_d<128, FWD_NW, FWD_QB, FWD_BC, false, true>(q, k, vt, none, B, H, N,
                                                                         ldv, softmax_scale, o,
                                                                         lse, stream, mask);
+}
+
+hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
+                                   int N, int D, int64_t ldv, float softmax_scale, int n_split,
+                                   float* o_part, float* lse_part, void* o, float* lse,
+                                   hipStream_t stream) {
+    const int tiles = (N + FWD_BC - 1) / FWD_BC;
+    n_split = n_split < tiles ? n_split : tiles;               // every key range non-empty
+    const StreamTable none{};
+    auto go = [&](auto d_tag, auto nw_tag) -> hipError_t {
+        constexpr int DD = decltype(d_tag)::value, NWW = decltype(nw_tag)::value;
+        constexpr int BR = NWW * FWD_QB * 32;
+        const int n_qtiles = (N + BR - 1) / BR;
+        const int total = n_qtiles * B * H * n_split;
+        hipLaunchKernelGGL((fwd_bf16_kernel<DD, NWW, FWD_QB, FWD_BC, false, false, true>),
+                           dim3(total), dim3(NWW * 64), 0, stream, static_cast<const __bf16*>(q),
+                           static_cast<const __bf16*>(k), static_cast<const __bf16*>(vt), none,
+                           nullptr, H, N, ldv, softmax_scale * kLog2e, nullptr, nullptr,
+                           n_qtiles, total, n_split, o_part, lse_part);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(splitkv_merge_kernel<DD>, dim3((N + 256 / (DD / 4) - 1) / (256 / (DD / 4)), B * H),
+                           dim3(256), 0, stream, o_part, lse_part, n_split, B * H, H, N,
+                           static_cast<__bf16*>(o), lse);
+        return hipGetLastError();
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using I4 = std::integral_constant<int, 4>;
+    using INW = std::integral_constant<int, FWD_NW>;
+    return D == 64 ? go(I64{}, I4{}) : go(I128{}, INW{});
 }
 
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,

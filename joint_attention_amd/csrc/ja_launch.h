@@ -31,6 +31,11 @@ hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
                                   const uint8_t* mask, int B, int H, int N, int D, int64_t ldv,
                                   float softmax_scale, void* o, float* lse, hipStream_t stream);
 
+hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
+                                   int N, int D, int64_t ldv, float softmax_scale, int n_split,
+                                   float* o_part, float* lse_part, void* o, float* lse,
+                                   hipStream_t stream);
+
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,
                                    float softmax_scale, void* o, float* lse,
                                    hipStream_t stream);

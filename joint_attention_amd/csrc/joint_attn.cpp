@@ -151,6 +151,46 @@ int joint_attn_fwd_bf16_sparse(const void* q, const void* k, const void* vt, int
                                                  static_cast<hipStream_t>(stream)));
 }
 
+int64_t joint_attn_fwd_bf16_splitkv_workspace(int B, int H, int64_t N, int D, int n_split) {
+    if (B <= 0 || H <= 0 || N < 0 || D <= 0 || n_split <= 0) return -1;
+    return (int64_t)n_split * B * H * N * (D + 1) * (int64_t)sizeof(float);
+}
+
+int joint_attn_fwd_bf16_splitkv_suggest(int B, int H, int64_t N, int D) {
+    if (B <= 0 || H <= 0 || N <= 0 || !head_size_ok(D)) return 1;
+    const int64_t rows = D == 64 ? 128 : 256;                  // query rows per workgroup
+    const int64_t wgs = (N + rows - 1) / rows * B * H;
+    const int64_t want = 4 * 256;                              // >= 4 rounds over 256 CUs
+    int64_t s = (want + wgs - 1) / wgs;
+    const int64_t tiles = (N + 31) / 32;
+    if (s > 16) s = 16;
+    if (s > tiles) s = tiles;
+    return s < 1 ? 1 : (int)s;
+}
+
+int joint_attn_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
+                                int64_t N, int D, int64_t ldv, float softmax_scale, int n_split,
+                                void* workspace, int64_t workspace_bytes, void* o, float* lse,
+                                void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (n_split <= 0 || n_split > 64) return JA_EINVAL;
+    if (N == 0) return JA_OK;
+    if (!q || !k || !vt || !o || !workspace) return JA_EINVAL;
+    if (workspace_bytes < joint_attn_fwd_bf16_splitkv_workspace(B, H, N, D, n_split))
+        return JA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o) ||
+        !aligned16(workspace))
+        return JA_EUNSUPPORTED;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = o_part + (int64_t)n_split * B * H * N * D;
+    return hip_status(ja::launch_fwd_bf16_splitkv(q, k, vt, B, H, (int)N, D, ldv, softmax_scale,
+                                                  n_split, o_part, lse_part, o, lse,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int joint_attn_fwd_bf16_streams(int n_streams, const void* const* q, const void* const* k,
                                 const void* const* v, const int64_t* lens, int B, int H, int D,
                                 float softmax_scale, void* o, float* lse, int64_t* offsets,

@@ -162,3 +162,22 @@ def test_sparse_validation(lib):
     assert f(fake, fake, fake, 1, 2, 131073, 128, 131088, fake, 0.1, fake, None, None) == 2
     assert f(fake, fake, fake, 1, 2, 64, 128, 64, fake, -1.0, fake, None, None) == 1
     assert f(None, None, None, 1, 2, 0, 128, 0, None, 0.1, None, None, None) == 0      # N == 0
+
+
+def test_splitkv_sizes_and_validation(lib):
+    fake = 0x10000
+    ws = lib.joint_attn_fwd_bf16_splitkv_workspace
+    assert ws(2, 24, 4608, 128, 2) == 2 * 2 * 24 * 4608 * 129 * 4
+    assert ws(0, 24, 4608, 128, 2) == -1 and ws(1, 1, 16, 64, 0) == -1
+    sug = lib.joint_attn_fwd_bf16_splitkv_suggest
+    assert sug(2, 24, 16896, 128) == 1          # 3168 workgroups already fill 256 CUs
+    assert sug(2, 24, 4608, 128) == 2           # 864 -> 1728
+    assert sug(1, 6, 16896, 128) == 3           # 396 -> 1188
+    assert sug(1, 1, 40, 128) == 2              # capped by the two 32-key tiles
+    f = lib.joint_attn_fwd_bf16_splitkv
+    need = ws(1, 2, 64, 128, 2)
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 0, fake, need, fake, None, None) == 1
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 2, fake, need - 1, fake, None, None) == 1
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 2, None, need, fake, None, None) == 1
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 2, fake + 8, need, fake, None, None) == 2
+    assert f(None, None, None, 1, 2, 0, 128, 0, 0.1, 2, None, 0, None, None, None) == 0

@@ -1,0 +1,69 @@
+"""GPU: split-KV bf16 forward (joint_attn_fwd_bf16_splitkv) against the fp64 oracle at the
+bf16 bar, for several split counts (1 up to more ranges than key tiles) on ragged shapes,
+and at full size on the shapes it is for (1024^2 T2I, one GPU's share of a head split)."""
+import numpy as np
+import pytest
+
+import oracle
+from joint_attention_amd import synth
+
+from _common import (BF16_MAX_ABS, BF16_REL_F, device_packed, from_device_bf16, gather_rows,
+                     host_streams, max_abs, packed_host, rel_frobenius, widen_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, n_split, sel=None):
+    import joint_attention_amd as ja
+    import torch
+    st = host_streams(w)
+    q, k, vt, offs = device_packed(st)
+    scale = 1.0 / np.sqrt(w.D)
+    o, lse = ja.joint_attn_fwd_bf16_splitkv(q, k, vt, scale, n_split=n_split, return_lse=True)
+    torch.cuda.synchronize()
+    qh, kh, vh, _ = packed_host(st)
+    if sel is None:
+        sel = oracle.all_rows(w.B, w.N, w.H)
+    ref, ref_lse = oracle.attention_rows(qh, kh, vh, scale, sel)
+    got = gather_rows(widen_bf16(from_device_bf16(o)), sel)
+    got_lse = lse.cpu().numpy()[sel[:, 0], sel[:, 1], sel[:, 2]].astype(np.float64)
+    return got, ref, got_lse, ref_lse, o
+
+
+def _assert(tag, got, ref, got_lse, ref_lse):
+    rf, ma = rel_frobenius(got, ref), max_abs(got, ref)
+    le = float(np.abs(got_lse - ref_lse).max())
+    print("%s: rel_F %.3e max %.3e lse %.2e" % (tag, rf, ma, le), flush=True)
+    assert rf <= BF16_REL_F and ma <= BF16_MAX_ABS, (tag, rf, ma)
+    assert le <= 1e-2, (tag, le)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("lens,n_split", [((32, 256), 2), ((100, 29), 3), ((1,), 4),
+                                          ((129, 64, 700), 7), ((63,), 64), ((512, 1000), 1)])
+def test_splitkv_every_row(D, lens, n_split):
+    w = synth.custom("skv", B=2, H=3, D=D, stream_lens=lens, outliers=4 if D == 128 else 0,
+                     seed=13 + sum(lens))
+    _assert("split %d %s D=%d" % (n_split, lens, D), *_run(w, n_split)[:4])
+
+
+@pytest.mark.parametrize("shape", ["t2i_1024", "ulysses4_share", "ulysses8_share"])
+def test_splitkv_full_size_suggested(shape):
+    import joint_attention_amd as ja
+    base = synth.WORKLOADS["t2i_1024_bf16" if shape == "t2i_1024" else "t2i_2048_bf16"]
+    heads = {"t2i_1024": base.H, "ulysses4_share": 6, "ulysses8_share": 3}[shape]
+    B = base.B if shape == "t2i_1024" else 1
+    w = synth.custom(shape, B=B, H=heads, D=base.D, stream_lens=base.stream_lens,
+                     outliers=base.outliers)
+    n = ja.load().joint_attn_fwd_bf16_splitkv_suggest(w.B, w.H, w.N, w.D)
+    assert n > 1, n
+    sel = synth.row_sample(w, 256, seed=23, n_pairs=min(4, w.B * w.H))
+    _assert("%s split %d" % (shape, n), *_run(w, n, sel)[:4])
+
+
+def test_splitkv_deterministic():
+    import torch
+    w = synth.custom("skvd", B=1, H=2, D=128, stream_lens=(64, 900), outliers=4, seed=2)
+    a = _run(w, 5, sel=oracle.all_rows(1, 4, 1))[4].clone()
+    b = _run(w, 5, sel=oracle.all_rows(1, 4, 1))[4]
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
