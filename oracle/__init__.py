@@ -7,6 +7,7 @@ FLUX 3 article (everytik.com translation) and the mathematics of softmax attenti
   attention  -- fp64 two-pass softmax attention (C, OpenMP over rows)
   fp8        -- OCP e4m3 codec, the block/channel quantiser, fp8 attention
   sparse     -- block-sparse attention with an input block mask
+  repair     -- token repair of fp8 attention (repair budget, error measure, selection)
 
 Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import this
 package.  The product path (joint_attention_amd) never imports it, and this package
@@ -18,6 +19,7 @@ from .fp8 import (E4M3_MAX, QK_BLOCK, P_SCALE_LOG2, HI_CHANNELS, e4m3_encode, e4
                   pow2_scale, quantise_qk, quantise_v, select_hi_channels, quantise_qk_split,
                   fp8_attention_rows, e4m3_midpoint_distance)
 from .sparse import SPARSE_BQ, SPARSE_BK, mask_shape, sparse_attention_rows
+from .repair import repair_count, residual_linf, select_repair_tokens, quantise_qk_repair
 from ._native import build, default_threads
 
 __all__ = [
@@ -27,4 +29,5 @@ __all__ = [
     "pow2_scale", "quantise_qk", "quantise_v", "select_hi_channels", "quantise_qk_split",
     "fp8_attention_rows", "e4m3_midpoint_distance",
     "SPARSE_BQ", "SPARSE_BK", "mask_shape", "sparse_attention_rows", "build", "default_threads",
+    "repair_count", "residual_linf", "select_repair_tokens", "quantise_qk_repair",
 ]

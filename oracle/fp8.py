@@ -167,7 +167,8 @@ def e4m3_midpoint_distance(x) -> np.ndarray:
 
 
 def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: float, sel,
-                       block: int = QK_BLOCK, q_hi=None, k_hi=None, rel_window=None):
+                       block: int = QK_BLOCK, q_hi=None, k_hi=None, rel_window=None,
+                       q_exact=None, k_exact=None, q_rep=None, k_rep=None):
     """Attention on the fp8 operands, selected rows (b, h, i).
 
     For each row, in float64 with exactly dequantised operands:
@@ -180,7 +181,10 @@ def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: flo
     q8/k8/v8 are token-major [B, N, H, D] codes; q_scale/k_scale [B, H, nblk];
     v_scale [B, H, D].  In the corrected mode q_hi/k_hi [B, N, H, r] hold the kept
     channels divided by their block scale and add (q_hi . k_hi) * qs * ks to the dot
-    product.  Returns (O [n, D], lse [n]).
+    product.  In the token-repair mode q_rep / k_rep [B, H, n] list, per (b, h), the
+    query / key tokens whose exact values (q_exact / k_exact, token-major bf16 bits
+    [B, N, H, D]) replace the dequantised ones in the dot product.  Returns
+    (O [n, D], lse [n]).
 
     Rounding P to e4m3 is a decision taken on a floating-point logit: an implementation
     whose logits differ by rounding alone may round 2**8 * p_j the other way where it
@@ -202,10 +206,17 @@ def fp8_attention_rows(q8, k8, v8, q_scale, k_scale, v_scale, softmax_scale: flo
             kd = e4m3_decode(k8[b, :, h, :]) * ks_tok[:, None]
             vd = e4m3_decode(v8[b, :, h, :]) * v_scale[b, h][None, :].astype(np.float64)
             kh = None if k_hi is None else k_hi[b, :, h, :] * ks_tok[:, None]
-            cache = {key: (kd, vd, kh)}                   # keep one (b, h) at a time
-        kd, vd, kh = cache[key]
+            if k_rep is not None:
+                idx = np.asarray(k_rep[b, h], dtype=np.int64)
+                kd[idx] = _widen_f32(k_exact[b, idx, h, :]).astype(np.float64)
+            qset = set() if q_rep is None else set(int(t) for t in q_rep[b, h])
+            cache = {key: (kd, vd, kh, qset)}             # keep one (b, h) at a time
+        kd, vd, kh, qset = cache[key]
         qs = float(q_scale[b, h, i // block])
-        qd = e4m3_decode(q8[b, i, h, :]) * qs
+        if int(i) in qset:
+            qd = _widen_f32(q_exact[b, i, h, :]).astype(np.float64)
+        else:
+            qd = e4m3_decode(q8[b, i, h, :]) * qs
         dots = kd @ qd
         if kh is not None:
             dots = dots + kh @ (q_hi[b, i, h, :] * qs)
