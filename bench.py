@@ -12,7 +12,8 @@ The same attention through joint_attn_fwd_bf16_streams (streams read in place, n
 is timed in its own loop and reported under "fused_bf16"; the block-sparse forward with a
 structured block mask under "sparse_bf16".
 The fp8 path (pack x3 -> joint_attn_quant_fp8 -> joint_attn_fwd_fp8) on the same
-inputs is timed the same way in its own loop and reported under "fp8".
+inputs is timed the same way in its own loop and reported under "fp8", for both modes,
+from the streams, and with token repair (rho = 0.005).
 value = algorithmic attention flops (4 B H N^2 D) per bf16 step / step time.
 
 Under "shapes", the forward alone is timed on the other shapes: 1024^2 T2I, 2048^2 I2I and
@@ -323,6 +324,46 @@ def main():
                                "fwd_fp8": round(float(f8s), 4)},
             }
             del t8s
+
+        # token repair (the repair budget rho = 0.005 of VC-Attention FP8): plain codes,
+        # the ceil(rho N) = 85 worst Q and K tokens per (b, h) back at their exact values
+        rho = 0.005
+        t8r = ja.joint_attn_quant_fp8_repair(q, k, vt, rho)
+
+        def step_fp8r(rec):
+            e = [ev() for _ in range(4)] if rec else None
+            if rec:
+                e[0].record(stream)
+            ja.joint_attn_pack(qs_d, "bhnd", out=q)
+            ja.joint_attn_pack(ks_d, "bhnd", out=k)
+            ja.joint_attn_pack(vs_d, "bhdn", out=vt)
+            if rec:
+                e[1].record(stream)
+            ja.joint_attn_quant_fp8_repair(q, k, vt, rho, out=t8r)
+            if rec:
+                e[2].record(stream)
+            ja.joint_attn_fwd_fp8_repair(t8r, scale, out=o)
+            if rec:
+                e[3].record(stream)
+            return e
+
+        log("timing fp8 token-repair path (rho %g, %d tokens per (b, h))" % (rho, t8r.n_repair))
+        wall8r, durs8r = timed(step_fp8r, args.steps, args.warmup)
+        ms8r = wall8r * 1e3 / args.steps
+        p8r, qn8r, f8r = durs8r.mean(axis=0)
+        out["fp8"]["repair"] = {
+            "mode": ja.JA_FP8_REPAIR, "rho": rho, "repaired_tokens_per_bh": t8r.n_repair,
+            "dtype": "fp8 e4m3 + repaired tokens' exact values (fp32 accumulate)",
+            "value": round(flops / (ms8r * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms8r, 4),
+            "step": "pack q,k,v + quant_fp8_repair + fwd_fp8_repair",
+            "kernels_ms": {"pack_qkv": round(float(p8r), 4),
+                           "quant_fp8_repair": round(float(qn8r), 4),
+                           "fwd_fp8_repair": round(float(f8r), 4)},
+            "fwd_fp8_tflops": round(flops / (f8r * 1e-3) / 1e12, 2),
+            "frac_of_fp8_peak": round(flops / (f8r * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        }
+        del t8r
 
     if not args.skip_shapes:
         # forward-only throughput of the other shapes: 1024^2 T2I and 2048^2 I2I from the

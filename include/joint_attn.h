@@ -61,6 +61,10 @@ extern "C" {
 
 #define JA_FP8_PLAIN 0      /* fp8 mode 0: every Q/K channel in e4m3 */
 #define JA_FP8_SPLIT 1      /* fp8 mode 1: JA_HI_CHANNELS outlier channels in bf16 */
+#define JA_FP8_REPAIR 2     /* fp8 token repair: the *_repair entry points below */
+
+#define JA_REPAIR_MAX_N 131072    /* longest sequence of joint_attn_fwd_fp8_repair */
+#define JA_REPAIR_TILE 64         /* v8t_sel row pitch: n_repair rounded up to this */
 
 /* Human-readable name of a status code (static string). */
 const char *joint_attn_strerror(int status);
@@ -257,6 +261,65 @@ int joint_attn_fwd_fp8(const void *q8, const void *k8, const void *v8t,
                        int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
                        int mode, const void *q_hi, const void *k_hi,
                        void *o, float *lse, void *stream);
+
+/*
+ * Token repair of fp8 attention: the repair budget rho of VC-Attention FP8 (VisualGen
+ * FLUX 3 article, everytik.com translation, section 量化注意力与稀疏注意力: the share
+ * rho of tokens with the highest quantisation error gets a residual correction).  Per
+ * (b, h), separately for Q and K, n = ceil(rho N) tokens are repaired: those with the
+ * largest max_c |x_c - decode(code_c) * scale| (exact in fp32; ties to the lower token
+ * index).  Their residual is added back, i.e. they enter Q K^T with their exact bf16
+ * values; P and V are as in mode JA_FP8_PLAIN.
+ *
+ * joint_attn_repair_count -- n = ceil(rho * N) evaluated in double, for N >= 0 and
+ *   0 <= rho <= 1; -1 otherwise.
+ */
+int64_t joint_attn_repair_count(int64_t N, double rho);
+
+/*
+ * joint_attn_quant_fp8_repair -- the JA_FP8_PLAIN quantisation of joint_attn_quant_fp8
+ * (same codes and scales, same layouts), plus the repair selection.
+ *   n_repair          0 <= n_repair <= N (normally joint_attn_repair_count(N, rho))
+ *   q_err, k_err      fp32 [B][H][N] out: each token's largest absolute residual
+ *   q_sel, k_sel      int32 [B][H][n_repair] out: the repaired tokens, ascending
+ *   v8t_sel           e4m3 [B][H][D][ldr] out, ldr = n_repair rounded up to
+ *                     JA_REPAIR_TILE: the V^T codes of the repaired keys (columns k_sel
+ *                     of v8t), zero padded, for the forward's key correction
+ *                     (q_sel, k_sel, v8t_sel may be NULL when n_repair == 0)
+ * Errors: JA_EINVAL for a NULL output or n_repair outside [0, N]; otherwise as
+ * joint_attn_quant_fp8.
+ */
+int joint_attn_quant_fp8_repair(const void *q, const void *k, const void *vt, int B, int H,
+                                int64_t N, int D, int64_t ldv, int64_t n_repair,
+                                void *q8, void *k8, void *v8t,
+                                float *q_scale, float *k_scale, float *v_scale,
+                                float *q_err, float *k_err, int32_t *q_sel, int32_t *k_sel,
+                                void *v8t_sel, void *stream);
+
+/*
+ * joint_attn_fwd_fp8_repair -- joint_attn_fwd_fp8 (mode JA_FP8_PLAIN) with the listed
+ * tokens repaired:
+ *     t_ij = q~_i . k~_j * softmax_scale * log2(e),  q~ = q for listed queries, else
+ *     decode(q8) * qs (likewise k~), P and O as in joint_attn_fwd_fp8.
+ * Three kernels on `stream`, in this order: the plain forward on the codes (writing O
+ * and lse); a correction of every row that replaces each listed key's code term by its
+ * exact-value term (rebuilding the row's state from O and lse); a recomputation of the
+ * listed query rows from their exact values.
+ *   q8 ... v_scale    as written by joint_attn_quant_fp8_repair
+ *   q, k              bf16 BHND [B][H][N][D]: the unquantised inputs of the quantiser
+ *   q_sel, k_sel, v8t_sel   as written by joint_attn_quant_fp8_repair
+ *   N                 at most JA_REPAIR_MAX_N
+ *   o                 bf16 BNHD [B][N][H][D];  lse fp32 [B][H][N], required (the key
+ *                     correction reads and rewrites it)
+ * Errors: as joint_attn_fwd_fp8, plus JA_EINVAL for NULL q / k / lse / lists or n_repair
+ * outside [0, N], JA_EUNSUPPORTED for N > JA_REPAIR_MAX_N.
+ */
+int joint_attn_fwd_fp8_repair(const void *q8, const void *k8, const void *v8t,
+                              const float *q_scale, const float *k_scale, const float *v_scale,
+                              const void *q, const void *k, const int32_t *q_sel,
+                              const int32_t *k_sel, const void *v8t_sel, int64_t n_repair,
+                              int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
+                              void *o, float *lse, void *stream);
 
 #ifdef __cplusplus
 }

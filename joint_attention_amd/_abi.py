@@ -22,7 +22,9 @@ JA_MAX_STREAMS = 16
 JA_QK_BLOCK = 128
 JA_HI_CHANNELS = 16
 JA_SPARSE_BLOCK, JA_SPARSE_MAX_N = 128, 131072
-JA_FP8_PLAIN, JA_FP8_SPLIT = 0, 1
+JA_FP8_PLAIN, JA_FP8_SPLIT, JA_FP8_REPAIR = 0, 1, 2
+JA_REPAIR_MAX_N = 131072
+JA_REPAIR_TILE = 64
 
 EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
            "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse",
@@ -30,7 +32,8 @@ EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld
            "joint_attn_fwd_bf16_splitkv_suggest",
            "joint_attn_fwd_bf16_streams",
            "joint_attn_quant_fp8", "joint_attn_quant_fp8_streams",
-           "joint_attn_fwd_fp8")
+           "joint_attn_fwd_fp8", "joint_attn_repair_count", "joint_attn_quant_fp8_repair",
+           "joint_attn_fwd_fp8_repair")
 
 _lock = threading.Lock()
 _lib = None
@@ -87,6 +90,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_fwd_fp8.restype = I
         h.joint_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, I, I64, I, I64, F, I, P, P, P, P,
                                          P]
+        h.joint_attn_repair_count.restype = I64
+        h.joint_attn_repair_count.argtypes = [I64, ctypes.c_double]
+        h.joint_attn_quant_fp8_repair.restype = I
+        h.joint_attn_quant_fp8_repair.argtypes = [P, P, P, I, I, I64, I, I64, I64, P, P, P, P, P,
+                                                  P, P, P, P, P, P, P]
+        h.joint_attn_fwd_fp8_repair.restype = I
+        h.joint_attn_fwd_fp8_repair.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I64, I, I, I64,
+                                                I, I64, F, P, P, P]
         _lib = h
         return h
 
@@ -281,7 +292,8 @@ def joint_attn_fwd_bf16_streams(q_streams, k_streams, v_streams,
 
 class Fp8Tensors:
     """Outputs of joint_attn_quant_fp8 (device tensors); the split-mode fields are None
-    in mode 0."""
+    outside mode 1, the token-repair fields (q_err, k_err, q_sel, k_sel, n_repair and the
+    unquantised q, k the forward needs) None outside mode 2."""
 
     def __init__(self, mode, q8, k8, v8t, q_scale, k_scale, v_scale, q_hi=None, k_hi=None,
                  hi_idx=None, ch_amax=None):
@@ -289,6 +301,9 @@ class Fp8Tensors:
         self.q8, self.k8, self.v8t = q8, k8, v8t
         self.q_scale, self.k_scale, self.v_scale = q_scale, k_scale, v_scale
         self.q_hi, self.k_hi, self.hi_idx, self.ch_amax = q_hi, k_hi, hi_idx, ch_amax
+        self.q_err = self.k_err = self.q_sel = self.k_sel = self.v8t_sel = None
+        self.q_src = self.k_src = None
+        self.n_repair = 0
 
 
 def _ptr(t):
@@ -376,11 +391,83 @@ def _alloc_fp8(mode, B, H, N, D, ldv, nblk, dev) -> Fp8Tensors:
     return out
 
 
+def joint_attn_repair_count(N: int, rho: float) -> int:
+    """Tokens repaired per (b, h) and operand: ceil(rho * N)."""
+    n = int(load().joint_attn_repair_count(int(N), float(rho)))
+    if n < 0:
+        raise ValueError("joint_attn_repair_count: need N >= 0 and 0 <= rho <= 1")
+    return n
+
+
+def joint_attn_quant_fp8_repair(q, k, vt, rho: float = 0.005, out: Fp8Tensors | None = None
+                                ) -> Fp8Tensors:
+    """Token-repair quantisation (mode JA_FP8_REPAIR): the plain codes and scales plus,
+    per (b, h) and operand, the ceil(rho N) tokens of largest residual.  The result keeps
+    q and k (the forward reads the repaired tokens' exact values from them)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, N, D = q.shape
+    ldv = int(vt.shape[3])
+    n_rep = joint_attn_repair_count(N, rho)
+    nblk = -(-N // JA_QK_BLOCK)
+    if out is not None:
+        if (out.mode != JA_FP8_REPAIR or tuple(out.q8.shape) != (B, H, N, D)
+                or tuple(out.v8t.shape) != (B, H, D, ldv) or out.n_repair != n_rep):
+            raise ValueError("joint_attn_quant_fp8_repair: `out` does not match the inputs")
+    else:
+        out = _alloc_fp8(JA_FP8_REPAIR, B, H, N, D, ldv, nblk, q.device)
+        out.q_err = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        out.k_err = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        out.q_sel = torch.empty((B, H, n_rep), dtype=torch.int32, device=q.device)
+        out.k_sel = torch.empty((B, H, n_rep), dtype=torch.int32, device=q.device)
+        ldr = -(-n_rep // JA_REPAIR_TILE) * JA_REPAIR_TILE
+        out.v8t_sel = torch.empty((B, H, D, ldr), dtype=torch.uint8, device=q.device)
+        out.n_repair = n_rep
+    out.q_src, out.k_src = q, k
+    st = load().joint_attn_quant_fp8_repair(
+        q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D, ldv, n_rep,
+        out.q8.data_ptr(), out.k8.data_ptr(), out.v8t.data_ptr(), out.q_scale.data_ptr(),
+        out.k_scale.data_ptr(), out.v_scale.data_ptr(), out.q_err.data_ptr(),
+        out.k_err.data_ptr(), _ptr(out.q_sel) if n_rep else None,
+        _ptr(out.k_sel) if n_rep else None, _ptr(out.v8t_sel) if n_rep else None, _stream(q))
+    _check("joint_attn_quant_fp8_repair", st)
+    return out
+
+
+def joint_attn_fwd_fp8_repair(t: Fp8Tensors, softmax_scale: float | None = None, out=None,
+                              return_lse: bool = False):
+    """fp8 attention with the repaired tokens of joint_attn_quant_fp8_repair.  Returns O
+    bf16 [B, N, H, D] (and lse)."""
+    torch = _torch()
+    if t.mode != JA_FP8_REPAIR or t.q_src is None or t.k_src is None:
+        raise ValueError("joint_attn_fwd_fp8_repair needs joint_attn_quant_fp8_repair's result")
+    B, H, N, D = t.q8.shape
+    ldv = int(t.v8t.shape[3])
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=t.q8.device)
+    _need(out, torch.bfloat16, "out", 4)
+    # the key correction reads and rewrites lse: always computed
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=t.q8.device)
+    n_rep = int(t.n_repair)
+    st = load().joint_attn_fwd_fp8_repair(
+        t.q8.data_ptr(), t.k8.data_ptr(), t.v8t.data_ptr(), t.q_scale.data_ptr(),
+        t.k_scale.data_ptr(), t.v_scale.data_ptr(), t.q_src.data_ptr(), t.k_src.data_ptr(),
+        _ptr(t.q_sel) if n_rep else None, _ptr(t.k_sel) if n_rep else None,
+        _ptr(t.v8t_sel) if n_rep else None, n_rep, B, H, N, D, ldv, scale, out.data_ptr(),
+        lse.data_ptr(), _stream(t.q8))
+    _check("joint_attn_fwd_fp8_repair", st)
+    return (out, lse) if return_lse else out
+
+
 def joint_attn_fwd_fp8(t: Fp8Tensors, softmax_scale: float | None = None, out=None,
                        return_lse: bool = False):
-    """fp8 attention on joint_attn_quant_fp8's outputs (its mode).  Returns O bf16
-    [B, N, H, D] (and lse)."""
+    """fp8 attention on joint_attn_quant_fp8's outputs (its mode; mode JA_FP8_REPAIR goes
+    to joint_attn_fwd_fp8_repair).  Returns O bf16 [B, N, H, D] (and lse)."""
     torch = _torch()
+    if t.mode == JA_FP8_REPAIR:
+        return joint_attn_fwd_fp8_repair(t, softmax_scale, out, return_lse)
     for x, n in ((t.q8, "q8"), (t.k8, "k8"), (t.v8t, "v8t")):
         _need(x, torch.uint8, n, 4)
     for x, n in ((t.q_scale, "q_scale"), (t.k_scale, "k_scale"), (t.v_scale, "v_scale")):

@@ -51,6 +51,17 @@ hipError_t launch_quant_fp8_streams(const StreamTable& st, int B, int H, int N, 
                                     void* k_hi, int32_t* hi_idx, float* ch_amax,
                                     hipStream_t stream);
 
+hipError_t launch_quant_fp8_repair(const void* q, const void* k, const void* vt, int B, int H,
+                                   int N, int D, int64_t ldv, int n_repair, void* q8, void* k8,
+                                   void* v8t, float* q_scale, float* k_scale, float* v_scale,
+                                   float* q_err, float* k_err, int32_t* q_sel, int32_t* k_sel,
+                                   void* v8t_sel, hipStream_t stream);
+hipError_t launch_fwd_fp8_repair(const void* q8, const void* k8, const void* v8t,
+                                 const float* q_scale, const float* k_scale, const float* v_scale,
+                                 const void* q, const void* k, const int32_t* q_sel,
+                                 const int32_t* k_sel, const void* v8t_sel, int n_repair, int B,
+                                 int H, int N, int D, int64_t ldv, float softmax_scale, void* o,
+                                 float* lse, hipStream_t stream);
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
                           const float* k_scale, const float* v_scale, int B, int H, int N, int D,
                           int64_t ldv, float softmax_scale, int mode, const void* q_hi,

@@ -277,4 +277,64 @@ int joint_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const fl
                                          static_cast<hipStream_t>(stream)));
 }
 
+int64_t joint_attn_repair_count(int64_t N, double rho) {
+    if (N < 0 || !(rho >= 0.0 && rho <= 1.0)) return -1;
+    const double x = std::ceil(rho * (double)N);
+    return x > (double)N ? N : (int64_t)x;
+}
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int joint_attn_quant_fp8_repair(const void* q, const void* k, const void* vt, int B, int H,
+                                int64_t N, int D, int64_t ldv, int64_t n_repair, void* q8,
+                                void* k8, void* v8t, float* q_scale, float* k_scale,
+                                float* v_scale, float* q_err, float* k_err, int32_t* q_sel,
+                                int32_t* k_sel, void* v8t_sel, void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (n_repair < 0 || n_repair > N) return JA_EINVAL;
+    if (N == 0) return JA_OK;
+    if (!q || !k || !vt) return JA_EINVAL;
+    const int ost = check_quant_outputs(JA_FP8_PLAIN, q8, k8, v8t, q_scale, k_scale, v_scale,
+                                        nullptr, nullptr, nullptr, nullptr);
+    if (ost != JA_OK) return ost;
+    if (!q_err || !k_err || (n_repair > 0 && (!q_sel || !k_sel || !v8t_sel))) return JA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt)) return JA_EUNSUPPORTED;
+    if (!aligned4(q_err) || !aligned4(k_err) || (n_repair > 0 && (!aligned4(q_sel) ||
+                                                                   !aligned4(k_sel))))
+        return JA_EUNSUPPORTED;
+    return hip_status(ja::launch_quant_fp8_repair(q, k, vt, B, H, (int)N, D, ldv, (int)n_repair,
+                                                  q8, k8, v8t, q_scale, k_scale, v_scale, q_err,
+                                                  k_err, q_sel, k_sel, v8t_sel,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int joint_attn_fwd_fp8_repair(const void* q8, const void* k8, const void* v8t,
+                              const float* q_scale, const float* k_scale, const float* v_scale,
+                              const void* q, const void* k, const int32_t* q_sel,
+                              const int32_t* k_sel, const void* v8t_sel, int64_t n_repair, int B,
+                              int H, int64_t N, int D, int64_t ldv, float softmax_scale, void* o,
+                              float* lse, void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (n_repair < 0 || n_repair > N) return JA_EINVAL;
+    if (N == 0) return JA_OK;
+    if (N > JA_REPAIR_MAX_N) return JA_EUNSUPPORTED;
+    if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o || !q || !k || !lse)
+        return JA_EINVAL;
+    if (n_repair > 0 && (!q_sel || !k_sel || !v8t_sel)) return JA_EINVAL;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) || !aligned16(q) ||
+        !aligned16(k))
+        return JA_EUNSUPPORTED;
+    if (!aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale) ||
+        !aligned4(lse) || (n_repair > 0 && (!aligned4(q_sel) || !aligned4(k_sel) ||
+                                            !aligned16(v8t_sel))))
+        return JA_EUNSUPPORTED;
+    return hip_status(ja::launch_fwd_fp8_repair(q8, k8, v8t, q_scale, k_scale, v_scale, q, k,
+                                                q_sel, k_sel, v8t_sel, (int)n_repair, B, H, (int)N, D,
+                                                ldv, softmax_scale, o, lse,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

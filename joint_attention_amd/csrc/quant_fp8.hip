@@ -20,6 +20,13 @@
 // all tokens and whose output is channel-major, through a block-parallel channel amax and
 // a 64-token tile kernel that quantises and transposes through LDS.
 //
+// Token repair (the repair budget of VC-Attention FP8, same article section): the plain
+// codes, plus per token the largest absolute residual |x - decode(code) * scale| over the
+// head's channels (exact in binary32: a bf16 value minus its e4m3 neighbour times a power
+// of two), and per (b, h) the n tokens of largest residual (ties to the lower index),
+// found by a 4-pass radix select over the residuals' bit patterns and listed in
+// ascending order by an ordered compaction.
+//
 // All kernels are bound by HBM bandwidth.  One workgroup owns one scale segment, which
 // is contiguous in the layouts used here (a 128-token block of a BHND tensor is
 // 128 * D consecutive elements; a V channel is one BHDN row): pass 1 takes the absolute
@@ -47,6 +54,13 @@ __device__ inline uint32_t e4m3_from_f32(float y) {
         code = (uint32_t)rintf(a * 512.0f);            // exact product, ties to even
     }
     return code | sign;
+}
+
+// e4m3 code -> binary32 value, exact (written from the same definition)
+__device__ inline float f32_from_e4m3(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float a = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -a : a;
 }
 
 // smallest k >= -126 with amax <= 448 * 2^k (k = 0 for amax == 0).  With
@@ -259,7 +273,8 @@ __global__ __launch_bounds__(64) void select_hi_kernel(const float* __restrict__
 
 // grid: (n_blocks, B*H, 2) -- z selects Q (0) or K (1).  With hi_idx, the selected
 // channels' codes are zero and their values / scale go to hi (bf16 [B, H, N, 16]).
-template <int D, bool SPLIT, bool GATHER>
+// ERR: also each token's largest absolute residual -> q_err / k_err (fp32 [B, H, N]).
+template <int D, bool SPLIT, bool GATHER, bool ERR = false>
 __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict__ q,
                                                      const uint16_t* __restrict__ k,
                                                      const StreamTable st, int H, int N,
@@ -269,7 +284,9 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
                                                      float* __restrict__ ks, int nblk,
                                                      const int32_t* __restrict__ hi_idx,
                                                      uint16_t* __restrict__ q_hi,
-                                                     uint16_t* __restrict__ k_hi) {
+                                                     uint16_t* __restrict__ k_hi,
+                                                     float* __restrict__ q_err = nullptr,
+                                                     float* __restrict__ k_err = nullptr) {
     static_assert(NT % (D / 8) == 0 && (JA_QK_BLOCK * D / 8) % NT == 0, "chunk mapping");
     __shared__ float red[NT / 64];
     __shared__ uint32_t mask[D / 32];
@@ -319,10 +336,31 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
         keep = (mask[c0 / 32] >> (c0 % 32)) & 0xFFu;
     }
     uint2* dst = reinterpret_cast<uint2*>(y + base);
+    const float scale = ldexpf(1.f, e);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int c = threadIdx.x + i * NT;
-        if (c < nch) dst[c] = quant8(reg[i], inv, keep);
+        const uint2 code = quant8(reg[i], inv, keep);
+        if (c < nch) dst[c] = code;
+        if constexpr (ERR) {
+            // residuals of this chunk's 8 channels; the D / 8 chunks of a token sit in
+            // D / 8 consecutive lanes of one wave
+            const uint32_t w[4] = {reg[i].x, reg[i].y, reg[i].z, reg[i].w};
+            const uint32_t cw[2] = {code.x, code.y};
+            float r = 0.f;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float lo, hi;
+                bf16x2_to_f32(w[e2], lo, hi);
+                const uint32_t pair = cw[e2 / 2] >> (16 * (e2 % 2));
+                r = fmaxf(r, fabsf(lo - f32_from_e4m3(pair & 0xFFu) * scale));
+                r = fmaxf(r, fabsf(hi - f32_from_e4m3((pair >> 8) & 0xFFu) * scale));
+            }
+#pragma unroll
+            for (int o = 1; o < D / 8; o <<= 1) r = fmaxf(r, __shfl_xor(r, o));
+            if (c < nch && (threadIdx.x % (D / 8)) == 0)
+                (blockIdx.z ? k_err : q_err)[(int64_t)bh * N + t0 + c / (D / 8)] = r;
+        }
     }
     if (SPLIT) {
         uint16_t* hi = (blockIdx.z ? k_hi : q_hi) + ((int64_t)bh * N + t0) * JA_HI_CHANNELS;
@@ -479,6 +517,99 @@ __global__ __launch_bounds__(NT) void v_scale_final_kernel(float* __restrict__ v
     if (i < n) vs[i] = ldexpf(1.f, pow2_exponent(vs[i]));
 }
 
+// Token repair: per (b, h) (blockIdx.x) and operand (blockIdx.y: Q, K), the n tokens of
+// largest residual, ties to the lower index, in ascending order.  The residuals are
+// non-negative floats, whose bit patterns order as integers: four 8-bit radix passes
+// find the n-th largest pattern T and how many tokens equal to T are taken (`need`);
+// an ordered compaction then takes every token above T and the first `need` at T.
+// Requires 1 <= n <= N.
+__global__ __launch_bounds__(NT) void select_repair_kernel(const float* __restrict__ q_err,
+                                                          const float* __restrict__ k_err,
+                                                          int N, int n,
+                                                          int32_t* __restrict__ q_sel,
+                                                          int32_t* __restrict__ k_sel) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sh_prefix, sh_need;
+    __shared__ int wave_take[NT / 64], wave_eq[NT / 64];
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const uint32_t* e = reinterpret_cast<const uint32_t*>((blockIdx.y ? k_err : q_err) +
+                                                          (int64_t)bh * N);
+    int32_t* out = (blockIdx.y ? k_sel : q_sel) + (int64_t)bh * n;
+
+    uint32_t prefix = 0, mask = 0, need = (uint32_t)n;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        hist[tid] = 0;                                      // NT == 256 bins
+        __syncthreads();
+        for (int i = tid; i < N; i += NT) {
+            const uint32_t u = e[i];
+            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            // digit d: the tokens above it (acc) number fewer than need, with it at least need
+            uint32_t acc = 0;
+            int d = 255;
+            for (; d > 0; --d) {
+                if (acc + hist[d] >= need) break;
+                acc += hist[d];
+            }
+            sh_prefix = prefix | ((uint32_t)d << shift);
+            sh_need = need - acc;
+        }
+        __syncthreads();
+        prefix = sh_prefix;
+        need = sh_need;
+        mask |= 255u << shift;
+    }
+    const uint32_t T = prefix;
+
+    int pos = 0, eq_seen = 0;                               // both uniform over the block
+    for (int c0 = 0; c0 < N; c0 += NT) {
+        const int i = c0 + tid;
+        const uint32_t u = i < N ? e[i] : 0u;
+        const bool gt = i < N && u > T, eq = i < N && u == T;
+        const uint64_t below = (1ull << lane) - 1ull;       // lanes before this one
+        const uint64_t beq = __ballot(eq);
+        if (lane == 0) wave_eq[wv] = __popcll(beq);
+        __syncthreads();
+        int eq_rank = eq_seen + __popcll(beq & below), eq_tot = 0;
+        for (int x = 0; x < NT / 64; ++x) {
+            if (x < wv) eq_rank += wave_eq[x];
+            eq_tot += wave_eq[x];
+        }
+        const bool take = gt || (eq && eq_rank < (int)need);
+        const uint64_t bt = __ballot(take);
+        if (lane == 0) wave_take[wv] = __popcll(bt);
+        __syncthreads();
+        int at = pos + __popcll(bt & below), tot = 0;
+        for (int x = 0; x < NT / 64; ++x) {
+            if (x < wv) at += wave_take[x];
+            tot += wave_take[x];
+        }
+        if (take) out[at] = i;
+        pos += tot;
+        eq_seen += eq_tot;
+        __syncthreads();                                    // wave_* reused next chunk
+    }
+}
+
+// Token repair: the V^T codes of the repaired keys, gathered once per (b, h) (blockIdx.x)
+// into [D][ldr] (ldr = n rounded up to 64, zero padded) for the forward's key correction.
+__global__ __launch_bounds__(NT) void gather_v_repair_kernel(const uint8_t* __restrict__ v8t,
+                                                            int64_t ldv, int D,
+                                                            const int32_t* __restrict__ k_sel,
+                                                            int n, int ldr,
+                                                            uint8_t* __restrict__ out) {
+    const int bh = blockIdx.x;
+    const uint8_t* src = v8t + (int64_t)bh * D * ldv;
+    const int32_t* sel = k_sel + (int64_t)bh * n;
+    uint8_t* dst = out + (int64_t)bh * D * ldr;
+    for (int i = threadIdx.x; i < D * ldr; i += NT) {
+        const int c = i / ldr, r = i - c * ldr;
+        dst[i] = r < n ? src[(int64_t)c * ldv + sel[r]] : (uint8_t)0;
+    }
+}
+
 template <int D, bool GATHER>
 hipError_t launch_d(const void* q, const void* k, const void* vt, const StreamTable& st, int B,
                     int H, int N, int64_t ldv, int mode, void* q8, void* k8, void* v8t,
@@ -540,6 +671,40 @@ hipError_t launch_quant_fp8(const void* q, const void* k, const void* vt, int B,
                    : launch_d<128, false>(q, k, vt, none, B, H, N, ldv, mode, q8, k8, v8t,
                                           q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx, ch_amax,
                                           stream);
+}
+
+hipError_t launch_quant_fp8_repair(const void* q, const void* k, const void* vt, int B, int H,
+                                   int N, int D, int64_t ldv, int n_repair, void* q8, void* k8,
+                                   void* v8t, float* q_scale, float* k_scale, float* v_scale,
+                                   float* q_err, float* k_err, int32_t* q_sel, int32_t* k_sel,
+                                   void* v8t_sel, hipStream_t stream) {
+    const int nblk = (N + JA_QK_BLOCK - 1) / JA_QK_BLOCK;
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    const uint16_t* kk = static_cast<const uint16_t*>(k);
+    const StreamTable none{};
+    if (D == 64)
+        hipLaunchKernelGGL((quant_qk_kernel<64, false, false, true>), dim3(nblk, B * H, 2),
+                           dim3(NT), 0, stream, qq, kk, none, H, N, static_cast<uint8_t*>(q8),
+                           static_cast<uint8_t*>(k8), q_scale, k_scale, nblk, nullptr, nullptr,
+                           nullptr, q_err, k_err);
+    else
+        hipLaunchKernelGGL((quant_qk_kernel<128, false, false, true>), dim3(nblk, B * H, 2),
+                           dim3(NT), 0, stream, qq, kk, none, H, N, static_cast<uint8_t*>(q8),
+                           static_cast<uint8_t*>(k8), q_scale, k_scale, nblk, nullptr, nullptr,
+                           nullptr, q_err, k_err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(quant_v_kernel, dim3(D, B * H), dim3(NT), 0, stream,
+                       static_cast<const uint16_t*>(vt), N, D, ldv, static_cast<uint8_t*>(v8t),
+                       v_scale);
+    if (n_repair > 0) {
+        hipLaunchKernelGGL(select_repair_kernel, dim3(B * H, 2), dim3(NT), 0, stream, q_err,
+                           k_err, N, n_repair, q_sel, k_sel);
+        hipLaunchKernelGGL(gather_v_repair_kernel, dim3(B * H), dim3(NT), 0, stream,
+                           static_cast<const uint8_t*>(v8t), ldv, D, k_sel, n_repair,
+                           (n_repair + 63) / 64 * 64, static_cast<uint8_t*>(v8t_sel));
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_fp8_streams(const StreamTable& st, int B, int H, int N, int D,

@@ -181,3 +181,30 @@ def test_splitkv_sizes_and_validation(lib):
     assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 2, None, need, fake, None, None) == 1
     assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 2, fake + 8, need, fake, None, None) == 2
     assert f(None, None, None, 1, 2, 0, 128, 0, 0.1, 2, None, 0, None, None, None) == 0
+
+
+def test_repair_count_and_validation(lib):
+    fake = 0x10000
+    rc = lib.joint_attn_repair_count
+    assert rc(16896, 0.005) == 85 and rc(200, 0.005) == 1 and rc(9, 0.0) == 0 and rc(9, 1.0) == 9
+    assert rc(9, 1.5) == -1 and rc(9, -0.1) == -1 and rc(-1, 0.5) == -1
+    assert rc(9, float("nan")) == -1
+    q = lib.joint_attn_quant_fp8_repair
+    args = lambda n, err=fake, sel=fake: (fake, fake, fake, 1, 2, 64, 128, 64, n, fake, fake,
+                                          fake, fake, fake, fake, err, err, sel, sel, sel, None)
+    assert q(*args(65)) == 1                                   # n_repair > N
+    assert q(*args(-1)) == 1
+    assert q(*args(3, err=None)) == 1                          # residual outputs required
+    assert q(*args(3, sel=None)) == 1                          # lists required when n > 0
+    assert q(*args(3, err=fake + 2)) == 2                      # fp32 outputs 4-byte aligned
+    f = lib.joint_attn_fwd_fp8_repair
+    fa = lambda N, n, qx=fake, sel=fake, lse=fake: (fake, fake, fake, fake, fake, fake, qx, qx,
+                                                    sel, sel, sel, n, 1, 2, N, 128,
+                                                    (N + 15) // 16 * 16, 0.1, fake, lse, None)
+    assert f(*fa(0, 0)) == 0                                   # N == 0: no-op
+    assert f(*fa(131073, 5)) == 2                              # beyond JA_REPAIR_MAX_N
+    assert f(*fa(64, 65)) == 1
+    assert f(*fa(64, 3, qx=None)) == 1                         # exact q, k required
+    assert f(*fa(64, 3, sel=None)) == 1
+    assert f(*fa(64, 3, qx=fake + 8)) == 2                     # bf16 inputs 16-byte aligned
+    assert f(*fa(64, 3, lse=None)) == 1                        # lse is read and rewritten
