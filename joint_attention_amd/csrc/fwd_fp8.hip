@@ -471,225 +471,263 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     }
 }
 
-// Token repair, the listed keys in every row: grid (ceil(N / 128), B*H), 4 waves of 32
-// rows.  Per 64 listed keys (codes and exact rows staged in LDS; V^T codes from the
-// quantiser's gathered copy, ld `ldr`), a wave forms both logits of each key: t^ from the
-// codes exactly as the main loop formed it, t~ from the exact row (Q codes widened to
-// bf16 against it).  Over them it keeps an integer maximum M' (raised only when
-// exceeded, every rescale a power of two) and accumulates dA = sum (e4m3(2^(8+t~-M')) -
-// e4m3(2^(8+t^-M'))) v8 on the fp8 matrix cores and dl = sum 2^(8+t~-M') - 2^(8+t^-M').
-// With u = 2^(M' - 8) / L, L = e^lse of the main kernel:
-//     O' = (O + u vs dA) / (1 + u dl),   lse' = lse + ln(1 + u dl).
+// Token repair, the listed keys in every row: grid (ceil(N / 512), B*H), 4 waves, each
+// taking 4 blocks of 32 rows in turn.  The listed keys are staged in LDS in groups of
+// 128 (codes and exact rows; once per workgroup when there are at most 128), their V^T
+// codes read from the quantiser's gathered copy (ld `ldr`).  For each key a wave forms
+// both logits: t^ from the codes exactly as the main loop formed it, t~ from the exact
+// row (Q codes widened to bf16 against it).  It keeps an integer maximum M', starting at
+// ceil(log2 L) (no code logit exceeds log2 L) and raised only when an exact logit exceeds
+// it (every rescale a power of two), and accumulates
+// dA = sum (e4m3(2^(8+t~-M')) - e4m3(2^(8+t^-M'))) v8 on the fp8 matrix cores and
+// dl = sum 2^(8+t~-M') - 2^(8+t^-M').  With u = 2^(M' - 8) / L, L = e^lse of the main
+// kernel:  O' = (O + u vs dA) / (1 + u dl),   lse' = lse + ln(1 + u dl).
 template <int D>
-__global__ __launch_bounds__(256) void fwd_fp8_keyfix_kernel(
+__global__ __launch_bounds__(256, 2) void fwd_fp8_keyfix_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const __bf16* __restrict__ K,
     const uint8_t* __restrict__ VSEL, const float* __restrict__ QS, const float* __restrict__ KS,
     const float* __restrict__ VS, const int32_t* __restrict__ KSEL, int NREP, int ldr, int H,
     int N, float c2, __bf16* __restrict__ O, float* __restrict__ LSE) {
-    constexpr int NWF = 4, BC = 64, KB = BC / 32, NQC = D / 64, NOB = D / 32, DC = D / 16;
+    constexpr int NWF = 4, QPW = 4, BC = 64, GT = 2, KB = BC / 32, NQC = D / 64, NOB = D / 32;
+    constexpr int DC = D / 16;
     constexpr int KRPB = 256 / D;                       // code rows per 256-byte bank line
     constexpr int XU = D / 8;                           // 16-byte units per exact row
     constexpr int XRPL = 256 / (2 * D) > 0 ? 256 / (2 * D) : 1;
-    __shared__ __attribute__((aligned(16))) uint8_t sk[BC * D];
-    __shared__ __attribute__((aligned(16))) __bf16 skx[BC * D];
-    __shared__ float ksl[BC];
-    __shared__ int ssel[BC];
+    __shared__ __attribute__((aligned(16))) uint8_t sk[GT][BC * D];
+    __shared__ __attribute__((aligned(16))) __bf16 skx[GT][BC * D];
+    __shared__ float ksl[GT * BC];
+    __shared__ int ssel[GT * BC];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
     const int nblk = (N + JA_QK_BLOCK - 1) / JA_QK_BLOCK;
-    const int q_row = blockIdx.x * (NWF * 32) + w * 32 + r32;
-    const int q_ld = min(q_row, N - 1);
     const uint8_t* K8bh = K8 + (int64_t)bh * N * D;
     const __bf16* Kbh = K + (int64_t)bh * N * D;
     const uint8_t* Vsel = VSEL + (int64_t)bh * D * ldr;
     const int32_t* sel = KSEL + (int64_t)bh * NREP;
-    const float qsc2 = QS[(int64_t)bh * nblk + q_ld / JA_QK_BLOCK] * c2;
-    intx8 qf[NQC];
-#pragma unroll
-    for (int c = 0; c < NQC; ++c) {
-        const uint4* p = reinterpret_cast<const uint4*>(Q8 + ((int64_t)bh * N + q_ld) * D + 64 * c +
-                                                        32 * hh);
-        const uint4 x0 = p[0], x1 = p[1];
-        qf[c] = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                      (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    }
     auto kz = [&](int row) { return (row / KRPB) % DC; };
     auto xunit = [&](int row, int u) { return u ^ ((row / XRPL) % XU); };
     auto slot_of = [&](int kb, int a) { return kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8); };
 
-    floatx16 dacc[NOB];
-#pragma unroll
-    for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) dacc[ob][a] = 0.f;
-    float mr = -INFINITY, dl = 0.f;
-    for (int r0 = 0; r0 < NREP; r0 += BC) {
-        __syncthreads();                                // earlier readers of the LDS tiles
-        if (tid < BC) {
-            const int key = r0 + tid < NREP ? sel[r0 + tid] : -1;
+    const int ngroups = (NREP + GT * BC - 1) / (GT * BC);
+    auto stage = [&](int g) {                           // listed keys g*128 .. -> LDS
+        __syncthreads();                                // earlier readers
+        if (tid < GT * BC) {
+            const int r = g * GT * BC + tid;
+            const int key = r < NREP ? sel[r] : -1;
             ssel[tid] = key;
             // empty slots: any finite positive factor, so that -inf logits stay -inf
             ksl[tid] = key >= 0 ? KS[(int64_t)bh * nblk + key / JA_QK_BLOCK] : 1.f;
         }
         __syncthreads();
-        for (int x = tid; x < BC * DC; x += 256) {
+        for (int x = tid; x < GT * BC * DC; x += 256) {
             const int kr = x / DC, u = x % DC, key = ssel[kr];
             const uint4 v = key >= 0 ? *reinterpret_cast<const uint4*>(K8bh + (int64_t)key * D + u * 16)
                                      : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(&sk[kr * D + (u ^ kz(kr)) * 16]) = v;
+            const int tt = kr / BC, row = kr % BC;
+            *reinterpret_cast<uint4*>(&sk[tt][row * D + (u ^ kz(row)) * 16]) = v;
         }
-        for (int x = tid; x < BC * XU; x += 256) {
+        for (int x = tid; x < GT * BC * XU; x += 256) {
             const int kr = x / XU, u = x % XU, key = ssel[kr];
             const uint4 v = key >= 0 ? *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + u * 8)
                                      : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(&skx[kr * D + xunit(kr, u) * 8]) = v;
+            const int tt = kr / BC, row = kr % BC;
+            *reinterpret_cast<uint4*>(&skx[tt][row * D + xunit(row, u) * 8]) = v;
         }
         __syncthreads();
+    };
+    if (ngroups == 1) stage(0);
 
-        floatx16 sh[KB], sx[KB];
+#pragma unroll 1
+    for (int qi = 0; qi < QPW; ++qi) {
+        const int q_row = ((blockIdx.x * NWF + w) * QPW + qi) * 32 + r32;
+        const int q_ld = min(q_row, N - 1);
+        const float qsc2 = QS[(int64_t)bh * nblk + q_ld / JA_QK_BLOCK] * c2;
+        intx8 qf[NQC];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int krow = kb * 32 + swap_bits23(r32);
-#pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                sh[kb][a] = 0.f;
-                sx[kb][a] = 0.f;
-            }
-#pragma unroll
-            for (int c = 0; c < NQC; ++c) {            // as the main loop: channels 64c + 32hh..
-                const int u0 = 4 * c + 2 * hh;
-                const uint4 x0 = *reinterpret_cast<const uint4*>(&sk[krow * D + (u0 ^ kz(krow)) * 16]);
-                const uint4 x1 =
-                    *reinterpret_cast<const uint4*>(&sk[krow * D + ((u0 + 1) ^ kz(krow)) * 16]);
-                const intx8 av = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
-                                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-                sh[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf[c], sh[kb], 0, 0,
-                                                                        0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int c16 = 0; c16 < D / 16; ++c16) {
-                const int c = c16 / 4, wq = 2 * (c16 % 4);
-                const bf16x8 bq = e4m3x8_to_bf16(qf[c][wq], qf[c][wq + 1]);
-                const bf16x8 ak = *reinterpret_cast<const bf16x8*>(
-                    &skx[krow * D + xunit(krow, rep_channel(c16, hh) / 8) * 8]);
-                sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, sx[kb], 0, 0, 0);
-            }
+        for (int c = 0; c < NQC; ++c) {
+            const uint4* p = reinterpret_cast<const uint4*>(Q8 + ((int64_t)bh * N + q_ld) * D +
+                                                            64 * c + 32 * hh);
+            const uint4 x0 = p[0], x1 = p[1];
+            qf[c] = intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                if (r0 + slot_of(kb, a) >= NREP) {
-                    sh[kb][a] = -INFINITY;
-                    sx[kb][a] = -INFINITY;
-                }
-                mx = fmaxf(mx, fmaxf(sh[kb][a] * (qsc2 * ksl[slot_of(kb, a)]), sx[kb][a] * qsc2));
-            }
-        if (__ballot(mx > mr) != 0) {
-            const float m_new = fmaxf(mr, ceilf(wave_halves_max(mx)));
-            const float alpha = (mr == -INFINITY) ? 0.f : ldexpf(1.f, (int)(mr - m_new));
-            mr = m_new;
-            dl *= alpha;
-#pragma unroll
-            for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-                for (int a = 0; a < 16; ++a) dacc[ob][a] *= alpha;
-        }
-        const float bias = 8.f - mr;
-        intx8 px, pn;
-#pragma unroll
-        for (int k = 0; k < 4 * KB; ++k) {
-            const int kb = k / 4, d = k % 4;
-            float p[4], q[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                p[e] = fast_exp2(fmaf(sx[kb][4 * d + e], qsc2, bias));
-                // the main loop's factor for this key, formed as the loop forms it
-                const float fk = qsc2 * ksl[slot_of(kb, 4 * d + e)];
-                q[e] = fast_exp2(fmaf(sh[kb][4 * d + e], fk, bias));
-            }
-            dl += ((p[0] + p[1]) + (p[2] + p[3])) - ((q[0] + q[1]) + (q[2] + q[3]));
-            const int wp = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-            px[k] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wp, true);
-            const int wn = __builtin_amdgcn_cvt_pk_fp8_f32(-q[0], -q[1], 0, false);
-            pn[k] = __builtin_amdgcn_cvt_pk_fp8_f32(-q[2], -q[3], wn, true);
-        }
-        // V^T codes of the gathered keys: row (channel) 32 i + r32, keys r0 + 16 u + 8 hh + e
-#pragma unroll
-        for (int i = 0; i < NOB; ++i) {
-            const uint8_t* vrow = Vsel + (int64_t)(32 * i + r32) * ldr + r0;
-            intx8 av;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint2 x = *reinterpret_cast<const uint2*>(vrow + 16 * u + 8 * hh);
-                av[2 * u] = (int)x.x;
-                av[2 * u + 1] = (int)x.y;
-            }
-            dacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, px, dacc[i], 0, 0, 0, 0,
-                                                                     0, 0);
-            dacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pn, dacc[i], 0, 0, 0, 0,
-                                                                     0, 0);
-        }
-    }
+        float* lp = LSE + (int64_t)bh * N + q_ld;
+        const float lam = *lp * kLog2e;                 // log2 L >= every code logit t^
+        __bf16* orow = O + (((int64_t)b * N + q_ld) * H + h) * D;
 
-    const float dlt = wave_halves_sum(dl);
-    if (q_row < N) {
-        float* lp = LSE + (int64_t)bh * N + q_row;
-        const float lam = *lp * kLog2e;
-        const float u = exp2f(mr - 8.f - lam);
-        const float den = 1.f + u * dlt;
-        const float inv = 1.f / den;
-        __bf16* orow = O + (((int64_t)b * N + q_row) * H + h) * D;
-        const float* vs = VS + (int64_t)bh * D;
+        floatx16 dacc[NOB];
 #pragma unroll
         for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c0 = ob * 32 + j * 8 + hh * 4;
-                const bf16x4 o4 = *reinterpret_cast<const bf16x4*>(orow + c0);
-                floatx4 v;
+            for (int a = 0; a < 16; ++a) dacc[ob][a] = 0.f;
+        // M' starts at ceil(log2 L): no code term exceeds it, only exact logits can raise it
+        float mr = ceilf(lam), dl = 0.f;
+        for (int g = 0; g < ngroups; ++g) {
+            if (ngroups > 1) stage(g);
+            for (int tt = 0; tt < GT; ++tt) {
+                const int r0 = (g * GT + tt) * BC;
+                if (r0 >= NREP) break;
+                // V^T codes of the gathered keys: row (channel) 32 i + r32, keys r0 + 16 u + 8 hh
+                intx8 av[NOB];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[e] = ((float)o4[e] + u * vs[c0 + e] * dacc[ob][4 * j + e]) * inv;
-                *reinterpret_cast<bf16x4*>(orow + c0) = __builtin_convertvector(v, bf16x4);
+                for (int i = 0; i < NOB; ++i) {
+                    const uint8_t* vrow = Vsel + (int64_t)(32 * i + r32) * ldr + r0;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint2 x = *reinterpret_cast<const uint2*>(vrow + 16 * u + 8 * hh);
+                        av[i][2 * u] = (int)x.x;
+                        av[i][2 * u + 1] = (int)x.y;
+                    }
+                }
+                floatx16 sh[KB], sx[KB];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int a = 0; a < 16; ++a) {
+                        sh[kb][a] = 0.f;
+                        sx[kb][a] = 0.f;
+                    }
+#pragma unroll
+                for (int c = 0; c < NQC; ++c) {        // as the main loop: channels 64c + 32hh..
+                    const int u0 = 4 * c + 2 * hh;
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const int krow = kb * 32 + swap_bits23(r32);
+                        const uint4 x0 = *reinterpret_cast<const uint4*>(
+                            &sk[tt][krow * D + (u0 ^ kz(krow)) * 16]);
+                        const uint4 x1 = *reinterpret_cast<const uint4*>(
+                            &sk[tt][krow * D + ((u0 + 1) ^ kz(krow)) * 16]);
+                        const intx8 ak = {(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                                          (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+                        sh[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ak, qf[c], sh[kb],
+                                                                                0, 0, 0, 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int c16 = 0; c16 < D / 16; ++c16) {
+                    const int c = c16 / 4, wq = 2 * (c16 % 4);
+                    const bf16x8 bq = e4m3x8_to_bf16(qf[c][wq], qf[c][wq + 1]);
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) {
+                        const int krow = kb * 32 + swap_bits23(r32);
+                        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(
+                            &skx[tt][krow * D + xunit(krow, rep_channel(c16, hh) / 8) * 8]);
+                        sx[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, bq, sx[kb], 0, 0, 0);
+                    }
+                }
+                const float* kslt = ksl + tt * BC;
+                if (r0 + BC > NREP) {                   // the last, partial tile
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                        for (int a = 0; a < 16; ++a)
+                            if (r0 + slot_of(kb, a) >= NREP) {
+                                sh[kb][a] = -INFINITY;
+                                sx[kb][a] = -INFINITY;
+                            }
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int a = 0; a < 16; ++a) mx = fmaxf(mx, sx[kb][a]);
+                mx *= qsc2;
+                if (__ballot(mx > mr) != 0) {
+                    const float m_new = fmaxf(mr, ceilf(wave_halves_max(mx)));
+                    const float alpha = ldexpf(1.f, (int)(mr - m_new));
+                    mr = m_new;
+                    dl *= alpha;
+#pragma unroll
+                    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                        for (int a = 0; a < 16; ++a) dacc[ob][a] *= alpha;
+                }
+                const float bias = 8.f - mr;
+                intx8 px, pn;
+#pragma unroll
+                for (int k = 0; k < 4 * KB; ++k) {
+                    const int kb = k / 4, d = k % 4;
+                    float p[4], q[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        p[e] = fast_exp2(fmaf(sx[kb][4 * d + e], qsc2, bias));
+                        // the main loop's factor for this key, formed as the loop forms it
+                        const float fk = qsc2 * kslt[slot_of(kb, 4 * d + e)];
+                        q[e] = fast_exp2(fmaf(sh[kb][4 * d + e], fk, bias));
+                    }
+                    dl += ((p[0] + p[1]) + (p[2] + p[3])) - ((q[0] + q[1]) + (q[2] + q[3]));
+                    const int wp = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                    px[k] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wp, true);
+                    const int wn = __builtin_amdgcn_cvt_pk_fp8_f32(-q[0], -q[1], 0, false);
+                    pn[k] = __builtin_amdgcn_cvt_pk_fp8_f32(-q[2], -q[3], wn, true);
+                }
+#pragma unroll
+                for (int i = 0; i < NOB; ++i) {
+                    dacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], px, dacc[i], 0,
+                                                                             0, 0, 0, 0, 0);
+                    dacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], pn, dacc[i], 0,
+                                                                             0, 0, 0, 0, 0);
+                }
             }
-        if (hh == 0) *lp = (lam + log2f(den)) * kLn2;
+        }
+
+        const float dlt = wave_halves_sum(dl);
+        if (q_row < N) {
+            const float u = exp2f(mr - 8.f - lam);
+            const float den = 1.f + u * dlt;
+            const float inv = 1.f / den;
+            const float* vs = VS + (int64_t)bh * D;
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c0 = ob * 32 + j * 8 + hh * 4;
+                    const bf16x4 o4 = *reinterpret_cast<const bf16x4*>(orow + c0);
+                    floatx4 v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = ((float)o4[e] + u * vs[c0 + e] * dacc[ob][4 * j + e]) * inv;
+                    *reinterpret_cast<bf16x4*>(orow + c0) = __builtin_convertvector(v, bf16x4);
+                }
+            if (hh == 0) *lp = (lam + log2f(den)) * kLn2;
+        }
     }
 }
 
-// Token repair, the listed query rows: grid (ceil(n / 32), B*H), 4 waves.  The 32 rows
+// Token repair, the listed query rows: grid (ceil(n / 32), B*H), 8 waves.  The 32 rows
 // of a workgroup (lane r32 <-> row QSEL[32 blockIdx.x + r32]) take their exact bf16 Q
 // values; keys are the codes widened to bf16 (exact), or for listed keys their exact
 // values divided by the block scale (exact: a power of two), so that one factor
 // c2 * k_scale per tile again turns products into base-2 logits.  Wave w visits tiles
-// w, w + 4, ..; P (e4m3, integer running maximum as in the main kernel) times V^T
-// codes runs on the fp8 matrix cores, the operands read straight from memory.  The
-// waves' states (all maxima are integers, so every rescale is a power of two) are
-// merged through LDS at the end.
+// w, w + 8, .., with the next tile's K and V^T codes loaded into registers while the
+// current one is computed; P (e4m3, integer running maximum as in the main kernel)
+// times V^T codes runs on the fp8 matrix cores.  The waves' states (all maxima are
+// integers, so every rescale is a power of two) are merged through LDS in wave order.
 template <int D>
-__global__ __launch_bounds__(256) void fwd_fp8_rows_kernel(
+__global__ __launch_bounds__(512) void fwd_fp8_rows_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const uint8_t* __restrict__ K8,
     const uint8_t* __restrict__ V8T, const float* __restrict__ KS, const float* __restrict__ VS,
     const int32_t* __restrict__ QSEL, const int32_t* __restrict__ KSEL, int NREP, int H, int N,
     int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE) {
-    constexpr int NWR = 4, BC = 64, KB = BC / 32, NOB = D / 32, NK16 = D / 16;
+    constexpr int NWR = 8, NT = NWR * 64, BC = 64, KB = BC / 32, NOB = D / 32, NK16 = D / 16;
     __shared__ uint32_t kmask[JA_REPAIR_MAX_N / 32];
     __shared__ float sm[NWR][32], sl[NWR][32];
-    __shared__ float so[NWR][D][33];                  // [wave][channel][row], padded
+    __shared__ float so[D][33];                        // [channel][row], padded
+    __shared__ __attribute__((aligned(16))) __bf16 sq[32][D + 8];   // exact Q rows, padded
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
     const int nblk = (N + JA_QK_BLOCK - 1) / JA_QK_BLOCK;
 
-    // listed keys as a bitmask
+    // listed keys as a bitmask; the merge buffer starts at zero
     const int nwords = (N + 31) / 32;
-    for (int i = tid; i < nwords; i += 256) kmask[i] = 0;
+    for (int i = tid; i < nwords; i += NT) kmask[i] = 0;
+    for (int i = tid; i < D * 33; i += NT) (&so[0][0])[i] = 0.f;
     __syncthreads();
-    for (int i = tid; i < NREP; i += 256) {
+    for (int i = tid; i < NREP; i += NT) {
         const int key = KSEL[(int64_t)bh * NREP + i];
         atomicOr(&kmask[key >> 5], 1u << (key & 31));
     }
@@ -697,14 +735,59 @@ __global__ __launch_bounds__(256) void fwd_fp8_rows_kernel(
 
     const int slot = blockIdx.x * 32 + r32;
     const int qi = QSEL[(int64_t)bh * NREP + min(slot, NREP - 1)];
-    bf16x8 qb[NK16];
-#pragma unroll
-    for (int c16 = 0; c16 < NK16; ++c16)
-        qb[c16] = *reinterpret_cast<const bf16x8*>(Q + ((int64_t)bh * N + qi) * D +
-                                                   rep_channel(c16, hh));
+    for (int x = tid; x < 32 * (D / 8); x += NT) {     // the 32 rows' exact Q -> LDS
+        const int r = x / (D / 8), u = x % (D / 8);
+        const int qr = QSEL[(int64_t)bh * NREP + min((int)blockIdx.x * 32 + r, NREP - 1)];
+        *reinterpret_cast<uint4*>(&sq[r][u * 8]) =
+            *reinterpret_cast<const uint4*>(Q + ((int64_t)bh * N + qr) * D + u * 8);
+    }
+    __syncthreads();
+    auto q_op = [&](int c16) {                          // B operand: this lane's row
+        return *reinterpret_cast<const bf16x8*>(&sq[r32][rep_channel(c16, hh)]);
+    };
     const uint8_t* K8bh = K8 + (int64_t)bh * N * D;
     const __bf16* Kbh = K + (int64_t)bh * N * D;
     const uint8_t* Vbh = V8T + (int64_t)bh * D * ldv;
+
+    // a tile's K codes (row kb*32 + swap_bits23(r32), 8 channels per k-step) and V^T
+    // codes (row 32 i + r32, keys 16 u + 8 hh ..)
+    // (the k-steps c16 = 2x, 2x + 1 of a lane are 16 consecutive channels: one load)
+    auto load_k = [&](int t, uint2 (&kx)[KB][NK16]) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int key = min(t * BC + kb * 32 + swap_bits23(r32), N - 1);
+#pragma unroll
+            for (int c16 = 0; c16 < NK16; c16 += 2) {
+                const uint4 x = *reinterpret_cast<const uint4*>(K8bh + (int64_t)key * D +
+                                                                rep_channel(c16, hh));
+                kx[kb][c16] = make_uint2(x.x, x.y);
+                kx[kb][c16 + 1] = make_uint2(x.z, x.w);
+            }
+        }
+    };
+    auto load_v = [&](int t, uint2 (&vx)[NOB][4]) {
+#pragma unroll
+        for (int i = 0; i < NOB; ++i) {
+            const uint8_t* vrow = Vbh + (int64_t)(32 * i + r32) * ldv;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k0 = t * BC + 16 * u + 8 * hh;
+                uint2 x = make_uint2(0, 0);
+                if (k0 < N) {
+                    // k0 < N, k0 % 8 == 0 and ldv % 16 == 0 keep the 8 bytes in the row
+                    x = *reinterpret_cast<const uint2*>(vrow + k0);
+                    if (k0 + 8 > N) {
+                        const int keep = N - k0;              // 1..7 bytes
+                        const uint64_t mk = (1ull << (8 * keep)) - 1ull;
+                        const uint64_t v64 = (((uint64_t)x.y << 32) | x.x) & mk;
+                        x = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
+                    }
+                }
+                vx[i][u] = x;
+            }
+        }
+    };
+    uint2 kc[KB][NK16];
 
     floatx16 oacc[NOB];
 #pragma unroll
@@ -713,7 +796,11 @@ __global__ __launch_bounds__(256) void fwd_fp8_rows_kernel(
         for (int a = 0; a < 16; ++a) oacc[ob][a] = 0.f;
     float m = -INFINITY, l = 0.f;
     const int nkt = (N + BC - 1) / BC;
+    if (w < nkt) load_k(w, kc);
     for (int t = w; t < nkt; t += NWR) {
+        uint2 vc[NOB][4], kn[KB][NK16];
+        load_v(t, vc);                                // in flight during QK and the softmax
+        if (t + NWR < nkt) load_k(t + NWR, kn);
         const float ks = KS[(int64_t)bh * nblk + (t * BC) / JA_QK_BLOCK];
         const float inv_ks = 1.f / ks;                // a power of two: exact
         floatx16 s[KB];
@@ -723,19 +810,24 @@ __global__ __launch_bounds__(256) void fwd_fp8_rows_kernel(
             const bool rep = (kmask[key >> 5] >> (key & 31)) & 1u;
 #pragma unroll
             for (int a = 0; a < 16; ++a) s[kb][a] = 0.f;
+            if (__ballot(rep) == 0) {                 // no listed key in this block
 #pragma unroll
-            for (int c16 = 0; c16 < NK16; ++c16) {
-                const int ch = rep_channel(c16, hh);
-                bf16x8 ak;
-                if (rep) {
-                    const bf16x8 x = *reinterpret_cast<const bf16x8*>(Kbh + (int64_t)key * D + ch);
+                for (int c16 = 0; c16 < NK16; ++c16)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        e4m3x8_to_bf16((int)kc[kb][c16].x, (int)kc[kb][c16].y), q_op(c16), s[kb],
+                        0, 0, 0);
+            } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) ak[e] = (__bf16)((float)x[e] * inv_ks);
-                } else {
-                    const uint2 c8 = *reinterpret_cast<const uint2*>(K8bh + (int64_t)key * D + ch);
-                    ak = e4m3x8_to_bf16((int)c8.x, (int)c8.y);
+                for (int c16 = 0; c16 < NK16; ++c16) {
+                    bf16x8 ak = e4m3x8_to_bf16((int)kc[kb][c16].x, (int)kc[kb][c16].y);
+                    if (rep) {
+                        const bf16x8 x = *reinterpret_cast<const bf16x8*>(
+                            Kbh + (int64_t)key * D + rep_channel(c16, hh));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ak[e] = (__bf16)((float)x[e] * inv_ks);
+                    }
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, q_op(c16), s[kb], 0, 0, 0);
                 }
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qb[c16], s[kb], 0, 0, 0);
             }
         }
         const float f = c2 * ks;
@@ -771,34 +863,26 @@ __global__ __launch_bounds__(256) void fwd_fp8_rows_kernel(
             const int wp = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
             pf[k] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wp, true);
         }
-        // V^T codes: row (channel) 32 i + r32, keys t*64 + 16 u + 8 hh + e, u = 0..3
 #pragma unroll
         for (int i = 0; i < NOB; ++i) {
-            const uint8_t* vrow = Vbh + (int64_t)(32 * i + r32) * ldv;
             intx8 av;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int k0 = t * BC + 16 * u + 8 * hh;
-                uint2 x = make_uint2(0, 0);
-                if (k0 < N) {
-                    // k0 < N, k0 % 8 == 0 and ldv % 16 == 0 keep the 8 bytes in the row
-                    x = *reinterpret_cast<const uint2*>(vrow + k0);
-                    if (k0 + 8 > N) {
-                        const int keep = N - k0;              // 1..7 bytes
-                        const uint64_t mk = (1ull << (8 * keep)) - 1ull;
-                        const uint64_t v64 = (((uint64_t)x.y << 32) | x.x) & mk;
-                        x = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
-                    }
-                }
-                av[2 * u] = (int)x.x;
-                av[2 * u + 1] = (int)x.y;
+                av[2 * u] = (int)vc[i][u].x;
+                av[2 * u + 1] = (int)vc[i][u].y;
             }
             oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pf, oacc[i], 0, 0, 0, 0,
                                                                      0, 0);
         }
+        if (t + NWR < nkt) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int c16 = 0; c16 < NK16; ++c16) kc[kb][c16] = kn[kb][c16];
+        }
     }
 
-    // merge the waves: rows' maxima, then rescaled sums and numerators
+    // merge the waves: rows' maxima, then the rescaled numerators added in wave order
     const float lw = wave_halves_sum(l);
     if (hh == 0) {
         sm[w][r32] = m;
@@ -810,12 +894,16 @@ __global__ __launch_bounds__(256) void fwd_fp8_rows_kernel(
     for (int x = 1; x < NWR; ++x) mt = fmaxf(mt, sm[x][r32]);
     const float sc = (m == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m - mt));
     // O^T slot (ob, a): channel ob*32 + 8 (a / 4) + 4 hh + a % 4, row r32
+    for (int x = 0; x < NWR; ++x) {
+        if (w == x) {
 #pragma unroll
-    for (int ob = 0; ob < NOB; ++ob)
+            for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
-        for (int a = 0; a < 16; ++a)
-            so[w][ob * 32 + 8 * (a / 4) + 4 * hh + (a % 4)][r32] = oacc[ob][a] * sc;
-    __syncthreads();
+                for (int a = 0; a < 16; ++a)
+                    so[ob * 32 + 8 * (a / 4) + 4 * hh + (a % 4)][r32] += oacc[ob][a] * sc;
+        }
+        __syncthreads();
+    }
     if (w == 0 && slot < NREP) {
         float lt = 0.f;
 #pragma unroll
@@ -824,11 +912,8 @@ __global__ __launch_bounds__(256) void fwd_fp8_rows_kernel(
         const float inv = 1.f / lt;
         __bf16* orow = O + (((int64_t)b * N + qi) * H + h) * D;
         const float* vs = VS + (int64_t)bh * D;
-        for (int c = hh; c < D; c += 2) {
-            const float v = (so[0][c][r32] + so[1][c][r32]) + (so[2][c][r32] + so[3][c][r32]);
-            orow[c] = (__bf16)(v * inv * vs[c]);
-        }
-        if (LSE != nullptr && hh == 0) LSE[(int64_t)bh * N + qi] = (mt - 8.f + log2f(lt)) * kLn2;
+        for (int c = hh; c < D; c += 2) orow[c] = (__bf16)(so[c][r32] * inv * vs[c]);
+        if (hh == 0) LSE[(int64_t)bh * N + qi] = (mt - 8.f + log2f(lt)) * kLn2;
     }
 }
 
@@ -861,11 +946,11 @@ hipError_t launch_repair_d(const void* q8, const void* k8, const void* v8t, cons
     const float c2 = softmax_scale * kLog2e;
     const int ldr = (n_repair + 63) / 64 * 64;
     // the listed keys in every row, then the listed rows again: in that order on `stream`
-    hipLaunchKernelGGL(fwd_fp8_keyfix_kernel<D>, dim3((N + 127) / 128, B * H), dim3(256), 0,
+    hipLaunchKernelGGL(fwd_fp8_keyfix_kernel<D>, dim3((N + 511) / 512, B * H), dim3(256), 0,
                        stream, static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
                        static_cast<const __bf16*>(k), static_cast<const uint8_t*>(v8t_sel), qs,
                        ks, vs, k_sel, n_repair, ldr, H, N, c2, static_cast<__bf16*>(o), lse);
-    hipLaunchKernelGGL(fwd_fp8_rows_kernel<D>, dim3((n_repair + 31) / 32, B * H), dim3(256), 0,
+    hipLaunchKernelGGL(fwd_fp8_rows_kernel<D>, dim3((n_repair + 31) / 32, B * H), dim3(512), 0,
                        stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                        static_cast<const uint8_t*>(k8), static_cast<const uint8_t*>(v8t), ks, vs,
                        q_sel, k_sel, n_repair, H, N, ldv, c2, static_cast<__bf16*>(o), lse);

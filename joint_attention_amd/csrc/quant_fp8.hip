@@ -520,17 +520,20 @@ __global__ __launch_bounds__(NT) void v_scale_final_kernel(float* __restrict__ v
 // Token repair: per (b, h) (blockIdx.x) and operand (blockIdx.y: Q, K), the n tokens of
 // largest residual, ties to the lower index, in ascending order.  The residuals are
 // non-negative floats, whose bit patterns order as integers: four 8-bit radix passes
-// find the n-th largest pattern T and how many tokens equal to T are taken (`need`);
-// an ordered compaction then takes every token above T and the first `need` at T.
-// Requires 1 <= n <= N.
-__global__ __launch_bounds__(NT) void select_repair_kernel(const float* __restrict__ q_err,
-                                                          const float* __restrict__ k_err,
-                                                          int N, int n,
-                                                          int32_t* __restrict__ q_sel,
-                                                          int32_t* __restrict__ k_sel) {
-    __shared__ uint32_t hist[256];
+// (per-wave histograms, summed per bin) find the n-th largest pattern T and how many
+// tokens equal to T are taken (`need`); an ordered compaction then takes every token
+// above T and the first `need` at T.  Requires 1 <= n <= N.
+constexpr int SNT = 1024;
+__global__ __launch_bounds__(SNT) void select_repair_kernel(const float* __restrict__ q_err,
+                                                           const float* __restrict__ k_err,
+                                                           int N, int n,
+                                                           int32_t* __restrict__ q_sel,
+                                                           int32_t* __restrict__ k_sel) {
+    constexpr int NWV = SNT / 64;
+    __shared__ uint32_t hist[NWV][256];
+    __shared__ uint32_t total[256];
     __shared__ uint32_t sh_prefix, sh_need;
-    __shared__ int wave_take[NT / 64], wave_eq[NT / 64];
+    __shared__ int wave_take[NWV], wave_eq[NWV];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint32_t* e = reinterpret_cast<const uint32_t*>((blockIdx.y ? k_err : q_err) +
                                                           (int64_t)bh * N);
@@ -538,11 +541,17 @@ __global__ __launch_bounds__(NT) void select_repair_kernel(const float* __restri
 
     uint32_t prefix = 0, mask = 0, need = (uint32_t)n;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        hist[tid] = 0;                                      // NT == 256 bins
+        for (int x = tid; x < NWV * 256; x += SNT) (&hist[0][0])[x] = 0;
         __syncthreads();
-        for (int i = tid; i < N; i += NT) {
+        for (int i = tid; i < N; i += SNT) {
             const uint32_t u = e[i];
-            if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+            if ((u & mask) == prefix) atomicAdd(&hist[wv][(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (tid < 256) {
+            uint32_t c = 0;
+            for (int x = 0; x < NWV; ++x) c += hist[x][tid];
+            total[tid] = c;
         }
         __syncthreads();
         if (tid == 0) {
@@ -550,8 +559,8 @@ __global__ __launch_bounds__(NT) void select_repair_kernel(const float* __restri
             uint32_t acc = 0;
             int d = 255;
             for (; d > 0; --d) {
-                if (acc + hist[d] >= need) break;
-                acc += hist[d];
+                if (acc + total[d] >= need) break;
+                acc += total[d];
             }
             sh_prefix = prefix | ((uint32_t)d << shift);
             sh_need = need - acc;
@@ -564,7 +573,7 @@ __global__ __launch_bounds__(NT) void select_repair_kernel(const float* __restri
     const uint32_t T = prefix;
 
     int pos = 0, eq_seen = 0;                               // both uniform over the block
-    for (int c0 = 0; c0 < N; c0 += NT) {
+    for (int c0 = 0; c0 < N; c0 += SNT) {
         const int i = c0 + tid;
         const uint32_t u = i < N ? e[i] : 0u;
         const bool gt = i < N && u > T, eq = i < N && u == T;
@@ -573,7 +582,7 @@ __global__ __launch_bounds__(NT) void select_repair_kernel(const float* __restri
         if (lane == 0) wave_eq[wv] = __popcll(beq);
         __syncthreads();
         int eq_rank = eq_seen + __popcll(beq & below), eq_tot = 0;
-        for (int x = 0; x < NT / 64; ++x) {
+        for (int x = 0; x < NWV; ++x) {
             if (x < wv) eq_rank += wave_eq[x];
             eq_tot += wave_eq[x];
         }
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(NT) void select_repair_kernel(const float* __restri
         if (lane == 0) wave_take[wv] = __popcll(bt);
         __syncthreads();
         int at = pos + __popcll(bt & below), tot = 0;
-        for (int x = 0; x < NT / 64; ++x) {
+        for (int x = 0; x < NWV; ++x) {
             if (x < wv) at += wave_take[x];
             tot += wave_take[x];
         }
@@ -595,18 +604,20 @@ __global__ __launch_bounds__(NT) void select_repair_kernel(const float* __restri
 
 // Token repair: the V^T codes of the repaired keys, gathered once per (b, h) (blockIdx.x)
 // into [D][ldr] (ldr = n rounded up to 64, zero padded) for the forward's key correction.
+// grid (B*H, D / 8).
 __global__ __launch_bounds__(NT) void gather_v_repair_kernel(const uint8_t* __restrict__ v8t,
                                                             int64_t ldv, int D,
                                                             const int32_t* __restrict__ k_sel,
                                                             int n, int ldr,
                                                             uint8_t* __restrict__ out) {
-    const int bh = blockIdx.x;
+    // blockIdx.y: a group of 8 channels
+    const int bh = blockIdx.x, c0 = blockIdx.y * 8;
     const uint8_t* src = v8t + (int64_t)bh * D * ldv;
     const int32_t* sel = k_sel + (int64_t)bh * n;
     uint8_t* dst = out + (int64_t)bh * D * ldr;
-    for (int i = threadIdx.x; i < D * ldr; i += NT) {
-        const int c = i / ldr, r = i - c * ldr;
-        dst[i] = r < n ? src[(int64_t)c * ldv + sel[r]] : (uint8_t)0;
+    for (int i = threadIdx.x; i < 8 * ldr; i += NT) {
+        const int c = c0 + i / ldr, r = i % ldr;
+        dst[(int64_t)c * ldr + r] = r < n ? src[(int64_t)c * ldv + sel[r]] : (uint8_t)0;
     }
 }
 
@@ -698,9 +709,9 @@ hipError_t launch_quant_fp8_repair(const void* q, const void* k, const void* vt,
                        static_cast<const uint16_t*>(vt), N, D, ldv, static_cast<uint8_t*>(v8t),
                        v_scale);
     if (n_repair > 0) {
-        hipLaunchKernelGGL(select_repair_kernel, dim3(B * H, 2), dim3(NT), 0, stream, q_err,
+        hipLaunchKernelGGL(select_repair_kernel, dim3(B * H, 2), dim3(SNT), 0, stream, q_err,
                            k_err, N, n_repair, q_sel, k_sel);
-        hipLaunchKernelGGL(gather_v_repair_kernel, dim3(B * H), dim3(NT), 0, stream,
+        hipLaunchKernelGGL(gather_v_repair_kernel, dim3(B * H, D / 8), dim3(NT), 0, stream,
                            static_cast<const uint8_t*>(v8t), ldv, D, k_sel, n_repair,
                            (n_repair + 63) / 64 * 64, static_cast<uint8_t*>(v8t_sel));
     }
