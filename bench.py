@@ -7,7 +7,10 @@ Workload: FLUX 3 Image Klein 2048x2048 text-to-image joint attention -- batch 2
 (N = 16896), seeded synthetic bf16 inputs (joint_attention_amd.synth), resident in HBM
 before timing starts.
 
-One timed step of the bf16 path = pack(Q), pack(K), pack(V^T) -> joint_attn_fwd_bf16.
+One timed step of the bf16 path = pack(Q), pack(K), pack(V^T) -> joint_attn_fwd_bf16_splitkv
+with the library's suggested split (the query tiles of the last, partial round of
+workgroups split into key ranges; workspace allocated before timing).  The same step with
+the plain joint_attn_fwd_bf16 is reported under "plain_bf16".
 The same attention through joint_attn_fwd_bf16_streams (streams read in place, no pack)
 is timed in its own loop and reported under "fused_bf16"; the block-sparse forward with a
 structured block mask under "sparse_bf16".
@@ -156,19 +159,33 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def step_bf16(rec):
-        e0, e1, e2 = (ev(), ev(), ev()) if rec else (None, None, None)
-        if rec:
-            e0.record(stream)
-        ja.joint_attn_pack(qs_d, "bhnd", out=q)
-        ja.joint_attn_pack(ks_d, "bhnd", out=k)
-        ja.joint_attn_pack(vs_d, "bhdn", out=vt)
-        if rec:
-            e1.record(stream)
-        ja.joint_attn_fwd_bf16(q, k, vt, scale, out=o)
-        if rec:
-            e2.record(stream)
-        return (e0, e1, e2)
+    # the forward of the timed step: the split-KV call with the library's suggested split
+    # (the query tiles of the last, partial round of workgroups run as key ranges in
+    # parallel, merged by log-sum-exp; 1 = the plain forward); workspace allocated here,
+    # outside the timing, like the outputs
+    ns_main = int(ja.load().joint_attn_fwd_bf16_splitkv_suggest(B, H, N, D))
+    ws_main = torch.empty((int(ja.load().joint_attn_fwd_bf16_splitkv_workspace(
+        B, H, N, D, ns_main)),), dtype=torch.uint8, device="cuda")
+
+    def make_step(fwd):
+        def step(rec):
+            e0, e1, e2 = (ev(), ev(), ev()) if rec else (None, None, None)
+            if rec:
+                e0.record(stream)
+            ja.joint_attn_pack(qs_d, "bhnd", out=q)
+            ja.joint_attn_pack(ks_d, "bhnd", out=k)
+            ja.joint_attn_pack(vs_d, "bhdn", out=vt)
+            if rec:
+                e1.record(stream)
+            fwd()
+            if rec:
+                e2.record(stream)
+            return (e0, e1, e2)
+        return step
+
+    step_bf16 = make_step(lambda: ja.joint_attn_fwd_bf16_splitkv(
+        q, k, vt, scale, n_split=ns_main, workspace=ws_main, out=o))
+    step_plain = make_step(lambda: ja.joint_attn_fwd_bf16(q, k, vt, scale, out=o))
 
     def timed(step, steps, warmup):
         for _ in range(warmup):
@@ -183,7 +200,8 @@ def main():
         durs = [[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in evs]
         return wall, np.asarray(durs)
 
-    log("timing bf16 path: %d warmup + %d steps" % (args.warmup, args.steps))
+    log("timing bf16 path (split-KV, n_split %d): %d warmup + %d steps"
+        % (ns_main, args.warmup, args.steps))
     wall, durs = timed(step_bf16, args.steps, args.warmup)
     ms_step = wall * 1e3 / args.steps
     pack_ms, fwd_ms = durs.mean(axis=0)
@@ -197,15 +215,31 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D,
-                   "stream_lens": list(w.stream_lens), "step": "pack q,k,v + fwd_bf16"},
+                   "stream_lens": list(w.stream_lens),
+                   "step": "pack q,k,v + fwd_bf16_splitkv (n_split %d for the last round's "
+                           "query tiles)" % ns_main},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name), "kernel": "fwd_bf16_kernel<128>",
+                     "traffic": measured_traffic(w.name),
+                     "kernel": "fwd_bf16_kernel<128,splitkv> + splitkv_merge_kernel<128>",
                      "avg_launch_ms": round(float(fwd_ms), 4),
                      "median_launch_ms": round(float(np.median(durs[:, 1])), 4),
                      "min_launch_ms": round(float(durs[:, 1].min()), 4)},
-        "kernels_ms": {"pack_qkv": round(float(pack_ms), 4), "fwd_bf16": round(float(fwd_ms), 4)},
+        "kernels_ms": {"pack_qkv": round(float(pack_ms), 4),
+                       "fwd_bf16_splitkv": round(float(fwd_ms), 4)},
         "pct_of_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+    }
+
+    # the same step with the plain forward (every query tile over all keys)
+    log("timing bf16 path with the plain forward")
+    wall_p, durs_p = timed(step_plain, args.steps, args.warmup)
+    ms_p = wall_p * 1e3 / args.steps
+    fwd_p = float(durs_p[:, 1].mean())
+    out["plain_bf16"] = {
+        "step": "pack q,k,v + fwd_bf16", "value": round(flops / (ms_p * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "ms_per_step": round(ms_p, 4), "kernel": "fwd_bf16_kernel<128>",
+        "fwd_ms": round(fwd_p, 4), "fwd_tflops": round(flops / (fwd_p * 1e-3) / 1e12, 2),
+        "frac_of_bf16_peak": round(flops / (fwd_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
     }
 
     # the same step through the call that reads the streams in place (no pack)
@@ -253,7 +287,7 @@ def main():
         "mask": "structured: text rows/columns, band 2, 15 % random", "block": 128,
         "attended_fraction": round(frac, 4), "kernel_ms": round(sp_ms, 4),
         "effective_tflops": round(flops * frac / (sp_ms * 1e-3) / 1e12, 2),
-        "speedup_vs_dense": round(float(fwd_ms) / sp_ms, 3),
+        "speedup_vs_dense": round(fwd_p / sp_ms, 3),
     }
 
     if not args.skip_fp8:

@@ -77,15 +77,18 @@ __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | (
 // SPARSE: only the key blocks that a block mask (uint8 [B][H][nqb][nkb], 128 x 128 blocks)
 // allows for at least one of the workgroup's query blocks are visited; a wave whose own
 // query block does not see a visited block gives it zero weight.
-// PARTIAL (split-KV): the keys are cut into n_split ranges of whole tiles, one workgroup
-// per (query tile, range); each writes its normalised fp32 partial output and lse to
-// OP / LP ([n_split][B*H][N][D] and [n_split][B*H][N]) for the merge kernel below.
+// PARTIAL (split-KV): the first n_full query tiles (whole rounds of workgroups over the
+// CUs) run over all keys and write O as usual; for each later query tile the keys are cut
+// into n_split ranges of whole tiles, one workgroup per (query tile, range), each writing
+// its normalised fp32 partial output and lse (OP [part][BR][D], LP [part][BR], part =
+// (tile - n_full) * n_split + range) for the merge kernel below.
 template <int D, int NW, int QB, int BC, bool GATHER, bool SPARSE, bool PARTIAL = false>
 __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ VT,
     const StreamTable st, const uint8_t* __restrict__ MASK, int H, int N, int64_t ldv, float c2,
     __bf16* __restrict__ O, float* __restrict__ LSE, int n_qtiles, int total,
-    int n_split = 1, float* __restrict__ OP = nullptr, float* __restrict__ LP = nullptr) {
+    int n_split = 1, float* __restrict__ OP = nullptr, float* __restrict__ LP = nullptr,
+    int n_full = 0) {
     static_assert(int(GATHER) + int(SPARSE) + int(PARTIAL) <= 1, "one variant at a time");
     constexpr int NTHREADS = NW * 64;
     constexpr int BR = NW * QB * 32;             // query rows per workgroup
@@ -112,18 +115,32 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
     const int r32 = lane & 31, hh = lane >> 5;
-    const int wg = xcd_remap(blockIdx.x, total);
-    // consecutive workgroups share (b, h) and, in PARTIAL, the key range
-    const int bhs = wg / n_qtiles, qt = wg - bhs * n_qtiles;
-    const int bh = PARTIAL ? bhs / n_split : bhs;
-    const int split = PARTIAL ? bhs - bh * n_split : 0;
+    // PARTIAL: the whole-round workgroups and the split ones are renumbered separately, so
+    // that both spread evenly over the XCDs (n_full is a multiple of the slot count)
+    const int bid = blockIdx.x;
+    const int wg = !PARTIAL ? xcd_remap(bid, total)
+                   : bid < n_full ? xcd_remap(bid, n_full)
+                                  : n_full + xcd_remap(bid - n_full, total - n_full);
+    // consecutive workgroups share (b, h); in PARTIAL those past n_full are the ranges of
+    // one query tile
+    int unit = wg, split = 0;
+    bool part_wg = false;
+    if constexpr (PARTIAL) {
+        if (wg >= n_full) {
+            const int x = wg - n_full;
+            unit = n_full + x / n_split;
+            split = x - (x / n_split) * n_split;
+            part_wg = true;
+        }
+    }
+    const int bh = unit / n_qtiles, qt = unit - bh * n_qtiles;
     const int b = bh / H, h = bh - b * H;
     const __bf16* Qbh = Q + (int64_t)bh * N * D;
     const __bf16* Kbh = K + (int64_t)bh * N * D;
     const __bf16* Vbh = VT + (int64_t)bh * D * ldv;
     int nkt = (N + BC - 1) / BC;
     int t_begin = 0;                             // PARTIAL: first key tile of this range
-    if constexpr (PARTIAL) {
+    if (PARTIAL && part_wg) {
         // n_split <= the number of key tiles (the launcher clamps it): no range is empty
         const int all = nkt;
         t_begin = (int)((int64_t)split * all / n_split);
@@ -689,10 +706,11 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         // (SPARSE rows that see no key: l = 0, O = 0, lse = -inf)
         const float inv = (SPARSE && l_tot == 0.f) ? 0.f : 1.f / l_tot;
         const int q_row = q_base + 32 * qb;
-        if constexpr (PARTIAL) {
+        if (PARTIAL && part_wg) {
             if (q_row < N) {
-                const int64_t part = (int64_t)split * (total / (n_qtiles * n_split)) + bh;
-                float* orow = OP + (part * N + q_row) * D;
+                const int64_t part = (int64_t)(unit - n_full) * n_split + split;
+                const int64_t r = part * BR + (q_row - qt * BR);
+                float* orow = OP + r * D;
 #pragma unroll
                 for (int ob = 0; ob < NOB; ++ob)
 #pragma unroll
@@ -700,7 +718,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                         *reinterpret_cast<floatx4*>(orow + ob * 32 + j * 8 + hh * 4) =
                             floatx4{oacc[qb][ob][4 * j] * inv, oacc[qb][ob][4 * j + 1] * inv,
                                     oacc[qb][ob][4 * j + 2] * inv, oacc[qb][ob][4 * j + 3] * inv};
-                if (hh == 0) LP[part * N + q_row] = (m[qb] + log2f(l_tot)) * kLn2;
+                if (hh == 0) LP[r] = (m[qb] + log2f(l_tot)) * kLn2;
             }
             continue;
         }
@@ -722,28 +740,34 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     }
 }
 
-// split-KV merge -- grid (ceil(N / 8), B*H), 256 threads: 8 rows x (D / 4) channel quads.
-// O = sum_s w_s O_s / sum_s w_s, w_s = exp(lse_s - max lse), lse = max + ln sum_s w_s (the
-// log-sum-exp rule for attention over a union of key sets).
-template <int D>
+// split-KV merge -- grid ((n_units - n_full) * BR / RPB), 256 threads: RPB rows x (D / 4)
+// channel quads of one split query tile.  O = sum_s w_s O_s / sum_s w_s,
+// w_s = exp(lse_s - max lse), lse = max + ln sum_s w_s (the log-sum-exp rule for attention
+// over a union of key sets).
+template <int D, int BR>
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(const float* __restrict__ OP,
                                                            const float* __restrict__ LP,
-                                                           int n_split, int BH, int H, int N,
-                                                           __bf16* __restrict__ O,
+                                                           int n_split, int n_full, int n_qtiles,
+                                                           int H, int N, __bf16* __restrict__ O,
                                                            float* __restrict__ LSE) {
     constexpr int TPR = D / 4;                    // threads per row
     constexpr int RPB = 256 / TPR;                // rows per block
-    const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
-    const int row = blockIdx.x * RPB + threadIdx.x / TPR, c = (threadIdx.x % TPR) * 4;
+    constexpr int BPU = BR / RPB;                 // blocks per query tile
+    const int ut = blockIdx.x / BPU;              // split tile index, 0 ..
+    const int unit = n_full + ut;
+    const int bh = unit / n_qtiles, qt = unit - bh * n_qtiles, b = bh / H, h = bh - b * H;
+    const int r = (blockIdx.x - ut * BPU) * RPB + threadIdx.x / TPR, c = (threadIdx.x % TPR) * 4;
+    const int row = qt * BR + r;
     if (row >= N) return;
+    const int64_t base = (int64_t)ut * n_split * BR + r;   // part (ut, 0), row r
     float mx = -INFINITY;
-    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, LP[((int64_t)s * BH + bh) * N + row]);
+    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, LP[base + (int64_t)s * BR]);
     float den = 0.f;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n_split; ++s) {
-        const int64_t part = (int64_t)s * BH + bh;
-        const float wgt = expf(LP[part * N + row] - mx);
-        const floatx4 o = *reinterpret_cast<const floatx4*>(OP + (part * N + row) * D + c);
+        const int64_t pr = base + (int64_t)s * BR;
+        const float wgt = expf(LP[pr] - mx);
+        const floatx4 o = *reinterpret_cast<const floatx4*>(OP + pr * D + c);
         den += wgt;
         acc += o * wgt;
     }
@@ -793,27 +817,53 @@ hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
                                                                         lse, stream, mask);
 }
 
+int splitkv_slots(int D) {
+    // workgroups that run at once: one per CU for the 8-wave D = 128 kernel, as the
+    // runtime's occupancy calculation gives for the kernel actually launched
+    int dev = 0, cus = 256, per = 1;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    hipError_t e = D == 64
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &per, fwd_bf16_kernel<64, 4, FWD_QB, FWD_BC, false, false, true>, 4 * 64, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &per, fwd_bf16_kernel<128, FWD_NW, FWD_QB, FWD_BC, false, false, true>, FWD_NW * 64,
+              0);
+    if (e != hipSuccess || per < 1) per = 1;
+    return cus * per;
+}
+
+int splitkv_rows_per_tile(int D) { return D == 64 ? 4 * FWD_QB * 32 : FWD_NW * FWD_QB * 32; }
+
 hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
                                    int N, int D, int64_t ldv, float softmax_scale, int n_split,
                                    float* o_part, float* lse_part, void* o, float* lse,
                                    hipStream_t stream) {
     const int tiles = (N + FWD_BC - 1) / FWD_BC;
     n_split = n_split < tiles ? n_split : tiles;               // every key range non-empty
+    const int BRr = splitkv_rows_per_tile(D);
+    const int n_units = (N + BRr - 1) / BRr * B * H;
+    const int tail = n_units % splitkv_slots(D);              // tiles of the last, partial round
+    if (n_split <= 1 || tail == 0) return launch_fwd_bf16(q, k, vt, B, H, N, D, ldv, softmax_scale,
+                                                           o, lse, stream);
+    const int n_full = n_units - tail;
     const StreamTable none{};
     auto go = [&](auto d_tag, auto nw_tag) -> hipError_t {
         constexpr int DD = decltype(d_tag)::value, NWW = decltype(nw_tag)::value;
         constexpr int BR = NWW * FWD_QB * 32;
+        constexpr int RPB = 256 / (DD / 4);
         const int n_qtiles = (N + BR - 1) / BR;
-        const int total = n_qtiles * B * H * n_split;
+        const int total = n_full + tail * n_split;
         hipLaunchKernelGGL((fwd_bf16_kernel<DD, NWW, FWD_QB, FWD_BC, false, false, true>),
                            dim3(total), dim3(NWW * 64), 0, stream, static_cast<const __bf16*>(q),
                            static_cast<const __bf16*>(k), static_cast<const __bf16*>(vt), none,
-                           nullptr, H, N, ldv, softmax_scale * kLog2e, nullptr, nullptr,
-                           n_qtiles, total, n_split, o_part, lse_part);
+                           nullptr, H, N, ldv, softmax_scale * kLog2e, static_cast<__bf16*>(o),
+                           lse, n_qtiles, total, n_split, o_part, lse_part, n_full);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(splitkv_merge_kernel<DD>, dim3((N + 256 / (DD / 4) - 1) / (256 / (DD / 4)), B * H),
-                           dim3(256), 0, stream, o_part, lse_part, n_split, B * H, H, N,
+        hipLaunchKernelGGL((splitkv_merge_kernel<DD, BR>), dim3(tail * (BR / RPB)), dim3(256), 0,
+                           stream, o_part, lse_part, n_split, n_full, n_qtiles, H, N,
                            static_cast<__bf16*>(o), lse);
         return hipGetLastError();
     };

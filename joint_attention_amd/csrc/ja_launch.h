@@ -31,6 +31,10 @@ hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
                                   const uint8_t* mask, int B, int H, int N, int D, int64_t ldv,
                                   float softmax_scale, void* o, float* lse, hipStream_t stream);
 
+// split-KV planning: workgroups that run at once on the current device, and query rows
+// per workgroup of the bf16 forward for head size D
+int splitkv_slots(int D);
+int splitkv_rows_per_tile(int D);
 hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
                                    int N, int D, int64_t ldv, float softmax_scale, int n_split,
                                    float* o_part, float* lse_part, void* o, float* lse,

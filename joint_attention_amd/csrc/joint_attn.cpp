@@ -152,20 +152,41 @@ int joint_attn_fwd_bf16_sparse(const void* q, const void* k, const void* vt, int
 }
 
 int64_t joint_attn_fwd_bf16_splitkv_workspace(int B, int H, int64_t N, int D, int n_split) {
-    if (B <= 0 || H <= 0 || N < 0 || D <= 0 || n_split <= 0) return -1;
-    return (int64_t)n_split * B * H * N * (D + 1) * (int64_t)sizeof(float);
+    if (B <= 0 || H <= 0 || N < 0 || D <= 0 || n_split <= 0 || !head_size_ok(D)) return -1;
+    // an upper bound: every query tile split (only the last round's are)
+    const int64_t br = ja::splitkv_rows_per_tile(D);
+    const int64_t units = (N + br - 1) / br * B * H;
+    return (int64_t)n_split * units * br * (D + 1) * (int64_t)sizeof(float);
 }
 
 int joint_attn_fwd_bf16_splitkv_suggest(int B, int H, int64_t N, int D) {
     if (B <= 0 || H <= 0 || N <= 0 || !head_size_ok(D)) return 1;
-    const int64_t rows = D == 64 ? 128 : 256;                  // query rows per workgroup
-    const int64_t wgs = (N + rows - 1) / rows * B * H;
-    const int64_t want = 4 * 256;                              // >= 4 rounds over 256 CUs
-    int64_t s = (want + wgs - 1) / wgs;
+    const int64_t br = ja::splitkv_rows_per_tile(D);
+    const int64_t units = (N + br - 1) / br * B * H;
+    const int64_t slots = ja::splitkv_slots(D);
+    const int64_t tail = units % slots;                 // query tiles of the last round
+    if (tail == 0) return 1;
     const int64_t tiles = (N + 31) / 32;
-    if (s > 16) s = 16;
-    if (s > tiles) s = tiles;
-    return s < 1 ? 1 : (int)s;
+    // In units of one round of full-length workgroups: the tail unsplit costs 1; split s
+    // ways it takes ceil(tail * s / slots) rounds of 1/s length, plus about 6 key tiles of
+    // fixed cost per workgroup (prologue, epilogue), plus reading its fp32 partials back
+    // in the merge (at ~4 TB/s, against a round of ~1 PFLOP/s work; their writes overlap
+    // the forward).  A split
+    // is suggested only where it should save over a tenth of a round (measured at 2048^2
+    // and 1024^2 T2I and head-split shares of 2048^2).
+    const double round_s = (double)slots * br * tiles * 32.0 * 4.0 * D / 1.0e15;
+    double best = 0.9;
+    int best_s = 1;
+    for (int s = 2; s <= 16 && s <= tiles; ++s) {
+        const double rounds = (double)((tail * s + slots - 1) / slots);
+        const double merge = (double)tail * s * br * (D + 1) * 4.0 / 4.0e12 / round_s;
+        const double cost = rounds * (1.0 / s + 6.0 / (double)tiles) + merge;
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_s = s;
+        }
+    }
+    return best_s;
 }
 
 int joint_attn_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
@@ -184,8 +205,9 @@ int joint_attn_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, in
         !aligned16(workspace))
         return JA_EUNSUPPORTED;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
+    const int64_t br = ja::splitkv_rows_per_tile(D);
     float* o_part = static_cast<float*>(workspace);
-    float* lse_part = o_part + (int64_t)n_split * B * H * N * D;
+    float* lse_part = o_part + (int64_t)n_split * ((N + br - 1) / br * B * H) * br * D;
     return hip_status(ja::launch_fwd_bf16_splitkv(q, k, vt, B, H, (int)N, D, ldv, softmax_scale,
                                                   n_split, o_part, lse_part, o, lse,
                                                   static_cast<hipStream_t>(stream)));

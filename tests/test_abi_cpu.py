@@ -167,13 +167,20 @@ def test_sparse_validation(lib):
 def test_splitkv_sizes_and_validation(lib):
     fake = 0x10000
     ws = lib.joint_attn_fwd_bf16_splitkv_workspace
-    assert ws(2, 24, 4608, 128, 2) == 2 * 2 * 24 * 4608 * 129 * 4
+    assert ws(2, 24, 4608, 128, 2) == 2 * 2 * 24 * 4608 * 129 * 4      # 18 whole 256-row tiles
+    assert ws(1, 1, 40, 128, 3) == 3 * 256 * 129 * 4                  # one padded tile
+    assert ws(1, 1, 40, 64, 3) == 3 * 128 * 65 * 4                   # 128-row tiles at D = 64
     assert ws(0, 24, 4608, 128, 2) == -1 and ws(1, 1, 16, 64, 0) == -1
+    assert ws(1, 1, 16, 96, 2) == -1
     sug = lib.joint_attn_fwd_bf16_splitkv_suggest
-    assert sug(2, 24, 16896, 128) == 1          # 3168 workgroups already fill 256 CUs
-    assert sug(2, 24, 4608, 128) == 2           # 864 -> 1728
-    assert sug(1, 6, 16896, 128) == 3           # 396 -> 1188
-    assert sug(1, 1, 40, 128) == 2              # capped by the two 32-key tiles
+    # without a GPU the plan assumes 256 slots (one 8-wave workgroup per CU)
+    assert sug(2, 24, 4608, 128) == 2           # 864 tiles: 96 in the last round
+    assert sug(1, 6, 16896, 128) == 7           # 396 tiles: 140 in the last round
+    assert sug(1, 3, 16896, 128) == 1           # 198 tiles, all in one round: not worth it
+    assert sug(1, 8, 16896, 128) == 16          # 528 tiles: 16 in the last round
+    assert sug(2, 24, 16896, 128) == 5          # 3168 tiles: 96 in the last round
+    assert sug(2, 24, 512, 128) == 1            # 16 key tiles: the fixed cost dominates
+    assert sug(1, 1, 40, 128) == 1
     f = lib.joint_attn_fwd_bf16_splitkv
     need = ws(1, 2, 64, 128, 2)
     assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 0, fake, need, fake, None, None) == 1

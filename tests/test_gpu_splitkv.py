@@ -1,6 +1,7 @@
 """GPU: split-KV bf16 forward (joint_attn_fwd_bf16_splitkv) against the fp64 oracle at the
 bf16 bar, for several split counts (1 up to more ranges than key tiles) on ragged shapes,
-and at full size on the shapes it is for (1024^2 T2I, one GPU's share of a head split)."""
+with whole rounds of unsplit query tiles before a split last round, and at full size with
+the suggested split (1024^2 and 2048^2 T2I, one GPU's share of a head split)."""
 import numpy as np
 import pytest
 
@@ -47,16 +48,27 @@ def test_splitkv_every_row(D, lens, n_split):
     _assert("split %d %s D=%d" % (n_split, lens, D), *_run(w, n_split)[:4])
 
 
-@pytest.mark.parametrize("shape", ["t2i_1024", "ulysses4_share", "ulysses8_share"])
-def test_splitkv_full_size_suggested(shape):
+@pytest.mark.parametrize("D,n_split", [(128, 3), (64, 4)])
+def test_splitkv_whole_rounds_and_tail(D, n_split):
+    # more query tiles than one round of workgroups: the whole rounds run unsplit, the
+    # last round's tiles split (every row compared)
+    w = synth.custom("skvt", B=2, H=65, D=D, stream_lens=(100, 200), outliers=4 if D == 128 else 0,
+                     seed=31)
+    _assert("whole rounds + tail D=%d split %d" % (D, n_split), *_run(w, n_split)[:4])
+
+
+@pytest.mark.parametrize("shape", ["t2i_1024", "t2i_2048", "ulysses4_share", "ulysses8_share"])
+def test_splitkv_full_size(shape):
     import joint_attention_amd as ja
     base = synth.WORKLOADS["t2i_1024_bf16" if shape == "t2i_1024" else "t2i_2048_bf16"]
-    heads = {"t2i_1024": base.H, "ulysses4_share": 6, "ulysses8_share": 3}[shape]
-    B = base.B if shape == "t2i_1024" else 1
+    heads = {"t2i_1024": base.H, "t2i_2048": base.H, "ulysses4_share": 6,
+             "ulysses8_share": 3}[shape]
+    B = base.B if shape in ("t2i_1024", "t2i_2048") else 1
     w = synth.custom(shape, B=B, H=heads, D=base.D, stream_lens=base.stream_lens,
                      outliers=base.outliers)
+    # the suggested split, or 5 where the library suggests none (all tiles then split)
     n = ja.load().joint_attn_fwd_bf16_splitkv_suggest(w.B, w.H, w.N, w.D)
-    assert n > 1, n
+    n = n if n > 1 else 5
     sel = synth.row_sample(w, 256, seed=23, n_pairs=min(4, w.B * w.H))
     _assert("%s split %d" % (shape, n), *_run(w, n, sel)[:4])
 
