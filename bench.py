@@ -47,14 +47,15 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0
 
-# HBM bytes per fwd_bf16 launch on this workload from two rocprofv3 --pmc runs
-# (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a plain copy of known size needs), valid
-# for the kernel sources whose hash is recorded; any later change reports null.
+# HBM bytes per timed forward (the split-KV kernel and its merge) on this workload from
+# two rocprofv3 --pmc runs (FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors a plain copy of
+# known size needs), valid for the kernel sources whose hash is recorded; any later
+# change reports null.
 MEASURED_TRAFFIC = {
     "workload": "t2i_2048_bf16",
-    "bytes": 1661200998,
+    "bytes": 1899518165,
     "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/ja_device.h"),
-    "sha256_16": "83aad4489abfaa33",
+    "sha256_16": "6f77e4f89a6ae5b2",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
 
