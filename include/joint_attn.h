@@ -133,19 +133,26 @@ int joint_attn_fwd_bf16_sparse(const void *q, const void *k, const void *vt,
                                void *o, float *lse, void *stream);
 
 /*
- * joint_attn_fwd_bf16_splitkv -- joint_attn_fwd_bf16 with the keys cut into n_split
- * ranges, one workgroup per (query tile, range), so that short sequences and small head
- * counts (a 1024x1024 image; one GPU's share of a head split) still fill the GPU.  The
- * partial results are merged with the log-sum-exp rule: for key sets S_1 .. S_n,
+ * joint_attn_fwd_bf16_splitkv -- joint_attn_fwd_bf16 with the query tiles of the last,
+ * partial round of workgroups split into n_split key ranges (one workgroup per (tile,
+ * range)), so that the CUs left idle by that round get work: a grid of B*H*ceil(N/256)
+ * workgroups (128-row tiles at D = 64) rarely fills whole rounds (2048x2048 T2I: 3168
+ * tiles for 256 CUs; a 1024x1024 image; one GPU's share of a head split).  The tiles
+ * that fill whole rounds run over all keys.  The split tiles' partial results are
+ * merged with the log-sum-exp rule: for key sets S_1 .. S_n,
  *     O = sum_s exp(lse_s - lse) O_s,   lse = ln sum_s exp(lse_s).
  * Same operation, layouts and arguments as joint_attn_fwd_bf16, plus:
- *   n_split          1 .. 64 (clamped to the number of 32-key tiles);
- *                    joint_attn_fwd_bf16_splitkv_suggest() gives one that fills the GPU
+ *   n_split          1 .. 64 (clamped to the number of 32-key tiles; 1, or a grid of
+ *                    whole rounds, is the plain forward);
+ *                    joint_attn_fwd_bf16_splitkv_suggest() gives one from a model of
+ *                    the rounds saved against the partial results' cost (1 = none)
  *   workspace        device scratch owned by the caller, 16-byte aligned, at least
  *                    joint_attn_fwd_bf16_splitkv_workspace() bytes (fp32 partial outputs
- *                    and log-sum-exps); its contents on entry do not matter
- * Results are deterministic but not bit-identical to joint_attn_fwd_bf16 (the sums are
- * split differently).
+ *                    and log-sum-exps; an upper bound that assumes every tile split);
+ *                    its contents on entry do not matter
+ * Results are deterministic but, in the split tiles, not bit-identical to
+ * joint_attn_fwd_bf16 (the sums are split differently).  Calls that share a workspace
+ * must not overlap.
  */
 int64_t joint_attn_fwd_bf16_splitkv_workspace(int B, int H, int64_t N, int D, int n_split);
 int joint_attn_fwd_bf16_splitkv_suggest(int B, int H, int64_t N, int D);

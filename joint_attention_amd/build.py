@@ -22,8 +22,9 @@ ARCH = os.environ.get("JA_OFFLOAD_ARCH", "gfx950")
 SOURCES = ["joint_attn.cpp", "pack.hip", "fwd_bf16.hip", "quant_fp8.hip", "fwd_fp8.hip"]
 
 # per-source code-generation options: the bf16 forward keeps its MFMA accumulators in
-# architectural VGPRs where possible, which is what lets its 64 query rows per wave,
-# two score tiles and two P tiles fit without spilling
+# architectural VGPRs (the score tiles are read by the softmax right away), which is
+# what lets its 32-row output accumulators, two score tiles, two P tiles and the staged
+# K/V tiles fit in 256 VGPRs without spilling at two waves per SIMD
 # (and, no NaN ever being an operand there, skips the NaN canonicalisation in front of
 # every v_max; infinities keep their meaning)
 EXTRA_FLAGS = {"fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
