@@ -308,10 +308,10 @@ int joint_attn_quant_fp8_repair(const void *q, const void *k, const void *vt, in
  * tokens repaired:
  *     t_ij = q~_i . k~_j * softmax_scale * log2(e),  q~ = q for listed queries, else
  *     decode(q8) * qs (likewise k~), P and O as in joint_attn_fwd_fp8.
- * Three kernels on `stream`, in this order: the plain forward on the codes (writing O
- * and lse); a correction of every row that replaces each listed key's code term by its
- * exact-value term (rebuilding the row's state from O and lse); a recomputation of the
- * listed query rows from their exact values.
+ * Two launches on `stream`, in this order: the plain forward on the codes (writing O
+ * and lse) with, appended to its grid, a recomputation of the listed query rows from
+ * their exact values; then a correction of every other row that replaces each listed
+ * key's code term by its exact-value term (rebuilding the row's state from O and lse).
  *   q8 ... v_scale    as written by joint_attn_quant_fp8_repair
  *   q, k              bf16 BHND [B][H][N][D]: the unquantised inputs of the quantiser
  *   q_sel, k_sel, v8t_sel   as written by joint_attn_quant_fp8_repair

@@ -38,8 +38,9 @@
 // total L = e^lse it adds (e4m3(2^(8 + t~ - M')) - e4m3(2^(8 + t^ - M'))) 2^(M' - 8) v
 // to L O and 2^t~ - 2^t^ to L, for an integer M' (the e4m3 rounding of a power-of-two
 // shift is the same for any integer M below the subnormal range, so the loop's code
-// term cancels to within 2^-14 of the row maximum).  fwd_fp8_rows_kernel finally
-// recomputes the listed query rows from their exact values.
+// term cancels to within 2^-14 of the row maximum).  Workgroups appended to the main grid
+// (repair_rows) recompute the listed query rows from their exact values; the main and the
+// correction kernels leave those rows alone.
 #include <type_traits>
 
 #include "ja_device.h"
@@ -80,13 +81,250 @@ __device__ inline bf16x8 e4m3x8_to_bf16(int w0, int w1) {
 // Q operand already holds in that lane (64 (c16 / 4) + 32 hh + 8 (c16 % 4) + e)
 __device__ inline int rep_channel(int c16, int hh) { return 64 * (c16 / 4) + 32 * hh + 8 * (c16 % 4); }
 
-template <int D, int NW, bool HI>
+// Token repair, the listed query rows: the workgroups after the main grid of
+// fwd_fp8_kernel<..., RROWS> (dispatched last, they fill the CUs its last round leaves
+// idle), block rb of (b, h) slice bh.  The 32 rows of a workgroup (lane r32 <-> row
+// QSEL[32 rb + r32]) take their exact bf16 Q
+// values; keys are the codes widened to bf16 (exact), or for listed keys their exact
+// values divided by the block scale (exact: a power of two), so that one factor
+// c2 * k_scale per tile again turns products into base-2 logits.  Wave w visits tiles
+// w, w + NWR, .., with the next tile's K codes loaded into registers while the
+// current one is computed; P (e4m3, integer running maximum as in the main kernel)
+// times V^T codes runs on the fp8 matrix cores.  The waves' states (all maxima are
+// integers, so every rescale is a power of two) are merged through LDS in wave order.
+template <int D, int NWR>
+__device__ __forceinline__ void repair_rows(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const uint8_t* __restrict__ K8,
+    const uint8_t* __restrict__ V8T, const float* __restrict__ KS, const float* __restrict__ VS,
+    const int32_t* __restrict__ QSEL, const int32_t* __restrict__ KSEL, int NREP, int H, int N,
+    int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE, const int rb,
+    const int bh) {
+    constexpr int NT = NWR * 64, BC = 64, KB = BC / 32, NOB = D / 32, NK16 = D / 16;
+    __shared__ uint32_t kmask[JA_REPAIR_MAX_N / 32];
+    __shared__ float sm[NWR][32], sl[NWR][32];
+    __shared__ float so[D][33];                        // [channel][row], padded
+    __shared__ __attribute__((aligned(16))) __bf16 sq[32][D + 8];   // exact Q rows, padded
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r32 = lane & 31, hh = lane >> 5;
+    const int b = bh / H, h = bh - b * H;
+    const int nblk = (N + JA_QK_BLOCK - 1) / JA_QK_BLOCK;
+
+    // listed keys as a bitmask; the merge buffer starts at zero
+    const int nwords = (N + 31) / 32;
+    for (int i = tid; i < nwords; i += NT) kmask[i] = 0;
+    for (int i = tid; i < D * 33; i += NT) (&so[0][0])[i] = 0.f;
+    __syncthreads();
+    for (int i = tid; i < NREP; i += NT) {
+        const int key = KSEL[(int64_t)bh * NREP + i];
+        atomicOr(&kmask[key >> 5], 1u << (key & 31));
+    }
+    __syncthreads();
+
+    const int slot = rb * 32 + r32;
+    const int qi = QSEL[(int64_t)bh * NREP + min(slot, NREP - 1)];
+    for (int x = tid; x < 32 * (D / 8); x += NT) {     // the 32 rows' exact Q -> LDS
+        const int r = x / (D / 8), u = x % (D / 8);
+        const int qr = QSEL[(int64_t)bh * NREP + min(rb * 32 + r, NREP - 1)];
+        *reinterpret_cast<uint4*>(&sq[r][u * 8]) =
+            *reinterpret_cast<const uint4*>(Q + ((int64_t)bh * N + qr) * D + u * 8);
+    }
+    __syncthreads();
+    auto q_op = [&](int c16) {                          // B operand: this lane's row
+        return *reinterpret_cast<const bf16x8*>(&sq[r32][rep_channel(c16, hh)]);
+    };
+    const uint8_t* K8bh = K8 + (int64_t)bh * N * D;
+    const __bf16* Kbh = K + (int64_t)bh * N * D;
+    const uint8_t* Vbh = V8T + (int64_t)bh * D * ldv;
+
+    // a tile's K codes (row kb*32 + swap_bits23(r32), 8 channels per k-step) and V^T
+    // codes (row 32 i + r32, keys 16 u + 8 hh ..)
+    // (the k-steps c16 = 2x, 2x + 1 of a lane are 16 consecutive channels: one load)
+    auto load_k = [&](int t, uint2 (&kx)[KB][NK16]) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int key = min(t * BC + kb * 32 + swap_bits23(r32), N - 1);
+#pragma unroll
+            for (int c16 = 0; c16 < NK16; c16 += 2) {
+                const uint4 x = *reinterpret_cast<const uint4*>(K8bh + (int64_t)key * D +
+                                                                rep_channel(c16, hh));
+                kx[kb][c16] = make_uint2(x.x, x.y);
+                kx[kb][c16 + 1] = make_uint2(x.z, x.w);
+            }
+        }
+    };
+    auto load_v = [&](int t, uint2 (&vx)[NOB][4]) {
+#pragma unroll
+        for (int i = 0; i < NOB; ++i) {
+            const uint8_t* vrow = Vbh + (int64_t)(32 * i + r32) * ldv;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k0 = t * BC + 16 * u + 8 * hh;
+                uint2 x = make_uint2(0, 0);
+                if (k0 < N) {
+                    // k0 < N, k0 % 8 == 0 and ldv % 16 == 0 keep the 8 bytes in the row
+                    x = *reinterpret_cast<const uint2*>(vrow + k0);
+                    if (k0 + 8 > N) {
+                        const int keep = N - k0;              // 1..7 bytes
+                        const uint64_t mk = (1ull << (8 * keep)) - 1ull;
+                        const uint64_t v64 = (((uint64_t)x.y << 32) | x.x) & mk;
+                        x = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
+                    }
+                }
+                vx[i][u] = x;
+            }
+        }
+    };
+    uint2 kc[KB][NK16];
+
+    floatx16 oacc[NOB];
+#pragma unroll
+    for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) oacc[ob][a] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const int nkt = (N + BC - 1) / BC;
+    if (w < nkt) load_k(w, kc);
+    for (int t = w; t < nkt; t += NWR) {
+        uint2 vc[NOB][4], kn[KB][NK16];
+        load_v(t, vc);                                // in flight during QK and the softmax
+        if (t + NWR < nkt) load_k(t + NWR, kn);
+        const float ks = KS[(int64_t)bh * nblk + (t * BC) / JA_QK_BLOCK];
+        const float inv_ks = 1.f / ks;                // a power of two: exact
+        floatx16 s[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int key = min(t * BC + kb * 32 + swap_bits23(r32), N - 1);
+            const bool rep = (kmask[key >> 5] >> (key & 31)) & 1u;
+#pragma unroll
+            for (int a = 0; a < 16; ++a) s[kb][a] = 0.f;
+            if (__ballot(rep) == 0) {                 // no listed key in this block
+#pragma unroll
+                for (int c16 = 0; c16 < NK16; ++c16)
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        e4m3x8_to_bf16((int)kc[kb][c16].x, (int)kc[kb][c16].y), q_op(c16), s[kb],
+                        0, 0, 0);
+            } else {
+#pragma unroll
+                for (int c16 = 0; c16 < NK16; ++c16) {
+                    bf16x8 ak = e4m3x8_to_bf16((int)kc[kb][c16].x, (int)kc[kb][c16].y);
+                    if (rep) {
+                        const bf16x8 x = *reinterpret_cast<const bf16x8*>(
+                            Kbh + (int64_t)key * D + rep_channel(c16, hh));
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ak[e] = (__bf16)((float)x[e] * inv_ks);
+                    }
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, q_op(c16), s[kb], 0, 0, 0);
+                }
+            }
+        }
+        const float f = c2 * ks;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int a = 0; a < 16; ++a) {
+                const int key = t * BC + kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8);
+                if (key >= N) s[kb][a] = -INFINITY;
+                mx = fmaxf(mx, s[kb][a]);
+            }
+        const float tmax = mx * f;
+        if (__ballot(tmax > m) != 0) {
+            const float m_new = fmaxf(m, ceilf(wave_halves_max(tmax)));
+            const float alpha = (m == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m - m_new));
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int a = 0; a < 16; ++a) oacc[ob][a] *= alpha;
+        }
+        const float bias = 8.f - m;
+        intx8 pf;
+#pragma unroll
+        for (int k = 0; k < 4 * KB; ++k) {
+            const int kb = k / 4, d = k % 4;
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[kb][4 * d + e], f, bias));
+            l += (p[0] + p[1]) + (p[2] + p[3]);
+            const int wp = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+            pf[k] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wp, true);
+        }
+#pragma unroll
+        for (int i = 0; i < NOB; ++i) {
+            intx8 av;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                av[2 * u] = (int)vc[i][u].x;
+                av[2 * u + 1] = (int)vc[i][u].y;
+            }
+            oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pf, oacc[i], 0, 0, 0, 0,
+                                                                     0, 0);
+        }
+        if (t + NWR < nkt) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int c16 = 0; c16 < NK16; ++c16) kc[kb][c16] = kn[kb][c16];
+        }
+    }
+
+    // merge the waves: rows' maxima, then the rescaled numerators added in wave order
+    const float lw = wave_halves_sum(l);
+    if (hh == 0) {
+        sm[w][r32] = m;
+        sl[w][r32] = lw;
+    }
+    __syncthreads();
+    float mt = sm[0][r32];
+#pragma unroll
+    for (int x = 1; x < NWR; ++x) mt = fmaxf(mt, sm[x][r32]);
+    const float sc = (m == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m - mt));
+    // O^T slot (ob, a): channel ob*32 + 8 (a / 4) + 4 hh + a % 4, row r32
+    for (int x = 0; x < NWR; ++x) {
+        if (w == x) {
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int a = 0; a < 16; ++a)
+                    so[ob * 32 + 8 * (a / 4) + 4 * hh + (a % 4)][r32] += oacc[ob][a] * sc;
+        }
+        __syncthreads();
+    }
+    if (w == 0 && slot < NREP) {
+        float lt = 0.f;
+#pragma unroll
+        for (int x = 0; x < NWR; ++x)
+            lt += sm[x][r32] == -INFINITY ? 0.f : sl[x][r32] * ldexpf(1.f, (int)(sm[x][r32] - mt));
+        const float inv = 1.f / lt;
+        __bf16* orow = O + (((int64_t)b * N + qi) * H + h) * D;
+        const float* vs = VS + (int64_t)bh * D;
+        for (int c = hh; c < D; c += 2) orow[c] = (__bf16)(so[c][r32] * inv * vs[c]);
+        if (hh == 0) LSE[(int64_t)bh * N + qi] = (mt - 8.f + log2f(lt)) * kLn2;
+    }
+}
+
+// RROWS (token repair): workgroups past `total` recompute the listed query rows
+// (repair_rows); the main workgroups leave those rows to them.
+template <int D, int NW, bool HI, bool RROWS = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8T,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     const __bf16* __restrict__ QH, const __bf16* __restrict__ KH,
     int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE,
-    int n_qtiles, int total) {
+    int n_qtiles, int total, const __bf16* __restrict__ QX = nullptr,
+    const __bf16* __restrict__ KX = nullptr, const int32_t* __restrict__ QSEL = nullptr,
+    const int32_t* __restrict__ KSEL = nullptr, int NREP = 0) {
+    static_assert(!(HI && RROWS), "token repair runs on the plain codes");
+    if constexpr (RROWS) {
+        if ((int)blockIdx.x >= total) {
+            const int r = (int)blockIdx.x - total, nb = (NREP + 31) / 32;
+            repair_rows<D, NW>(QX, KX, K8, V8T, KS, VS, QSEL, KSEL, NREP, H, N, ldv, c2, O, LSE,
+                               r % nb, r / nb);
+            return;
+        }
+    }
     constexpr int NTHREADS = NW * 64;
     constexpr int BR = NW * 32;              // query rows per workgroup
     constexpr int BC = 64;                   // keys per tile
@@ -122,6 +360,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     const __bf16* KHbh = HI ? KH + (int64_t)bh * N * HC : nullptr;
     const float* KSbh = KS + (int64_t)bh * nblk;
     const int nkt = (N + BC - 1) / BC;
+    // RROWS: which of this workgroup's rows are listed (left to the row recomputation)
+    __shared__ uint32_t rmask[RROWS ? NW : 1];
+    if constexpr (RROWS) {
+        if (tid < NW) rmask[tid] = 0;
+        __syncthreads();
+        const int r0 = qt * BR;
+        for (int i = tid; i < NREP; i += NTHREADS) {
+            const int r = QSEL[(int64_t)bh * NREP + i] - r0;
+            if (r >= 0 && r < BR) atomicOr(&rmask[r >> 5], 1u << (r & 31));
+        }
+        __syncthreads();
+    }
 
     // ---- staging: chunk x = tid + i * NTHREADS of a tile is K row x / DC, 16-byte
     //      chunk x % DC, and V^T row x / 4, keys 16 (x % 4) ..; threads t < 128 also
@@ -452,7 +702,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
 
     const float l_tot = wave_halves_sum(l);
     const float inv = 1.f / l_tot;
-    if (q_row < N) {
+    const bool listed = RROWS && ((rmask[w] >> r32) & 1u);
+    if (q_row < N && !listed) {
         __bf16* orow = O + (((int64_t)b * N + q_row) * H + h) * D;
         const float* vs = VS + (int64_t)bh * D;
 #pragma unroll
@@ -486,8 +737,9 @@ template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_fp8_keyfix_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const __bf16* __restrict__ K,
     const uint8_t* __restrict__ VSEL, const float* __restrict__ QS, const float* __restrict__ KS,
-    const float* __restrict__ VS, const int32_t* __restrict__ KSEL, int NREP, int ldr, int H,
-    int N, float c2, __bf16* __restrict__ O, float* __restrict__ LSE) {
+    const float* __restrict__ VS, const int32_t* __restrict__ KSEL,
+    const int32_t* __restrict__ QSEL, int NREP, int ldr, int H, int N, float c2,
+    __bf16* __restrict__ O, float* __restrict__ LSE) {
     constexpr int NWF = 4, QPW = 4, BC = 64, GT = 2, KB = BC / 32, NQC = D / 64, NOB = D / 32;
     constexpr int DC = D / 16;
     constexpr int KRPB = 256 / D;                       // code rows per 256-byte bank line
@@ -509,6 +761,17 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_keyfix_kernel(
     auto kz = [&](int row) { return (row / KRPB) % DC; };
     auto xunit = [&](int row, int u) { return u ^ ((row / XRPL) % XU); };
     auto slot_of = [&](int kb, int a) { return kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8); };
+
+    // listed query rows of this workgroup's 512: recomputed with exact values already
+    constexpr int WGR = NWF * QPW * 32;
+    __shared__ uint32_t rmask[WGR / 32];
+    if (tid < WGR / 32) rmask[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < NREP; i += 256) {
+        const int r = QSEL[(int64_t)bh * NREP + i] - (int)blockIdx.x * WGR;
+        if (r >= 0 && r < WGR) atomicOr(&rmask[r >> 5], 1u << (r & 31));
+    }
+    __syncthreads();
 
     const int ngroups = (NREP + GT * BC - 1) / (GT * BC);
     auto stage = [&](int g) {                           // listed keys g*128 .. -> LDS
@@ -674,7 +937,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_keyfix_kernel(
         }
 
         const float dlt = wave_halves_sum(dl);
-        if (q_row < N) {
+        const int wr = q_row - (int)blockIdx.x * WGR;          // 0 <= wr < WGR
+        if (q_row < N && !((rmask[wr >> 5] >> (wr & 31)) & 1u)) {
             const float u = exp2f(mr - 8.f - lam);
             const float den = 1.f + u * dlt;
             const float inv = 1.f / den;
@@ -693,227 +957,6 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_keyfix_kernel(
                 }
             if (hh == 0) *lp = (lam + log2f(den)) * kLn2;
         }
-    }
-}
-
-// Token repair, the listed query rows: grid (ceil(n / 32), B*H), 8 waves.  The 32 rows
-// of a workgroup (lane r32 <-> row QSEL[32 blockIdx.x + r32]) take their exact bf16 Q
-// values; keys are the codes widened to bf16 (exact), or for listed keys their exact
-// values divided by the block scale (exact: a power of two), so that one factor
-// c2 * k_scale per tile again turns products into base-2 logits.  Wave w visits tiles
-// w, w + 8, .., with the next tile's K and V^T codes loaded into registers while the
-// current one is computed; P (e4m3, integer running maximum as in the main kernel)
-// times V^T codes runs on the fp8 matrix cores.  The waves' states (all maxima are
-// integers, so every rescale is a power of two) are merged through LDS in wave order.
-template <int D>
-__global__ __launch_bounds__(512) void fwd_fp8_rows_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const uint8_t* __restrict__ K8,
-    const uint8_t* __restrict__ V8T, const float* __restrict__ KS, const float* __restrict__ VS,
-    const int32_t* __restrict__ QSEL, const int32_t* __restrict__ KSEL, int NREP, int H, int N,
-    int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE) {
-    constexpr int NWR = 8, NT = NWR * 64, BC = 64, KB = BC / 32, NOB = D / 32, NK16 = D / 16;
-    __shared__ uint32_t kmask[JA_REPAIR_MAX_N / 32];
-    __shared__ float sm[NWR][32], sl[NWR][32];
-    __shared__ float so[D][33];                        // [channel][row], padded
-    __shared__ __attribute__((aligned(16))) __bf16 sq[32][D + 8];   // exact Q rows, padded
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r32 = lane & 31, hh = lane >> 5;
-    const int bh = blockIdx.y, b = bh / H, h = bh - b * H;
-    const int nblk = (N + JA_QK_BLOCK - 1) / JA_QK_BLOCK;
-
-    // listed keys as a bitmask; the merge buffer starts at zero
-    const int nwords = (N + 31) / 32;
-    for (int i = tid; i < nwords; i += NT) kmask[i] = 0;
-    for (int i = tid; i < D * 33; i += NT) (&so[0][0])[i] = 0.f;
-    __syncthreads();
-    for (int i = tid; i < NREP; i += NT) {
-        const int key = KSEL[(int64_t)bh * NREP + i];
-        atomicOr(&kmask[key >> 5], 1u << (key & 31));
-    }
-    __syncthreads();
-
-    const int slot = blockIdx.x * 32 + r32;
-    const int qi = QSEL[(int64_t)bh * NREP + min(slot, NREP - 1)];
-    for (int x = tid; x < 32 * (D / 8); x += NT) {     // the 32 rows' exact Q -> LDS
-        const int r = x / (D / 8), u = x % (D / 8);
-        const int qr = QSEL[(int64_t)bh * NREP + min((int)blockIdx.x * 32 + r, NREP - 1)];
-        *reinterpret_cast<uint4*>(&sq[r][u * 8]) =
-            *reinterpret_cast<const uint4*>(Q + ((int64_t)bh * N + qr) * D + u * 8);
-    }
-    __syncthreads();
-    auto q_op = [&](int c16) {                          // B operand: this lane's row
-        return *reinterpret_cast<const bf16x8*>(&sq[r32][rep_channel(c16, hh)]);
-    };
-    const uint8_t* K8bh = K8 + (int64_t)bh * N * D;
-    const __bf16* Kbh = K + (int64_t)bh * N * D;
-    const uint8_t* Vbh = V8T + (int64_t)bh * D * ldv;
-
-    // a tile's K codes (row kb*32 + swap_bits23(r32), 8 channels per k-step) and V^T
-    // codes (row 32 i + r32, keys 16 u + 8 hh ..)
-    // (the k-steps c16 = 2x, 2x + 1 of a lane are 16 consecutive channels: one load)
-    auto load_k = [&](int t, uint2 (&kx)[KB][NK16]) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int key = min(t * BC + kb * 32 + swap_bits23(r32), N - 1);
-#pragma unroll
-            for (int c16 = 0; c16 < NK16; c16 += 2) {
-                const uint4 x = *reinterpret_cast<const uint4*>(K8bh + (int64_t)key * D +
-                                                                rep_channel(c16, hh));
-                kx[kb][c16] = make_uint2(x.x, x.y);
-                kx[kb][c16 + 1] = make_uint2(x.z, x.w);
-            }
-        }
-    };
-    auto load_v = [&](int t, uint2 (&vx)[NOB][4]) {
-#pragma unroll
-        for (int i = 0; i < NOB; ++i) {
-            const uint8_t* vrow = Vbh + (int64_t)(32 * i + r32) * ldv;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int k0 = t * BC + 16 * u + 8 * hh;
-                uint2 x = make_uint2(0, 0);
-                if (k0 < N) {
-                    // k0 < N, k0 % 8 == 0 and ldv % 16 == 0 keep the 8 bytes in the row
-                    x = *reinterpret_cast<const uint2*>(vrow + k0);
-                    if (k0 + 8 > N) {
-                        const int keep = N - k0;              // 1..7 bytes
-                        const uint64_t mk = (1ull << (8 * keep)) - 1ull;
-                        const uint64_t v64 = (((uint64_t)x.y << 32) | x.x) & mk;
-                        x = make_uint2((uint32_t)v64, (uint32_t)(v64 >> 32));
-                    }
-                }
-                vx[i][u] = x;
-            }
-        }
-    };
-    uint2 kc[KB][NK16];
-
-    floatx16 oacc[NOB];
-#pragma unroll
-    for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) oacc[ob][a] = 0.f;
-    float m = -INFINITY, l = 0.f;
-    const int nkt = (N + BC - 1) / BC;
-    if (w < nkt) load_k(w, kc);
-    for (int t = w; t < nkt; t += NWR) {
-        uint2 vc[NOB][4], kn[KB][NK16];
-        load_v(t, vc);                                // in flight during QK and the softmax
-        if (t + NWR < nkt) load_k(t + NWR, kn);
-        const float ks = KS[(int64_t)bh * nblk + (t * BC) / JA_QK_BLOCK];
-        const float inv_ks = 1.f / ks;                // a power of two: exact
-        floatx16 s[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int key = min(t * BC + kb * 32 + swap_bits23(r32), N - 1);
-            const bool rep = (kmask[key >> 5] >> (key & 31)) & 1u;
-#pragma unroll
-            for (int a = 0; a < 16; ++a) s[kb][a] = 0.f;
-            if (__ballot(rep) == 0) {                 // no listed key in this block
-#pragma unroll
-                for (int c16 = 0; c16 < NK16; ++c16)
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        e4m3x8_to_bf16((int)kc[kb][c16].x, (int)kc[kb][c16].y), q_op(c16), s[kb],
-                        0, 0, 0);
-            } else {
-#pragma unroll
-                for (int c16 = 0; c16 < NK16; ++c16) {
-                    bf16x8 ak = e4m3x8_to_bf16((int)kc[kb][c16].x, (int)kc[kb][c16].y);
-                    if (rep) {
-                        const bf16x8 x = *reinterpret_cast<const bf16x8*>(
-                            Kbh + (int64_t)key * D + rep_channel(c16, hh));
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) ak[e] = (__bf16)((float)x[e] * inv_ks);
-                    }
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, q_op(c16), s[kb], 0, 0, 0);
-                }
-            }
-        }
-        const float f = c2 * ks;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int a = 0; a < 16; ++a) {
-                const int key = t * BC + kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8);
-                if (key >= N) s[kb][a] = -INFINITY;
-                mx = fmaxf(mx, s[kb][a]);
-            }
-        const float tmax = mx * f;
-        if (__ballot(tmax > m) != 0) {
-            const float m_new = fmaxf(m, ceilf(wave_halves_max(tmax)));
-            const float alpha = (m == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m - m_new));
-            m = m_new;
-            l *= alpha;
-#pragma unroll
-            for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-                for (int a = 0; a < 16; ++a) oacc[ob][a] *= alpha;
-        }
-        const float bias = 8.f - m;
-        intx8 pf;
-#pragma unroll
-        for (int k = 0; k < 4 * KB; ++k) {
-            const int kb = k / 4, d = k % 4;
-            float p[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[kb][4 * d + e], f, bias));
-            l += (p[0] + p[1]) + (p[2] + p[3]);
-            const int wp = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-            pf[k] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wp, true);
-        }
-#pragma unroll
-        for (int i = 0; i < NOB; ++i) {
-            intx8 av;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                av[2 * u] = (int)vc[i][u].x;
-                av[2 * u + 1] = (int)vc[i][u].y;
-            }
-            oacc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, pf, oacc[i], 0, 0, 0, 0,
-                                                                     0, 0);
-        }
-        if (t + NWR < nkt) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int c16 = 0; c16 < NK16; ++c16) kc[kb][c16] = kn[kb][c16];
-        }
-    }
-
-    // merge the waves: rows' maxima, then the rescaled numerators added in wave order
-    const float lw = wave_halves_sum(l);
-    if (hh == 0) {
-        sm[w][r32] = m;
-        sl[w][r32] = lw;
-    }
-    __syncthreads();
-    float mt = sm[0][r32];
-#pragma unroll
-    for (int x = 1; x < NWR; ++x) mt = fmaxf(mt, sm[x][r32]);
-    const float sc = (m == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m - mt));
-    // O^T slot (ob, a): channel ob*32 + 8 (a / 4) + 4 hh + a % 4, row r32
-    for (int x = 0; x < NWR; ++x) {
-        if (w == x) {
-#pragma unroll
-            for (int ob = 0; ob < NOB; ++ob)
-#pragma unroll
-                for (int a = 0; a < 16; ++a)
-                    so[ob * 32 + 8 * (a / 4) + 4 * hh + (a % 4)][r32] += oacc[ob][a] * sc;
-        }
-        __syncthreads();
-    }
-    if (w == 0 && slot < NREP) {
-        float lt = 0.f;
-#pragma unroll
-        for (int x = 0; x < NWR; ++x)
-            lt += sm[x][r32] == -INFINITY ? 0.f : sl[x][r32] * ldexpf(1.f, (int)(sm[x][r32] - mt));
-        const float inv = 1.f / lt;
-        __bf16* orow = O + (((int64_t)b * N + qi) * H + h) * D;
-        const float* vs = VS + (int64_t)bh * D;
-        for (int c = hh; c < D; c += 2) orow[c] = (__bf16)(so[c][r32] * inv * vs[c]);
-        if (hh == 0) LSE[(int64_t)bh * N + qi] = (mt - 8.f + log2f(lt)) * kLn2;
     }
 }
 
@@ -940,20 +983,31 @@ hipError_t launch_repair_d(const void* q8, const void* k8, const void* v8t, cons
                            const int32_t* q_sel, const int32_t* k_sel, const void* v8t_sel,
                            int n_repair, int B, int H, int N, int64_t ldv, float softmax_scale,
                            void* o, float* lse, hipStream_t stream) {
-    const hipError_t e0 = launch_d<D, false>(q8, k8, v8t, qs, ks, vs, nullptr, nullptr, B, H, N,
-                                             ldv, softmax_scale, o, lse, stream);
-    if (e0 != hipSuccess || n_repair == 0) return e0;
+    if (n_repair == 0)
+        return launch_d<D, false>(q8, k8, v8t, qs, ks, vs, nullptr, nullptr, B, H, N, ldv,
+                                  softmax_scale, o, lse, stream);
+    constexpr int NW = D == 128 ? FP8_NW128 : 4;
+    constexpr int BR = NW * 32;
+    const int n_qtiles = (N + BR - 1) / BR;
+    const int total = n_qtiles * B * H;
+    const int row_wgs = (n_repair + 31) / 32 * B * H;
     const float c2 = softmax_scale * kLog2e;
+    // the main grid, then the listed rows' workgroups (dispatched last: they fill the
+    // CUs the main grid's last round leaves idle); then the listed keys in every other row
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, false, true>), dim3(total + row_wgs), dim3(NW * 64),
+                       0, stream, static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
+                       static_cast<const uint8_t*>(v8t), qs, ks, vs, nullptr, nullptr, H, N, ldv, c2,
+                       static_cast<__bf16*>(o), lse, n_qtiles, total,
+                       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), q_sel, k_sel,
+                       n_repair);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int ldr = (n_repair + 63) / 64 * 64;
-    // the listed keys in every row, then the listed rows again: in that order on `stream`
     hipLaunchKernelGGL(fwd_fp8_keyfix_kernel<D>, dim3((N + 511) / 512, B * H), dim3(256), 0,
                        stream, static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
                        static_cast<const __bf16*>(k), static_cast<const uint8_t*>(v8t_sel), qs,
-                       ks, vs, k_sel, n_repair, ldr, H, N, c2, static_cast<__bf16*>(o), lse);
-    hipLaunchKernelGGL(fwd_fp8_rows_kernel<D>, dim3((n_repair + 31) / 32, B * H), dim3(512), 0,
-                       stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
-                       static_cast<const uint8_t*>(k8), static_cast<const uint8_t*>(v8t), ks, vs,
-                       q_sel, k_sel, n_repair, H, N, ldv, c2, static_cast<__bf16*>(o), lse);
+                       ks, vs, k_sel, q_sel, n_repair, ldr, H, N, c2, static_cast<__bf16*>(o),
+                       lse);
     return hipGetLastError();
 }
 
