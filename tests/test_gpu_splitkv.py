@@ -79,3 +79,19 @@ def test_splitkv_deterministic():
     a = _run(w, 5, sel=oracle.all_rows(1, 4, 1))[4].clone()
     b = _run(w, 5, sel=oracle.all_rows(1, 4, 1))[4]
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,H,lens,n_split", [(1, 3, (100, 300), 1), (2, 128, (256,), 4)])
+def test_splitkv_without_a_tail_is_the_plain_forward(B, H, lens, n_split):
+    # n_split = 1, or a grid of whole rounds (2 x 128 heads x one 256-row tile = 256
+    # workgroups on 256 CUs): the plain forward runs, bit for bit
+    import joint_attention_amd as ja
+    import torch
+    w = synth.custom("skvp", B=B, H=H, D=128, stream_lens=lens, outliers=4, seed=17)
+    q, k, vt, _ = device_packed(host_streams(w))
+    a = ja.joint_attn_fwd_bf16(q, k, vt)
+    b = ja.joint_attn_fwd_bf16_splitkv(q, k, vt, n_split=n_split)
+    torch.cuda.synchronize()
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256 and n_split > 1:
+        pytest.skip("the whole-rounds case assumes 256 CUs")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
