@@ -11,7 +11,8 @@
 //
 // Variants of the same kernel: GATHER reads Q, K and V in place from the per-stream
 // tensors (no pack step); SPARSE visits only the key blocks that an input block mask
-// allows.
+// allows; PARTIAL splits the keys of the last round's query tiles into ranges whose
+// partial results splitkv_merge_kernel combines (split-KV).
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, wave64).  The wave computes the
 // transposed scores S^T = K Q^T: operand A = 32 keys (from LDS), operand B = the
