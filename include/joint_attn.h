@@ -147,9 +147,9 @@ int joint_attn_fwd_bf16_sparse(const void *q, const void *k, const void *vt,
  *                    joint_attn_fwd_bf16_splitkv_suggest() gives one from a model of
  *                    the rounds saved against the partial results' cost (1 = none)
  *   workspace        device scratch owned by the caller, 16-byte aligned, at least
- *                    joint_attn_fwd_bf16_splitkv_workspace() bytes (fp32 partial outputs
- *                    and log-sum-exps; an upper bound that assumes every tile split);
- *                    its contents on entry do not matter
+ *                    joint_attn_fwd_bf16_splitkv_workspace() bytes, asked on the device
+ *                    the call runs on (fp32 partial outputs and log-sum-exps of at most
+ *                    one round of split tiles); its contents on entry do not matter
  * Results are deterministic but, in the split tiles, not bit-identical to
  * joint_attn_fwd_bf16 (the sums are split differently).  Calls that share a workspace
  * must not overlap.

@@ -2,6 +2,7 @@
 // Declarations and the contract of every call are in include/joint_attn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -153,10 +154,12 @@ int joint_attn_fwd_bf16_sparse(const void* q, const void* k, const void* vt, int
 
 int64_t joint_attn_fwd_bf16_splitkv_workspace(int B, int H, int64_t N, int D, int n_split) {
     if (B <= 0 || H <= 0 || N < 0 || D <= 0 || n_split <= 0 || !head_size_ok(D)) return -1;
-    // an upper bound: every query tile split (only the last round's are)
+    // only the query tiles of the last, partial round are split: fewer than the slots
+    // (workgroups running at once on the current device) and than all tiles
     const int64_t br = ja::splitkv_rows_per_tile(D);
     const int64_t units = (N + br - 1) / br * B * H;
-    return (int64_t)n_split * units * br * (D + 1) * (int64_t)sizeof(float);
+    const int64_t split_tiles = std::min<int64_t>(units, ja::splitkv_slots(D));
+    return (int64_t)n_split * split_tiles * br * (D + 1) * (int64_t)sizeof(float);
 }
 
 int joint_attn_fwd_bf16_splitkv_suggest(int B, int H, int64_t N, int D) {
@@ -206,8 +209,10 @@ int joint_attn_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, in
         return JA_EUNSUPPORTED;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
     const int64_t br = ja::splitkv_rows_per_tile(D);
+    const int64_t split_tiles =
+        std::min<int64_t>((N + br - 1) / br * B * H, ja::splitkv_slots(D));
     float* o_part = static_cast<float*>(workspace);
-    float* lse_part = o_part + (int64_t)n_split * ((N + br - 1) / br * B * H) * br * D;
+    float* lse_part = o_part + (int64_t)n_split * split_tiles * br * D;
     return hip_status(ja::launch_fwd_bf16_splitkv(q, k, vt, B, H, (int)N, D, ldv, softmax_scale,
                                                   n_split, o_part, lse_part, o, lse,
                                                   static_cast<hipStream_t>(stream)));

@@ -167,7 +167,9 @@ def test_sparse_validation(lib):
 def test_splitkv_sizes_and_validation(lib):
     fake = 0x10000
     ws = lib.joint_attn_fwd_bf16_splitkv_workspace
-    assert ws(2, 24, 4608, 128, 2) == 2 * 2 * 24 * 4608 * 129 * 4      # 18 whole 256-row tiles
+    # at most one round of split tiles: min(tiles, 256 slots) -- 256 without a GPU
+    assert ws(2, 24, 4608, 128, 2) == 2 * 256 * 256 * 129 * 4          # 864 tiles
+    assert ws(1, 2, 4608, 128, 2) == 2 * 36 * 256 * 129 * 4            # 36 tiles
     assert ws(1, 1, 40, 128, 3) == 3 * 256 * 129 * 4                  # one padded tile
     assert ws(1, 1, 40, 64, 3) == 3 * 128 * 65 * 4                   # 128-row tiles at D = 64
     assert ws(0, 24, 4608, 128, 2) == -1 and ws(1, 1, 16, 64, 0) == -1
