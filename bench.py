@@ -14,9 +14,10 @@ the plain joint_attn_fwd_bf16 is reported under "plain_bf16".
 The same attention through joint_attn_fwd_bf16_streams (streams read in place, no pack)
 is timed in its own loop and reported under "fused_bf16"; the block-sparse forward with a
 structured block mask under "sparse_bf16".
-The fp8 path (pack x3 -> joint_attn_quant_fp8 -> joint_attn_fwd_fp8) on the same
-inputs is timed the same way in its own loop and reported under "fp8", for both modes,
-from the streams, and with token repair (rho = 0.005).
+The fp8 path (pack x3 -> joint_attn_quant_fp8 -> joint_attn_fwd_fp8_splitkv, the plain
+joint_attn_fwd_fp8 timed beside it) on the same inputs is timed the same way in its own
+loop and reported under "fp8", for both modes, from the streams, and with token repair
+(rho = 0.005).
 value = algorithmic attention flops (4 B H N^2 D) per bf16 step / step time.
 
 Under "shapes", the forward alone is timed on the other shapes: 1024^2 T2I, 2048^2 I2I and
@@ -295,8 +296,13 @@ def main():
         out["fp8"] = {}
         for mode, name in ((ja.JA_FP8_SPLIT, "split"), (ja.JA_FP8_PLAIN, "plain")):
             t8 = ja.joint_attn_quant_fp8(q, k, vt, mode)
+            # the forward through the split-KV call (last round's tiles split), workspace
+            # allocated outside the timing
+            ns8 = int(ja.load().joint_attn_fwd_fp8_splitkv_suggest(B, H, N, D, mode))
+            ws8 = torch.empty((int(ja.load().joint_attn_fwd_fp8_splitkv_workspace(
+                B, H, N, D, ns8)),), dtype=torch.uint8, device="cuda")
 
-            def step_fp8(rec, mode=mode, t8=t8):
+            def step_fp8(rec, mode=mode, t8=t8, ns8=ns8, ws8=ws8):
                 e = [ev() for _ in range(4)] if rec else None
                 if rec:
                     e[0].record(stream)
@@ -308,29 +314,44 @@ def main():
                 ja.joint_attn_quant_fp8(q, k, vt, mode, out=t8)
                 if rec:
                     e[2].record(stream)
-                ja.joint_attn_fwd_fp8(t8, scale, out=o)
+                ja.joint_attn_fwd_fp8_splitkv(t8, scale, n_split=ns8, workspace=ws8, out=o)
                 if rec:
                     e[3].record(stream)
                 return e
 
-            log("timing fp8 path, mode %d (%s)" % (mode, name))
+            log("timing fp8 path, mode %d (%s), split-KV n_split %d" % (mode, name, ns8))
             wall8, durs8 = timed(step_fp8, args.steps, args.warmup)
             ms8 = wall8 * 1e3 / args.steps
             p8, qn8, f8 = durs8.mean(axis=0)
+
+            # the plain fp8 forward alone (every query tile over all keys)
+            def step_f8p(rec, t8=t8):
+                e = [ev() for _ in range(2)] if rec else None
+                if rec:
+                    e[0].record(stream)
+                ja.joint_attn_fwd_fp8(t8, scale, out=o)
+                if rec:
+                    e[1].record(stream)
+                return e
+
+            _, durs8p = timed(step_f8p, args.steps, args.warmup)
+            f8p = float(durs8p.mean())
             out["fp8"][name] = {
                 "workload": "t2i_2048_fp8 (same inputs)", "mode": mode,
                 "dtype": "fp8 e4m3" + (" + bf16 outlier channels" if mode else "")
                          + " (fp32 accumulate)",
                 "value": round(flops / (ms8 * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                 "ms_per_step": round(ms8, 4),
-                "step": "pack q,k,v + quant_fp8 + fwd_fp8",
+                "step": "pack q,k,v + quant_fp8 + fwd_fp8_splitkv (n_split %d)" % ns8,
                 "kernels_ms": {"pack_qkv": round(float(p8), 4), "quant_fp8": round(float(qn8), 4),
-                               "fwd_fp8": round(float(f8), 4)},
+                               "fwd_fp8_splitkv": round(float(f8), 4)},
                 "fwd_fp8_tflops": round(flops / (f8 * 1e-3) / 1e12, 2),
                 "frac_of_fp8_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
                 "frac_of_bf16_peak": round(flops / (f8 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "plain_fwd_fp8_ms": round(f8p, 4),
+                "plain_fwd_fp8_tflops": round(flops / (f8p * 1e-3) / 1e12, 2),
             }
-            del t8
+            del t8, ws8
 
             # the same fp8 step with the quantiser reading the streams in place (no pack)
             t8s, _ = ja.joint_attn_quant_fp8_streams(qs_d, ks_d, vs_d, mode)

@@ -270,6 +270,31 @@ int joint_attn_fwd_fp8(const void *q8, const void *k8, const void *v8t,
                        void *o, float *lse, void *stream);
 
 /*
+ * joint_attn_fwd_fp8_splitkv -- joint_attn_fwd_fp8 (either mode) with the query tiles of
+ * the last, partial round of workgroups split into n_split ranges of 64-key tiles, merged
+ * with the log-sum-exp rule, as joint_attn_fwd_bf16_splitkv does for the bf16 forward
+ * (same motivation: 2048x2048 T2I has 3168 workgroups for 256 CUs).  Same operation,
+ * layouts and arguments as joint_attn_fwd_fp8, plus:
+ *   n_split          1 .. 64 (clamped to the number of 64-key tiles; 1, or a grid of
+ *                    whole rounds, is the plain forward);
+ *                    joint_attn_fwd_fp8_splitkv_suggest() gives one for the mode
+ *   workspace        device scratch owned by the caller, 16-byte aligned, at least
+ *                    joint_attn_fwd_fp8_splitkv_workspace() bytes, asked on the device
+ *                    the call runs on; its contents on entry do not matter
+ * The split tiles' partial outputs carry the V scale; results are deterministic, not
+ * bit-identical to joint_attn_fwd_fp8 in the split tiles.  Calls that share a workspace
+ * must not overlap.
+ */
+int64_t joint_attn_fwd_fp8_splitkv_workspace(int B, int H, int64_t N, int D, int n_split);
+int joint_attn_fwd_fp8_splitkv_suggest(int B, int H, int64_t N, int D, int mode);
+int joint_attn_fwd_fp8_splitkv(const void *q8, const void *k8, const void *v8t,
+                               const float *q_scale, const float *k_scale, const float *v_scale,
+                               int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
+                               int mode, const void *q_hi, const void *k_hi, int n_split,
+                               void *workspace, int64_t workspace_bytes,
+                               void *o, float *lse, void *stream);
+
+/*
  * Token repair of fp8 attention: the repair budget rho of VC-Attention FP8 (VisualGen
  * FLUX 3 article, everytik.com translation, section 量化注意力与稀疏注意力: the share
  * rho of tokens with the highest quantisation error gets a residual correction).  Per

@@ -8,7 +8,8 @@ from ._abi import (JointAttnError, Fp8Tensors, load, joint_attn_vt_ld, joint_att
                    joint_attn_fwd_bf16, joint_attn_fwd_bf16_sparse, joint_attn_fwd_bf16_splitkv,
                    joint_attn_fwd_bf16_streams,
                    joint_attn_quant_fp8,
-                   joint_attn_quant_fp8_streams, joint_attn_fwd_fp8, joint_attn_repair_count,
+                   joint_attn_quant_fp8_streams, joint_attn_fwd_fp8, joint_attn_fwd_fp8_splitkv,
+                   joint_attn_repair_count,
                    joint_attn_quant_fp8_repair, joint_attn_fwd_fp8_repair, EXPORTS, LIB_PATH,
                    JA_QK_BLOCK, JA_HI_CHANNELS, JA_FP8_PLAIN, JA_FP8_SPLIT, JA_FP8_REPAIR,
                    JA_SPARSE_BLOCK, JA_SPARSE_MAX_N, JA_REPAIR_MAX_N)
@@ -17,7 +18,8 @@ __all__ = ["JointAttnError", "Fp8Tensors", "load", "joint_attn_vt_ld", "joint_at
            "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse", "joint_attn_fwd_bf16_splitkv",
            "joint_attn_fwd_bf16_streams",
            "joint_attn_quant_fp8",
-           "joint_attn_quant_fp8_streams", "joint_attn_fwd_fp8", "joint_attn_repair_count",
+           "joint_attn_quant_fp8_streams", "joint_attn_fwd_fp8", "joint_attn_fwd_fp8_splitkv",
+           "joint_attn_repair_count",
            "joint_attn_quant_fp8_repair", "joint_attn_fwd_fp8_repair", "JA_FP8_REPAIR",
            "JA_REPAIR_MAX_N",
            "EXPORTS", "LIB_PATH", "JA_QK_BLOCK", "JA_HI_CHANNELS", "JA_FP8_PLAIN",

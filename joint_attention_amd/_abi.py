@@ -32,7 +32,9 @@ EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld
            "joint_attn_fwd_bf16_splitkv_suggest",
            "joint_attn_fwd_bf16_streams",
            "joint_attn_quant_fp8", "joint_attn_quant_fp8_streams",
-           "joint_attn_fwd_fp8", "joint_attn_repair_count", "joint_attn_quant_fp8_repair",
+           "joint_attn_fwd_fp8", "joint_attn_fwd_fp8_splitkv", "joint_attn_fwd_fp8_splitkv_workspace",
+           "joint_attn_fwd_fp8_splitkv_suggest", "joint_attn_repair_count",
+           "joint_attn_quant_fp8_repair",
            "joint_attn_fwd_fp8_repair")
 
 _lock = threading.Lock()
@@ -90,6 +92,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_fwd_fp8.restype = I
         h.joint_attn_fwd_fp8.argtypes = [P, P, P, P, P, P, I, I, I64, I, I64, F, I, P, P, P, P,
                                          P]
+        h.joint_attn_fwd_fp8_splitkv_workspace.restype = I64
+        h.joint_attn_fwd_fp8_splitkv_workspace.argtypes = [I, I, I64, I, I]
+        h.joint_attn_fwd_fp8_splitkv_suggest.restype = I
+        h.joint_attn_fwd_fp8_splitkv_suggest.argtypes = [I, I, I64, I, I]
+        h.joint_attn_fwd_fp8_splitkv.restype = I
+        h.joint_attn_fwd_fp8_splitkv.argtypes = [P, P, P, P, P, P, I, I, I64, I, I64, F, I, P, P, I,
+                                                 P, I64, P, P, P]
         h.joint_attn_repair_count.restype = I64
         h.joint_attn_repair_count.argtypes = [I64, ctypes.c_double]
         h.joint_attn_quant_fp8_repair.restype = I
@@ -389,6 +398,41 @@ def _alloc_fp8(mode, B, H, N, D, ldv, nblk, dev) -> Fp8Tensors:
         out.hi_idx = torch.empty((B, H, JA_HI_CHANNELS), dtype=torch.int32, device=dev)
         out.ch_amax = torch.empty((B, H, 2, D), dtype=torch.float32, device=dev)
     return out
+
+
+def joint_attn_fwd_fp8_splitkv(t: Fp8Tensors, softmax_scale: float | None = None,
+                               n_split: int | None = None, workspace=None, out=None,
+                               return_lse: bool = False):
+    """joint_attn_fwd_fp8 (modes 0 and 1) with the last round's query tiles split into
+    key ranges.  n_split defaults to the library's suggestion; workspace (a device tensor
+    of at least the required bytes) is allocated here if not given."""
+    torch = _torch()
+    if t.mode not in (JA_FP8_PLAIN, JA_FP8_SPLIT):
+        raise ValueError("joint_attn_fwd_fp8_splitkv: modes 0 and 1 only")
+    for x, n in ((t.q8, "q8"), (t.k8, "k8"), (t.v8t, "v8t")):
+        _need(x, torch.uint8, n, 4)
+    B, H, N, D = t.q8.shape
+    ldv = int(t.v8t.shape[3])
+    lib = load()
+    if n_split is None:
+        n_split = lib.joint_attn_fwd_fp8_splitkv_suggest(B, H, N, D, int(t.mode))
+    need = int(lib.joint_attn_fwd_fp8_splitkv_workspace(B, H, N, D, int(n_split)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=t.q8.device)
+    if workspace.device != t.q8.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=t.q8.device)
+    _need(out, torch.bfloat16, "out", 4)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=t.q8.device) if return_lse else None
+    st = lib.joint_attn_fwd_fp8_splitkv(
+        t.q8.data_ptr(), t.k8.data_ptr(), t.v8t.data_ptr(), t.q_scale.data_ptr(),
+        t.k_scale.data_ptr(), t.v_scale.data_ptr(), B, H, N, D, ldv, scale, int(t.mode),
+        _ptr(t.q_hi), _ptr(t.k_hi), int(n_split), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), out.data_ptr(), _ptr(lse), _stream(t.q8))
+    _check("joint_attn_fwd_fp8_splitkv", st)
+    return (out, lse) if return_lse else out
 
 
 def joint_attn_repair_count(N: int, rho: float) -> int:

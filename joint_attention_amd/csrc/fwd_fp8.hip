@@ -45,6 +45,7 @@
 
 #include "ja_device.h"
 #include "ja_launch.h"
+#include "splitkv_merge.h"
 
 namespace ja {
 namespace {
@@ -307,7 +308,10 @@ __device__ __forceinline__ void repair_rows(
 
 // RROWS (token repair): workgroups past `total` recompute the listed query rows
 // (repair_rows); the main workgroups leave those rows to them.
-template <int D, int NW, bool HI, bool RROWS = false>
+// PARTIAL (split-KV): the query tiles from n_full on (the last, partial round of
+// workgroups) run as n_split key ranges of whole tiles, each writing its normalised fp32
+// output (V scale applied) and natural-log lse for splitkv_merge_kernel.
+template <int D, int NW, bool HI, bool RROWS = false, bool PARTIAL = false>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8T,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
@@ -315,8 +319,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     int H, int N, int64_t ldv, float c2, __bf16* __restrict__ O, float* __restrict__ LSE,
     int n_qtiles, int total, const __bf16* __restrict__ QX = nullptr,
     const __bf16* __restrict__ KX = nullptr, const int32_t* __restrict__ QSEL = nullptr,
-    const int32_t* __restrict__ KSEL = nullptr, int NREP = 0) {
+    const int32_t* __restrict__ KSEL = nullptr, int NREP = 0, int n_split = 1,
+    float* __restrict__ OP = nullptr, float* __restrict__ LP = nullptr, int n_full = 0) {
     static_assert(!(HI && RROWS), "token repair runs on the plain codes");
+    static_assert(!(RROWS && PARTIAL), "one variant at a time");
     if constexpr (RROWS) {
         if ((int)blockIdx.x >= total) {
             const int r = (int)blockIdx.x - total, nb = (NREP + 31) / 32;
@@ -350,8 +356,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r32 = lane & 31, hh = lane >> 5;
-    const int wg = xcd_remap(blockIdx.x, total);
-    const int bh = wg / n_qtiles, qt = wg - bh * n_qtiles;
+    // PARTIAL: the whole-round workgroups and the split ones are renumbered separately, so
+    // that both spread evenly over the XCDs (n_full is a multiple of the slot count)
+    const int bid = blockIdx.x;
+    const int wg = !PARTIAL ? xcd_remap(bid, total)
+                   : bid < n_full ? xcd_remap(bid, n_full)
+                                  : n_full + xcd_remap(bid - n_full, total - n_full);
+    int unit = wg, split = 0;
+    bool part_wg = false;
+    if constexpr (PARTIAL) {
+        if (wg >= n_full) {
+            const int x = wg - n_full;
+            unit = n_full + x / n_split;
+            split = x - (x / n_split) * n_split;
+            part_wg = true;
+        }
+    }
+    const int bh = unit / n_qtiles, qt = unit - bh * n_qtiles;
     const int b = bh / H, h = bh - b * H;
     const int nblk = (N + JA_QK_BLOCK - 1) / JA_QK_BLOCK;
     const uint8_t* Qbh = Q8 + (int64_t)bh * N * D;
@@ -359,7 +380,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     const uint8_t* Vbh = V8T + (int64_t)bh * D * ldv;
     const __bf16* KHbh = HI ? KH + (int64_t)bh * N * HC : nullptr;
     const float* KSbh = KS + (int64_t)bh * nblk;
-    const int nkt = (N + BC - 1) / BC;
+    int nkt = (N + BC - 1) / BC;
+    int t_begin = 0;                               // PARTIAL: first key tile of the range
+    if (PARTIAL && part_wg) {
+        // n_split <= the number of key tiles (the launcher clamps it): no range is empty
+        const int all = nkt;
+        t_begin = (int)((int64_t)split * all / n_split);
+        nkt = (int)((int64_t)(split + 1) * all / n_split) - t_begin;
+    }
     // RROWS: which of this workgroup's rows are listed (left to the row recomputation)
     __shared__ uint32_t rmask[RROWS ? NW : 1];
     if constexpr (RROWS) {
@@ -378,7 +406,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     //      own half a kept-channel row
     uint4 kst[KCH], vst[VCH], hst = make_uint4(0, 0, 0, 0);
     auto load_k = [&](int kt) {
-        const int k0 = kt * BC;
+        const int k0 = (t_begin + kt) * BC;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             const int x = tid + i * NTHREADS, kr = x / DC, kc = x % DC;
@@ -396,7 +424,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int x = tid + i * NTHREADS, vr = x / (BC / 16), vj = x % (BC / 16);
-            const int key = kt * BC + 16 * vj;
+            const int key = (t_begin + kt) * BC + 16 * vj;
             if (key + 16 <= N) {
                 vst[i] = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
             } else {
@@ -556,7 +584,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
         pf[k] = word;
     };
     auto mask_tail = [&](floatx16 (&s)[KB], int kt) {
-        const int k0 = kt * BC;
+        const int k0 = (t_begin + kt) * BC;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -596,7 +624,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
         if (HAS_QK) load_k(min(j + 3, nkt - 1));
         load_v(min(j + 1, nkt - 1));
 
-        const float f = qsc2 * KSbh[(j * BC) / JA_QK_BLOCK];
+        const float f = qsc2 * KSbh[((t_begin + j) * BC) / JA_QK_BLOCK];
         float bias = 0.f, alpha = 1.f;
         bool grow = false;
         // raise M only if some score of the tile exceeds it (a wave-uniform branch)
@@ -702,6 +730,25 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
 
     const float l_tot = wave_halves_sum(l);
     const float inv = 1.f / l_tot;
+    if (PARTIAL && part_wg) {
+        if (q_row < N) {
+            const int64_t r = ((int64_t)(unit - n_full) * n_split + split) * BR + (q_row - qt * BR);
+            float* orow = OP + r * D;
+            const float* vs = VS + (int64_t)bh * D;
+#pragma unroll
+            for (int ob = 0; ob < NOB; ++ob)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c0 = ob * 32 + j * 8 + hh * 4;
+                    *reinterpret_cast<floatx4*>(orow + c0) =
+                        floatx4{oacc[ob][4 * j] * inv * vs[c0], oacc[ob][4 * j + 1] * inv * vs[c0 + 1],
+                                oacc[ob][4 * j + 2] * inv * vs[c0 + 2],
+                                oacc[ob][4 * j + 3] * inv * vs[c0 + 3]};
+                }
+            if (hh == 0) LP[r] = (m - 8.f + log2f(l_tot)) * kLn2;
+        }
+        return;
+    }
     const bool listed = RROWS && ((rmask[w] >> r32) & 1u);
     if (q_row < N && !listed) {
         __bf16* orow = O + (((int64_t)b * N + q_row) * H + h) * D;
@@ -977,6 +1024,34 @@ hipError_t launch_d(const void* q8, const void* k8, const void* v8t, const float
     return hipGetLastError();
 }
 
+// split-KV: whole rounds of query tiles over all keys, the last round's `tail` tiles as
+// n_split key ranges each, then the merge of the split tiles
+template <int D, bool HI>
+hipError_t launch_split_d(const void* q8, const void* k8, const void* v8t, const float* qs,
+                          const float* ks, const float* vs, const void* qh, const void* kh, int B,
+                          int H, int N, int64_t ldv, float softmax_scale, int n_split, int tail,
+                          float* o_part, float* lse_part, void* o, float* lse,
+                          hipStream_t stream) {
+    constexpr int NW = D == 128 ? FP8_NW128 : 4;
+    constexpr int BR = NW * 32;
+    constexpr int RPB = 256 / (D / 4);
+    const int n_qtiles = (N + BR - 1) / BR;
+    const int n_full = n_qtiles * B * H - tail;
+    const int total = n_full + tail * n_split;
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, NW, HI, false, true>), dim3(total), dim3(NW * 64), 0,
+                       stream, static_cast<const uint8_t*>(q8), static_cast<const uint8_t*>(k8),
+                       static_cast<const uint8_t*>(v8t), qs, ks, vs,
+                       static_cast<const __bf16*>(qh), static_cast<const __bf16*>(kh), H, N, ldv,
+                       softmax_scale * kLog2e, static_cast<__bf16*>(o), lse, n_qtiles, total,
+                       nullptr, nullptr, nullptr, nullptr, 0, n_split, o_part, lse_part, n_full);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((splitkv_merge_kernel<D, BR>), dim3(tail * (BR / RPB)), dim3(256), 0,
+                       stream, o_part, lse_part, n_split, n_full, n_qtiles, H, N,
+                       static_cast<__bf16*>(o), lse);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_repair_d(const void* q8, const void* k8, const void* v8t, const float* qs,
                            const float* ks, const float* vs, const void* q, const void* k,
@@ -1025,6 +1100,62 @@ hipError_t launch_fwd_fp8_repair(const void* q8, const void* k8, const void* v8t
                    : launch_repair_d<128>(q8, k8, v8t, q_scale, k_scale, v_scale, q, k, q_sel,
                                           k_sel, v8t_sel, n_repair, B, H, N, ldv, softmax_scale,
                                           o, lse, stream);
+}
+
+int fp8_splitkv_slots(int D, int mode) {
+    // workgroups that run at once: the device's CUs times the occupancy the runtime gives
+    // for the kernel actually launched
+    int dev = 0, cus = 256, per = 1;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    constexpr int NW128 = FP8_NW128;
+    hipError_t e;
+    if (D == 64)
+        e = mode == JA_FP8_SPLIT
+                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                      &per, fwd_fp8_kernel<64, 4, true, false, true>, 4 * 64, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                      &per, fwd_fp8_kernel<64, 4, false, false, true>, 4 * 64, 0);
+    else
+        e = mode == JA_FP8_SPLIT
+                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                      &per, fwd_fp8_kernel<128, NW128, true, false, true>, NW128 * 64, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                      &per, fwd_fp8_kernel<128, NW128, false, false, true>, NW128 * 64, 0);
+    if (e != hipSuccess || per < 1) per = 1;
+    return cus * per;
+}
+
+int fp8_splitkv_rows_per_tile(int D) { return D == 128 ? FP8_NW128 * 32 : 4 * 32; }
+
+hipError_t launch_fwd_fp8_splitkv(const void* q8, const void* k8, const void* v8t,
+                                  const float* q_scale, const float* k_scale,
+                                  const float* v_scale, int B, int H, int N, int D, int64_t ldv,
+                                  float softmax_scale, int mode, const void* q_hi,
+                                  const void* k_hi, int n_split, float* o_part, float* lse_part,
+                                  void* o, float* lse, hipStream_t stream) {
+    const int tiles = (N + 63) / 64;                        // 64-key tiles
+    n_split = n_split < tiles ? n_split : tiles;            // every key range non-empty
+    const int br = fp8_splitkv_rows_per_tile(D);
+    const int units = (N + br - 1) / br * B * H;
+    const int tail = units % fp8_splitkv_slots(D, mode);   // tiles of the last round
+    if (n_split <= 1 || tail == 0)
+        return launch_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, B, H, N, D, ldv,
+                              softmax_scale, mode, q_hi, k_hi, o, lse, stream);
+    if (mode == JA_FP8_SPLIT)
+        return D == 64 ? launch_split_d<64, true>(q8, k8, v8t, q_scale, k_scale, v_scale, q_hi,
+                                                  k_hi, B, H, N, ldv, softmax_scale, n_split,
+                                                  tail, o_part, lse_part, o, lse, stream)
+                       : launch_split_d<128, true>(q8, k8, v8t, q_scale, k_scale, v_scale, q_hi,
+                                                   k_hi, B, H, N, ldv, softmax_scale, n_split,
+                                                   tail, o_part, lse_part, o, lse, stream);
+    return D == 64 ? launch_split_d<64, false>(q8, k8, v8t, q_scale, k_scale, v_scale, nullptr,
+                                               nullptr, B, H, N, ldv, softmax_scale, n_split,
+                                               tail, o_part, lse_part, o, lse, stream)
+                   : launch_split_d<128, false>(q8, k8, v8t, q_scale, k_scale, v_scale, nullptr,
+                                                nullptr, B, H, N, ldv, softmax_scale, n_split,
+                                                tail, o_part, lse_part, o, lse, stream);
 }
 
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,

@@ -66,6 +66,15 @@ hipError_t launch_fwd_fp8_repair(const void* q8, const void* k8, const void* v8t
                                  const int32_t* k_sel, const void* v8t_sel, int n_repair, int B,
                                  int H, int N, int D, int64_t ldv, float softmax_scale, void* o,
                                  float* lse, hipStream_t stream);
+// fp8 split-KV planning and launch (as for the bf16 forward; 64-key tiles)
+int fp8_splitkv_slots(int D, int mode);
+int fp8_splitkv_rows_per_tile(int D);
+hipError_t launch_fwd_fp8_splitkv(const void* q8, const void* k8, const void* v8t,
+                                  const float* q_scale, const float* k_scale,
+                                  const float* v_scale, int B, int H, int N, int D, int64_t ldv,
+                                  float softmax_scale, int mode, const void* q_hi,
+                                  const void* k_hi, int n_split, float* o_part, float* lse_part,
+                                  void* o, float* lse, hipStream_t stream);
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
                           const float* k_scale, const float* v_scale, int B, int H, int N, int D,
                           int64_t ldv, float softmax_scale, int mode, const void* q_hi,

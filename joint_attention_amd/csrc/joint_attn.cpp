@@ -304,6 +304,82 @@ int joint_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const fl
                                          static_cast<hipStream_t>(stream)));
 }
 
+int64_t joint_attn_fwd_fp8_splitkv_workspace(int B, int H, int64_t N, int D, int n_split) {
+    if (B <= 0 || H <= 0 || N < 0 || n_split <= 0 || !head_size_ok(D)) return -1;
+    // only the query tiles of the last, partial round are split: fewer than the slots of
+    // either mode's kernel on the current device, and than all tiles
+    const int64_t br = ja::fp8_splitkv_rows_per_tile(D);
+    const int64_t units = (N + br - 1) / br * B * H;
+    const int64_t slots = std::max(ja::fp8_splitkv_slots(D, JA_FP8_PLAIN),
+                                   ja::fp8_splitkv_slots(D, JA_FP8_SPLIT));
+    return (int64_t)n_split * std::min(units, slots) * br * (D + 1) * (int64_t)sizeof(float);
+}
+
+int joint_attn_fwd_fp8_splitkv_suggest(int B, int H, int64_t N, int D, int mode) {
+    if (B <= 0 || H <= 0 || N <= 0 || !head_size_ok(D) ||
+        (mode != JA_FP8_PLAIN && mode != JA_FP8_SPLIT))
+        return 1;
+    const int64_t br = ja::fp8_splitkv_rows_per_tile(D);
+    const int64_t units = (N + br - 1) / br * B * H;
+    const int64_t slots = ja::fp8_splitkv_slots(D, mode);
+    const int64_t tail = units % slots;
+    if (tail == 0) return 1;
+    const int64_t tiles = (N + 63) / 64;
+    // the bf16 model (one round of full-length workgroups = 1; about 6 key tiles of fixed
+    // cost per workgroup; the merge reading the partials at ~4 TB/s) with 64-key tiles
+    // and ~1.7 PFLOP/s rounds
+    const double round_s = (double)slots * br * tiles * 64.0 * 4.0 * D / 1.7e15;
+    double best = 0.9;
+    int best_s = 1;
+    for (int s = 2; s <= 16 && s <= tiles; ++s) {
+        const double rounds = (double)((tail * s + slots - 1) / slots);
+        const double merge = (double)tail * s * br * (D + 1) * 4.0 / 4.0e12 / round_s;
+        const double cost = rounds * (1.0 / s + 6.0 / (double)tiles) + merge;
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_s = s;
+        }
+    }
+    return best_s;
+}
+
+int joint_attn_fwd_fp8_splitkv(const void* q8, const void* k8, const void* v8t,
+                               const float* q_scale, const float* k_scale, const float* v_scale,
+                               int B, int H, int64_t N, int D, int64_t ldv, float softmax_scale,
+                               int mode, const void* q_hi, const void* k_hi, int n_split,
+                               void* workspace, int64_t workspace_bytes, void* o, float* lse,
+                               void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (mode != JA_FP8_PLAIN && mode != JA_FP8_SPLIT) return JA_EUNSUPPORTED;
+    if (n_split <= 0 || n_split > 64) return JA_EINVAL;
+    if (N == 0) return JA_OK;
+    if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o || !workspace)
+        return JA_EINVAL;
+    if (mode == JA_FP8_SPLIT && (!q_hi || !k_hi)) return JA_EINVAL;
+    if (workspace_bytes < joint_attn_fwd_fp8_splitkv_workspace(B, H, N, D, n_split))
+        return JA_EINVAL;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) ||
+        !aligned16(workspace))
+        return JA_EUNSUPPORTED;
+    if (mode == JA_FP8_SPLIT && (!aligned16(q_hi) || !aligned16(k_hi))) return JA_EUNSUPPORTED;
+    if (((reinterpret_cast<uintptr_t>(q_scale) | reinterpret_cast<uintptr_t>(k_scale) |
+          reinterpret_cast<uintptr_t>(v_scale)) & 3u) ||
+        (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return JA_EUNSUPPORTED;
+    const int64_t br = ja::fp8_splitkv_rows_per_tile(D);
+    const int64_t slots = std::max(ja::fp8_splitkv_slots(D, JA_FP8_PLAIN),
+                                   ja::fp8_splitkv_slots(D, JA_FP8_SPLIT));
+    const int64_t split_tiles = std::min<int64_t>((N + br - 1) / br * B * H, slots);
+    float* o_part = static_cast<float*>(workspace);
+    float* lse_part = o_part + (int64_t)n_split * split_tiles * br * D;
+    return hip_status(ja::launch_fwd_fp8_splitkv(q8, k8, v8t, q_scale, k_scale, v_scale, B, H,
+                                                 (int)N, D, ldv, softmax_scale, mode, q_hi, k_hi,
+                                                 n_split, o_part, lse_part, o, lse,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int64_t joint_attn_repair_count(int64_t N, double rho) {
     if (N < 0 || !(rho >= 0.0 && rho <= 1.0)) return -1;
     const double x = std::ceil(rho * (double)N);

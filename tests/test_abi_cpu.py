@@ -217,3 +217,24 @@ def test_repair_count_and_validation(lib):
     assert f(*fa(64, 3, sel=None)) == 1
     assert f(*fa(64, 3, qx=fake + 8)) == 2                     # bf16 inputs 16-byte aligned
     assert f(*fa(64, 3, lse=None)) == 1                        # lse is read and rewritten
+
+
+def test_fp8_splitkv_sizes_and_validation(lib):
+    fake = 0x10000
+    ws = lib.joint_attn_fwd_fp8_splitkv_workspace
+    assert ws(2, 24, 16896, 128, 5) == 5 * 256 * 256 * 129 * 4        # one round of tiles
+    assert ws(1, 2, 300, 64, 3) == 3 * 6 * 128 * 65 * 4               # 6 tiles of 128 rows
+    assert ws(1, 1, 16, 96, 2) == -1 and ws(1, 1, 16, 64, 0) == -1
+    sug = lib.joint_attn_fwd_fp8_splitkv_suggest
+    assert sug(2, 24, 16896, 128, 0) == 5 and sug(2, 24, 16896, 128, 1) == 5
+    assert sug(2, 24, 16896, 128, 7) == 1 and sug(1, 1, 40, 128, 0) == 1
+    f = lib.joint_attn_fwd_fp8_splitkv
+    need = ws(1, 2, 64, 128, 2)
+    a = lambda mode=0, n=2, w=fake, wb=need, hi=None: (fake, fake, fake, fake, fake, fake, 1, 2, 64,
+                                                       128, 64, 0.1, mode, hi, hi, n, w, wb, fake,
+                                                       None, None)
+    assert f(*a(n=0)) == 1 and f(*a(n=65)) == 1
+    assert f(*a(wb=need - 1)) == 1 and f(*a(w=None)) == 1
+    assert f(*a(mode=1)) == 1                                  # split mode needs q_hi, k_hi
+    assert f(*a(mode=2)) == 2                                  # repair has its own entry point
+    assert f(*a(w=fake + 4)) == 2

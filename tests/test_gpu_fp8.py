@@ -130,16 +130,20 @@ def test_quant_split_channels_cover_the_outliers():
             assert set(st.outlier_channels.tolist()) <= set(res["got"]["hi_idx"][b, h].tolist())
 
 
-def _fwd_fp8(w, mode, sel=None):
-    """GPU fp8 forward vs the oracle's fp8 attention and its fp64 attention.  The oracle
-    side runs per (b, h) slice (the method is independent per slice), so full-size
-    workloads only quantise the slices that the sampled rows touch."""
+def _fwd_fp8(w, mode, sel=None, n_split=None):
+    """GPU fp8 forward (the split-KV call when n_split is given) vs the oracle's fp8
+    attention and its fp64 attention.  The oracle side runs per (b, h) slice (the method
+    is independent per slice), so full-size workloads only quantise the slices that the
+    sampled rows touch."""
     import joint_attention_amd as ja
     import torch
     res = _quant_both(w, mode)
     t = res["dev"][3]
     scale = 1.0 / math.sqrt(w.D)
-    o, lse = ja.joint_attn_fwd_fp8(t, scale, return_lse=True)
+    if n_split is None:
+        o, lse = ja.joint_attn_fwd_fp8(t, scale, return_lse=True)
+    else:
+        o, lse = ja.joint_attn_fwd_fp8_splitkv(t, scale, n_split=n_split, return_lse=True)
     torch.cuda.synchronize()
     qh, kh, vh = res["host"]
     if sel is None:
