@@ -55,7 +55,8 @@ PEAK_HBM_GBS = 8000.0
 MEASURED_TRAFFIC = {
     "workload": "t2i_2048_bf16",
     "bytes": 1898992704,
-    "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/ja_device.h"),
+    "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/splitkv_merge.h",
+                "joint_attention_amd/csrc/ja_device.h"),
     "sha256_16": "d767b976631ba852",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
