@@ -57,7 +57,7 @@ MEASURED_TRAFFIC = {
     "bytes": 1900311662,
     "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/splitkv_merge.h",
                 "joint_attention_amd/csrc/ja_device.h"),
-    "sha256_16": "fc253fb645ac61ee",
+    "sha256_16": "a04e5a96a2491397",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
 

@@ -373,6 +373,8 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     // 4 (k & 3) .. + 3 of the group's 16 channels; the transposing read hands lane r the 4
     // keys of channel c0 + r.  Written later to `vs` in the V^T layout of the operand reads
     // (the write waits for the reads, so it is placed a few MFMA steps after them).
+    static_assert(!GATHER || NTHREADS * 8 == TILE_ELEMS,
+                  "the transpose moves one 16-byte V^T chunk per thread");
     auto transpose_read = [&](const __bf16* ts) {
         typedef short v4s __attribute__((ext_vector_type(4)));
         const int grp = tid >> 4, i16 = tid & 15;
