@@ -33,7 +33,10 @@
  *       BHDN  [B][H][D][ld]  channel-major with row pitch ld >= N, ld % 16 == 0, used for
  *                            V (columns N..ld-1 are padding that pack writes as zero)
  *   - Supported head sizes D: 64 and 128.  N may be any positive length (no multiple
- *     required); N == 0 is accepted and does nothing.
+ *     required); N == 0 is accepted and does nothing.  The longest sequence is set by
+ *     one head's BHDN V tensor, D * ld <= JA_MAX_HEAD_ELEMS elements (N <= 8,388,608 at
+ *     D = 128, 16,777,216 at D = 64), which keeps every in-kernel offset inside that
+ *     tensor in 32 bits; longer sequences return JA_EINVAL.
  */
 #ifndef JOINT_ATTN_H
 #define JOINT_ATTN_H
@@ -53,6 +56,7 @@ extern "C" {
 #define JA_LAYOUT_BHDN 1
 
 #define JA_MAX_STREAMS 16   /* text + target + up to 14 reference images */
+#define JA_MAX_HEAD_ELEMS (1 << 30)   /* D * ld of one (b, h) of a BHDN tensor, at most */
 #define JA_QK_BLOCK 128     /* tokens per fp8 scale block of Q and K */
 #define JA_HI_CHANNELS 16   /* Q/K channels per (b, h) kept out of e4m3 in fp8 mode 1 */
 

@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("JOINT_ATTN_LIB") or os.path.join(HERE, "libjoint_attn
 JA_OK, JA_EINVAL, JA_EUNSUPPORTED, JA_EHIP = 0, 1, 2, 3
 JA_LAYOUT_BHND, JA_LAYOUT_BHDN = 0, 1
 JA_MAX_STREAMS = 16
+JA_MAX_HEAD_ELEMS = 1 << 30
 JA_QK_BLOCK = 128
 JA_HI_CHANNELS = 16
 JA_SPARSE_BLOCK, JA_SPARSE_MAX_N = 128, 131072

@@ -30,6 +30,7 @@ int check_shape(int B, int H, int64_t N, int D, int64_t ldv) {
     if (B <= 0 || H <= 0 || N < 0 || D <= 0) return JA_EINVAL;
     if (!head_size_ok(D)) return JA_EUNSUPPORTED;
     if (N > kMaxInt / 2 || ldv < N || ldv % 16 != 0) return JA_EINVAL;
+    if ((int64_t)D * ldv > JA_MAX_HEAD_ELEMS) return JA_EINVAL;   // 32-bit V^T offsets
     if ((int64_t)B * H > 65535) return JA_EINVAL;
     const int64_t qtiles = (N + 63) / 64;             // finest query tiling any kernel uses
     if (qtiles * B * H > kMaxInt) return JA_EINVAL;

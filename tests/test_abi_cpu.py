@@ -33,6 +33,16 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_header_constants_match_the_binding():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    defines = dict(re.findall(r"^#define\s+(JA_\w+)\s+(.+?)\s*$", text, flags=re.M))
+    assert len(defines) >= 15
+    for name, value in defines.items():
+        if not re.fullmatch(r"[0-9()<\s]+", value):
+            continue
+        assert getattr(_abi, name) == eval(value), name      # digits, parentheses, shifts
+
+
 def test_strerror_and_ld(lib):
     assert lib.joint_attn_strerror(0) == b"ok"
     assert b"invalid" in lib.joint_attn_strerror(1)
@@ -79,6 +89,13 @@ def test_attention_validation(lib):
     assert f(fake + 4, fake, fake, 1, 2, 64, 128, 64, 0.1, fake, None, None) == 2
     assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, fake, fake + 2, None) == 2  # lse align
     assert f(None, None, None, 1, 2, 0, 128, 0, 0.1, None, None, None) == 0       # N == 0
+    # one head's V^T past JA_MAX_HEAD_ELEMS (its in-kernel offsets are 32-bit)
+    big = _abi.JA_MAX_HEAD_ELEMS // 128 + 16
+    assert f(fake, fake, fake, 1, 1, big, 128, big, 0.1, fake, None, None) == 1
+    assert f(fake, fake, fake, 1, 1, big - 16, 128, big, 0.1, fake, None, None) == 1   # pitch
+    assert f(fake, fake, fake, 1, 1, 2 * big, 64, 2 * big, 0.1, fake, None, None) == 1
+    assert lib.joint_attn_fwd_bf16_splitkv(fake, fake, fake, 1, 1, big, 128, big, 0.1, 2,
+                                           fake, 1 << 30, fake, None, None) == 1
     g = lib.joint_attn_fwd_fp8
     assert g(fake, fake, fake, fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 7, None, None, fake,
              None, None) == 2                                                   # mode
