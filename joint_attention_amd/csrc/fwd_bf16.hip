@@ -62,10 +62,16 @@ namespace {
 #define FWD_BC 32
 #endif
 #ifndef FWD_LEAD
-#define FWD_LEAD 3
+#define FWD_LEAD 2          // operand read distance, tiles loaded by DMA
+#endif
+#ifndef FWD_LEAD_GATHER
+#define FWD_LEAD_GATHER 3   // the same for the register-staged stream gather
 #endif
 #ifndef FWD_TW
 #define FWD_TW 3
+#endif
+#ifndef FWD_DMA
+#define FWD_DMA 1
 #endif
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
@@ -403,6 +409,48 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
             *reinterpret_cast<uint4*>(slot + (w * LOADS + i) * 512 + lane * 8) = vst[i];
     };
 
+    // direct global -> LDS loads (gfx950 global_load_lds_dwordx4; not for GATHER, whose V
+    // goes through a transpose): each wave's 16-byte chunks land lane-linear in the slot,
+    // the layout store_k / store_v write (the swizzle lives in the global offsets), with
+    // no staging registers and no LDS store instructions
+    constexpr bool DMA = FWD_DMA && !GATHER;
+    auto dma16 = [&](const void* src, __bf16* dst) {
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)src,
+            (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    };
+    auto dma_k = [&](int kt, __bf16* slot) {
+        const int k0 = tile_k0(kt);
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const char* src;
+            if (k0 + BC <= N) {
+                src = reinterpret_cast<const char*>(Kbh + (int64_t)k0 * D) + k_off[i];
+            } else {
+                const int key = min(k0 + k_row(i), N - 1);     // rows past N: any finite row
+                src = reinterpret_cast<const char*>(Kbh + (int64_t)key * D + k_chunk(i) * 8);
+            }
+            dma16(src, slot + (w * LOADS + i) * 512);
+        }
+    };
+    auto dma_v = [&](int kt, __bf16* slot) {
+        const int k0 = tile_k0(kt);
+        if (k0 + BC <= N) {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i)
+                dma16(reinterpret_cast<const char*>(Vbh + k0) + v_off[i],
+                      slot + (w * LOADS + i) * 512);
+        } else {                                       // last tile: columns >= N zeroed
+            load_v(kt);
+            store_v(slot);
+        }
+    };
+    // the DMA writes land in LDS asynchronously (counted by vmcnt): every wave waits for
+    // its own before the barrier that hands the slot to the others
+    auto dma_wait = [&]() {
+        if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
+
     // ---- resident state
     const int q_base = qt * BR + w * (QB * 32) + r32;     // query row of block 0
     bf16x8 qf[QB][NQC];
@@ -525,23 +573,31 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                 }
     };
 
-    // prologue: K_0, K_1 -> LDS; S_0; stage K_2 and V_0
-    load_k(0);
-    store_k(sk0);
-    if (nkt > 1) {
-        load_k(1);
-        store_k(sk1);
+    // prologue: K_0, K_1 -> LDS; S_0; (register path) stage K_2 and V_0
+    if constexpr (DMA) {
+        dma_k(0, sk0);
+        if (nkt > 1) dma_k(1, sk1);
+        dma_wait();
+    } else {
+        load_k(0);
+        store_k(sk0);
+        if (nkt > 1) {
+            load_k(1);
+            store_k(sk1);
+        }
     }
     __syncthreads();
     qk_all(sk0, sA);
-    load_k(min(2, nkt - 1));
-    if constexpr (GATHER) {
-        // V_0 token-major before the first barrier; V_1 staged for iteration 0
-        load_v(0);
-        store_v(st0);
-        load_v(min(1, nkt - 1));
-    } else {
-        load_v(0);
+    if constexpr (!DMA) {
+        load_k(min(2, nkt - 1));
+        if constexpr (GATHER) {
+            // V_0 token-major before the first barrier; V_1 staged for iteration 0
+            load_v(0);
+            store_v(st0);
+            load_v(min(1, nkt - 1));
+        } else {
+            load_v(0);
+        }
     }
 
     // iteration j: softmax(S_j) || P_{j-1} V_{j-1} and Q K_{j+1}^T; loads V_j, K_{j+2}
@@ -558,21 +614,27 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         bf16x8 (&p_out)[QB][2 * KB] = P ? pB : pA; // P_j
         bf16x8 (&p_in)[QB][2 * KB] = P ? pA : pB;  // P_{j-1}
         if (!HAS_QK && (N % BC) != 0) mask_tail(s_in, j);
+        dma_wait();
         __syncthreads();
-        // the staged K_{j+2} and V_j go to the slots freed by the barrier; then stage
-        // K_{j+3} and V_{j+1} (indices past the end reload the last tile, unused)
-        if (HAS_QK) store_k(my_k);
+        // DMA: K_{j+2} and V_j go straight to the slots freed by the barrier and land
+        // before the next one.  Register path: the staged K_{j+2} and V_j go there, then
+        // K_{j+3} and V_{j+1} are staged (indices past the end reload the last tile, unused)
+        if constexpr (DMA) {
+            if (HAS_QK && j + 2 < nkt) dma_k(j + 2, my_k);
+            dma_v(j, my_v);
+        }
+        if (!DMA && HAS_QK) store_k(my_k);
         // GATHER: V_{j+1} token-major into the free staging slot; V_j (staged last
         // iteration) read transposed now, written to the V^T slot during the steps
         uint4 vtr = {};
         if constexpr (GATHER) {
             store_v(P ? st0 : st1);
             vtr = transpose_read(P ? st1 : st0);
-        } else {
+        } else if constexpr (!DMA) {
             store_v(my_v);
         }
-        if (HAS_QK) load_k(min(j + 3, nkt - 1));
-        load_v(min(j + (GATHER ? 2 : 1), nkt - 1));
+        if (!DMA && HAS_QK) load_k(min(j + 3, nkt - 1));
+        if constexpr (!DMA) load_v(min(j + (GATHER ? 2 : 1), nkt - 1));
 
         // SPARSE: a wave skips the products and numerators of tiles its query block does not
         // see (their weights are zero; scores left stale are never read: see check)
@@ -582,7 +644,8 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         constexpr int S0 = HAS_PV ? 0 : NPV;           // first MFMA step
         constexpr int S1 = HAS_QK ? NPV + NQK : NPV;   // one past the last step
         constexpr int NST = S1 - S0;
-        constexpr int LEAD = FWD_LEAD;                 // operand reads run this far ahead
+        // operand reads run this far ahead (measured best per load path)
+        constexpr int LEAD = DMA ? FWD_LEAD : FWD_LEAD_GATHER;
         // Offset update.  Each lane first takes the maximum of its own scores only; the
         // wave raises m (exact maximum over both lane halves, rescale of l now and of O
         // after this iteration's P V products) only if some lane's maximum exceeds m by
@@ -697,6 +760,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     {
         const int jl = nkt - 1;
         __bf16* const vs = (jl & 1) ? sv1 : sv0;
+        dma_wait();
         __syncthreads();
         if (!SPARSE || tile_on(jl)) {              // (SPARSE: skipped tiles left P stale)
             if (jl & 1) pv_all(vs, pB);
