@@ -54,10 +54,10 @@ PEAK_HBM_GBS = 8000.0
 # change reports null.
 MEASURED_TRAFFIC = {
     "workload": "t2i_2048_bf16",
-    "bytes": 1900311662,
+    "bytes": 1898368309,
     "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/splitkv_merge.h",
                 "joint_attention_amd/csrc/ja_device.h"),
-    "sha256_16": "a04e5a96a2491397",
+    "sha256_16": "5ccfa4549e47fe9b",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
 
