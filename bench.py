@@ -57,7 +57,7 @@ MEASURED_TRAFFIC = {
     "bytes": 1898368309,
     "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/splitkv_merge.h",
                 "joint_attention_amd/csrc/ja_device.h"),
-    "sha256_16": "5ccfa4549e47fe9b",
+    "sha256_16": "3ff07ed4deaf71e8",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
 

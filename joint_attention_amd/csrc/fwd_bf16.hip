@@ -70,9 +70,6 @@ namespace {
 #ifndef FWD_TW
 #define FWD_TW 3
 #endif
-#ifndef FWD_DMA
-#define FWD_DMA 1
-#endif
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
@@ -259,9 +256,10 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     };
     Cursor kcur = cursor_init(st.k), vcur = cursor_init(st.v);
 
-    // ---- K / V^T tile loads, staged through registers: lane `lane` of wave w owns
-    //      tile bytes (w*LOADS + i) * 1024 + 16 * lane; the swizzle is inverted on the
-    //      global side, so the LDS store is one linear 16-byte write per chunk
+    // ---- K / V^T tile placement: lane `lane` of wave w owns tile bytes
+    //      (w*LOADS + i) * 1024 + 16 * lane; the swizzle is inverted on the global side,
+    //      so each 16-byte chunk lands lane-linear (by DMA, or by one linear LDS store on
+    //      the register-staged path)
     auto k_row = [&](int i) { return ((w * LOADS + i) * 1024 + lane * 16) / (2 * D); };
     auto k_chunk = [&](int i) {
         const int off = (w * LOADS + i) * 1024 + lane * 16;
@@ -288,7 +286,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                           : (uint32_t)(v_row(i) * (int)ldv + v_chunk(i) * 8) * 2u;
     }
     uint4 kst[LOADS], vst[LOADS];                 // staged tiles (global -> registers)
-    auto load_k = [&](int kt) {
+    auto load_k = [&](int kt) {                  // GATHER only (the others load K by DMA)
         const int k0 = tile_k0(kt);
         if constexpr (GATHER) {
             advance(kcur, st.k, k0);                            // wave-uniform
@@ -305,19 +303,6 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                     kst[i] = *reinterpret_cast<const uint4*>(
                         stream_row(st.k, stream_of(key), key) + k_chunk(i) * 8);
                 }
-            }
-            return;
-        }
-        if (k0 + BC <= N) {
-            const char* base = reinterpret_cast<const char*>(Kbh + (int64_t)k0 * D);
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i)
-                kst[i] = *reinterpret_cast<const uint4*>(base + k_off[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                const int key = min(k0 + k_row(i), N - 1);     // rows past N: any finite row
-                kst[i] = *reinterpret_cast<const uint4*>(Kbh + (int64_t)key * D + k_chunk(i) * 8);
             }
         }
     };
@@ -413,7 +398,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     // goes through a transpose): each wave's 16-byte chunks land lane-linear in the slot,
     // the layout store_k / store_v write (the swizzle lives in the global offsets), with
     // no staging registers and no LDS store instructions
-    constexpr bool DMA = FWD_DMA && !GATHER;
+    constexpr bool DMA = !GATHER;
     auto dma16 = [&](const void* src, __bf16* dst) {
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)src,
@@ -588,16 +573,12 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     }
     __syncthreads();
     qk_all(sk0, sA);
-    if constexpr (!DMA) {
+    if constexpr (GATHER) {
         load_k(min(2, nkt - 1));
-        if constexpr (GATHER) {
-            // V_0 token-major before the first barrier; V_1 staged for iteration 0
-            load_v(0);
-            store_v(st0);
-            load_v(min(1, nkt - 1));
-        } else {
-            load_v(0);
-        }
+        // V_0 token-major before the first barrier; V_1 staged for iteration 0
+        load_v(0);
+        store_v(st0);
+        load_v(min(1, nkt - 1));
     }
 
     // iteration j: softmax(S_j) || P_{j-1} V_{j-1} and Q K_{j+1}^T; loads V_j, K_{j+2}
@@ -617,24 +598,21 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         dma_wait();
         __syncthreads();
         // DMA: K_{j+2} and V_j go straight to the slots freed by the barrier and land
-        // before the next one.  Register path: the staged K_{j+2} and V_j go there, then
-        // K_{j+3} and V_{j+1} are staged (indices past the end reload the last tile, unused)
+        // before the next one.  GATHER: the staged K_{j+2} goes there, then K_{j+3} is
+        // staged (indices past the end reload the last tile, unused); V_{j+1} goes
+        // token-major into the free staging slot and V_j (staged last iteration) is read
+        // transposed now, then written to the V^T slot during the steps
+        uint4 vtr = {};
         if constexpr (DMA) {
             if (HAS_QK && j + 2 < nkt) dma_k(j + 2, my_k);
             dma_v(j, my_v);
-        }
-        if (!DMA && HAS_QK) store_k(my_k);
-        // GATHER: V_{j+1} token-major into the free staging slot; V_j (staged last
-        // iteration) read transposed now, written to the V^T slot during the steps
-        uint4 vtr = {};
-        if constexpr (GATHER) {
+        } else {
+            if (HAS_QK) store_k(my_k);
             store_v(P ? st0 : st1);
             vtr = transpose_read(P ? st1 : st0);
-        } else if constexpr (!DMA) {
-            store_v(my_v);
+            if (HAS_QK) load_k(min(j + 3, nkt - 1));
+            load_v(min(j + 2, nkt - 1));
         }
-        if (!DMA && HAS_QK) load_k(min(j + 3, nkt - 1));
-        if constexpr (!DMA) load_v(min(j + (GATHER ? 2 : 1), nkt - 1));
 
         // SPARSE: a wave skips the products and numerators of tiles its query block does not
         // see (their weights are zero; scores left stale are never read: see check)
