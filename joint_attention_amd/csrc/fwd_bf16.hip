@@ -55,6 +55,11 @@ namespace {
 #ifndef FWD_NW
 #define FWD_NW 8
 #endif
+// block-sparse D = 128: 128-row workgroups (two per CU), so that a workgroup visits exactly
+// its own mask row's key blocks instead of the union of two rows'
+#ifndef FWD_NW_SPARSE
+#define FWD_NW_SPARSE 4
+#endif
 #ifndef FWD_QB
 #define FWD_QB 1
 #endif
@@ -821,9 +826,8 @@ hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
     return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, false, true>(q, k, vt, none, B, H, N, ldv,
                                                                   softmax_scale, o, lse, stream,
                                                                   mask)
-                   : launch_d<128, FWD_NW, FWD_QB, FWD_BC, false, true>(q, k, vt, none, B, H, N,
-                                                                        ldv, softmax_scale, o,
-                                                                        lse, stream, mask);
+                   : launch_d<128, FWD_NW_SPARSE, FWD_QB, FWD_BC, false, true>(
+                         q, k, vt, none, B, H, N, ldv, softmax_scale, o, lse, stream, mask);
 }
 
 int splitkv_slots(int D) {
