@@ -79,8 +79,10 @@ namespace {
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 // NW: waves per workgroup (each owns QB 32-row query blocks); BC: keys per tile.  With
-// NW * QB = 8 one workgroup covers 256 query rows, so every K/V tile loaded into LDS
-// serves 256 rows, and two waves share each SIMD.
+// NW * QB = 8 one workgroup covers 256 query rows (every K/V tile loaded into LDS serves
+// 256 rows) and fills a CU at two waves per SIMD; with NW * QB = 4 two 128-row workgroups
+// share a CU (D = 64, and the block-sparse forward, whose workgroups then match its mask
+// blocks).
 // GATHER: Q, K and V are read in place from the per-stream tensors of `st` (token-major
 // [B][L_s][H][D]) instead of the packed Q, K (BHND) and V^T (BHDN); V tiles are then kept
 // token-major in LDS and read with transposing LDS loads.
