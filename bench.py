@@ -54,10 +54,10 @@ PEAK_HBM_GBS = 8000.0
 # change reports null.
 MEASURED_TRAFFIC = {
     "workload": "t2i_2048_bf16",
-    "bytes": 1898368309,
+    "bytes": 1898099395,
     "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/splitkv_merge.h",
                 "joint_attention_amd/csrc/ja_device.h"),
-    "sha256_16": "3ff07ed4deaf71e8",
+    "sha256_16": "1bd083a50be46121",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
 
