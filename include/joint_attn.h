@@ -124,8 +124,8 @@ int joint_attn_fwd_bf16(const void *q, const void *k, const void *vt,
  * runs on a general block-sparse attention kernel; the rule that picks the blocks is not
  * part of this library, the mask is an input.  Query row i of (b, h) attends key j only if
  *     block_mask[b][h][i / JA_SPARSE_BLOCK][j / JA_SPARSE_BLOCK] != 0;
- * a row that attends no key gets O = 0 and lse = -inf.  Key blocks that no query row of a
- * workgroup attends are skipped (the work saved scales with the zero blocks).
+ * a row that attends no key gets O = 0 and lse = -inf.  Each 128-row query block visits
+ * only the key blocks its mask row allows (the work saved scales with the zero blocks).
  *
  *   q, k, vt, o, lse  as for joint_attn_fwd_bf16
  *   block_mask        device uint8 [B][H][nb][nb], nb = ceil(N / JA_SPARSE_BLOCK)
