@@ -57,7 +57,7 @@ MEASURED_TRAFFIC = {
     "bytes": 1898099395,
     "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/splitkv_merge.h",
                 "joint_attention_amd/csrc/ja_device.h"),
-    "sha256_16": "1bd083a50be46121",
+    "sha256_16": "17f063fbb50fe0be",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
 

@@ -853,13 +853,13 @@ int splitkv_rows_per_tile(int D) { return D == 64 ? 4 * FWD_QB * 32 : FWD_NW * F
 
 hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
                                    int N, int D, int64_t ldv, float softmax_scale, int n_split,
-                                   float* o_part, float* lse_part, void* o, float* lse,
-                                   hipStream_t stream) {
+                                   int slots, float* o_part, float* lse_part, void* o,
+                                   float* lse, hipStream_t stream) {
     const int tiles = (N + FWD_BC - 1) / FWD_BC;
     n_split = n_split < tiles ? n_split : tiles;               // every key range non-empty
     const int BRr = splitkv_rows_per_tile(D);
     const int n_units = (N + BRr - 1) / BRr * B * H;
-    const int tail = n_units % splitkv_slots(D);              // tiles of the last, partial round
+    const int tail = n_units % slots;                         // tiles of the last, partial round
     if (n_split <= 1 || tail == 0) return launch_fwd_bf16(q, k, vt, B, H, N, D, ldv, softmax_scale,
                                                            o, lse, stream);
     const int n_full = n_units - tail;

@@ -1133,13 +1133,13 @@ hipError_t launch_fwd_fp8_splitkv(const void* q8, const void* k8, const void* v8
                                   const float* q_scale, const float* k_scale,
                                   const float* v_scale, int B, int H, int N, int D, int64_t ldv,
                                   float softmax_scale, int mode, const void* q_hi,
-                                  const void* k_hi, int n_split, float* o_part, float* lse_part,
-                                  void* o, float* lse, hipStream_t stream) {
+                                  const void* k_hi, int n_split, int slots, float* o_part,
+                                  float* lse_part, void* o, float* lse, hipStream_t stream) {
     const int tiles = (N + 63) / 64;                        // 64-key tiles
     n_split = n_split < tiles ? n_split : tiles;            // every key range non-empty
     const int br = fp8_splitkv_rows_per_tile(D);
     const int units = (N + br - 1) / br * B * H;
-    const int tail = units % fp8_splitkv_slots(D, mode);   // tiles of the last round
+    const int tail = units % slots;                         // tiles of the last round
     if (n_split <= 1 || tail == 0)
         return launch_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, B, H, N, D, ldv,
                               softmax_scale, mode, q_hi, k_hi, o, lse, stream);

@@ -32,13 +32,14 @@ hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
                                   float softmax_scale, void* o, float* lse, hipStream_t stream);
 
 // split-KV planning: workgroups that run at once on the current device, and query rows
-// per workgroup of the bf16 forward for head size D
+// per workgroup of the bf16 forward for head size D.  The launch takes the slot count the
+// caller sized the workspace with, so that both use one answer of the device query.
 int splitkv_slots(int D);
 int splitkv_rows_per_tile(int D);
 hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
                                    int N, int D, int64_t ldv, float softmax_scale, int n_split,
-                                   float* o_part, float* lse_part, void* o, float* lse,
-                                   hipStream_t stream);
+                                   int slots, float* o_part, float* lse_part, void* o,
+                                   float* lse, hipStream_t stream);
 
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,
                                    float softmax_scale, void* o, float* lse,
@@ -73,8 +74,8 @@ hipError_t launch_fwd_fp8_splitkv(const void* q8, const void* k8, const void* v8
                                   const float* q_scale, const float* k_scale,
                                   const float* v_scale, int B, int H, int N, int D, int64_t ldv,
                                   float softmax_scale, int mode, const void* q_hi,
-                                  const void* k_hi, int n_split, float* o_part, float* lse_part,
-                                  void* o, float* lse, hipStream_t stream);
+                                  const void* k_hi, int n_split, int slots, float* o_part,
+                                  float* lse_part, void* o, float* lse, hipStream_t stream);
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
                           const float* k_scale, const float* v_scale, int B, int H, int N, int D,
                           int64_t ldv, float softmax_scale, int mode, const void* q_hi,

@@ -203,19 +203,20 @@ int joint_attn_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, in
     if (n_split <= 0 || n_split > 64) return JA_EINVAL;
     if (N == 0) return JA_OK;
     if (!q || !k || !vt || !o || !workspace) return JA_EINVAL;
-    if (workspace_bytes < joint_attn_fwd_bf16_splitkv_workspace(B, H, N, D, n_split))
+    // one device query sizes the workspace check, the partial layout and the launch
+    const int slots = ja::splitkv_slots(D);
+    const int64_t br = ja::splitkv_rows_per_tile(D);
+    const int64_t split_tiles = std::min<int64_t>((N + br - 1) / br * B * H, slots);
+    if (workspace_bytes < (int64_t)n_split * split_tiles * br * (D + 1) * (int64_t)sizeof(float))
         return JA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o) ||
         !aligned16(workspace))
         return JA_EUNSUPPORTED;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
-    const int64_t br = ja::splitkv_rows_per_tile(D);
-    const int64_t split_tiles =
-        std::min<int64_t>((N + br - 1) / br * B * H, ja::splitkv_slots(D));
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = o_part + (int64_t)n_split * split_tiles * br * D;
     return hip_status(ja::launch_fwd_bf16_splitkv(q, k, vt, B, H, (int)N, D, ldv, softmax_scale,
-                                                  n_split, o_part, lse_part, o, lse,
+                                                  n_split, slots, o_part, lse_part, o, lse,
                                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -359,7 +360,14 @@ int joint_attn_fwd_fp8_splitkv(const void* q8, const void* k8, const void* v8t,
     if (!q8 || !k8 || !v8t || !q_scale || !k_scale || !v_scale || !o || !workspace)
         return JA_EINVAL;
     if (mode == JA_FP8_SPLIT && (!q_hi || !k_hi)) return JA_EINVAL;
-    if (workspace_bytes < joint_attn_fwd_fp8_splitkv_workspace(B, H, N, D, n_split))
+    // one device query per mode: the launch's slots never exceed the ones the partial
+    // layout and the workspace check are sized with (their maximum over both modes)
+    const int slots = ja::fp8_splitkv_slots(D, mode);
+    const int64_t br = ja::fp8_splitkv_rows_per_tile(D);
+    const int64_t slots_ws = std::max<int64_t>(
+        slots, ja::fp8_splitkv_slots(D, mode == JA_FP8_PLAIN ? JA_FP8_SPLIT : JA_FP8_PLAIN));
+    const int64_t split_tiles = std::min<int64_t>((N + br - 1) / br * B * H, slots_ws);
+    if (workspace_bytes < (int64_t)n_split * split_tiles * br * (D + 1) * (int64_t)sizeof(float))
         return JA_EINVAL;
     if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) ||
         !aligned16(workspace))
@@ -369,15 +377,11 @@ int joint_attn_fwd_fp8_splitkv(const void* q8, const void* k8, const void* v8t,
           reinterpret_cast<uintptr_t>(v_scale)) & 3u) ||
         (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return JA_EUNSUPPORTED;
-    const int64_t br = ja::fp8_splitkv_rows_per_tile(D);
-    const int64_t slots = std::max(ja::fp8_splitkv_slots(D, JA_FP8_PLAIN),
-                                   ja::fp8_splitkv_slots(D, JA_FP8_SPLIT));
-    const int64_t split_tiles = std::min<int64_t>((N + br - 1) / br * B * H, slots);
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = o_part + (int64_t)n_split * split_tiles * br * D;
     return hip_status(ja::launch_fwd_fp8_splitkv(q8, k8, v8t, q_scale, k_scale, v_scale, B, H,
                                                  (int)N, D, ldv, softmax_scale, mode, q_hi, k_hi,
-                                                 n_split, o_part, lse_part, o, lse,
+                                                 n_split, slots, o_part, lse_part, o, lse,
                                                  static_cast<hipStream_t>(stream)));
 }
 
