@@ -343,7 +343,10 @@ int joint_attn_quant_fp8_repair(const void *q, const void *k, const void *vt, in
  * key's code term by its exact-value term (rebuilding the row's state from O and lse).
  *   q8 ... v_scale    as written by joint_attn_quant_fp8_repair
  *   q, k              bf16 BHND [B][H][N][D]: the unquantised inputs of the quantiser
- *   q_sel, k_sel, v8t_sel   as written by joint_attn_quant_fp8_repair
+ *   q_sel, k_sel, v8t_sel   as written by joint_attn_quant_fp8_repair with the same
+ *                     n_repair: ascending distinct token indices in [0, N).  The kernels
+ *                     index Q, K and LDS with them unchecked (checking would cost a pass
+ *                     over the lists); other contents are undefined behaviour.
  *   N                 at most JA_REPAIR_MAX_N
  *   o                 bf16 BNHD [B][N][H][D];  lse fp32 [B][H][N], required (the key
  *                     correction reads and rewrites it)
