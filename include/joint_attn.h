@@ -345,8 +345,9 @@ int joint_attn_quant_fp8_repair(const void *q, const void *k, const void *vt, in
  *   q, k              bf16 BHND [B][H][N][D]: the unquantised inputs of the quantiser
  *   q_sel, k_sel, v8t_sel   as written by joint_attn_quant_fp8_repair with the same
  *                     n_repair: ascending distinct token indices in [0, N).  The kernels
- *                     index Q, K and LDS with them unchecked (checking would cost a pass
- *                     over the lists); other contents are undefined behaviour.
+ *                     clamp every entry they load into [0, N) (a negative key entry is
+ *                     skipped), so lists of other contents give wrong results in O and
+ *                     lse but no access outside the arguments' extents.
  *   N                 at most JA_REPAIR_MAX_N
  *   o                 bf16 BNHD [B][N][H][D];  lse fp32 [B][H][N], required (the key
  *                     correction reads and rewrites it)

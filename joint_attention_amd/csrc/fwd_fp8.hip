@@ -116,17 +116,19 @@ __device__ __forceinline__ void repair_rows(
     for (int i = tid; i < nwords; i += NT) kmask[i] = 0;
     for (int i = tid; i < D * 33; i += NT) (&so[0][0])[i] = 0.f;
     __syncthreads();
+    // list entries are clamped to [0, N): a caller's bad list gives wrong rows, never an
+    // access outside Q, K, O, LSE or the LDS mask
     for (int i = tid; i < NREP; i += NT) {
-        const int key = KSEL[(int64_t)bh * NREP + i];
+        const int key = min(max(KSEL[(int64_t)bh * NREP + i], 0), N - 1);
         atomicOr(&kmask[key >> 5], 1u << (key & 31));
     }
     __syncthreads();
 
     const int slot = rb * 32 + r32;
-    const int qi = QSEL[(int64_t)bh * NREP + min(slot, NREP - 1)];
+    const int qi = min(max(QSEL[(int64_t)bh * NREP + min(slot, NREP - 1)], 0), N - 1);
     for (int x = tid; x < 32 * (D / 8); x += NT) {     // the 32 rows' exact Q -> LDS
         const int r = x / (D / 8), u = x % (D / 8);
-        const int qr = QSEL[(int64_t)bh * NREP + min(rb * 32 + r, NREP - 1)];
+        const int qr = min(max(QSEL[(int64_t)bh * NREP + min(rb * 32 + r, NREP - 1)], 0), N - 1);
         *reinterpret_cast<uint4*>(&sq[r][u * 8]) =
             *reinterpret_cast<const uint4*>(Q + ((int64_t)bh * N + qr) * D + u * 8);
     }
@@ -825,7 +827,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_keyfix_kernel(
         __syncthreads();                                // earlier readers
         if (tid < GT * BC) {
             const int r = g * GT * BC + tid;
-            const int key = r < NREP ? sel[r] : -1;
+            // (entries clamped below N; a negative one counts as an empty slot)
+            const int key = r < NREP ? min(sel[r], N - 1) : -1;
             ssel[tid] = key;
             // empty slots: any finite positive factor, so that -inf logits stay -inf
             ksl[tid] = key >= 0 ? KS[(int64_t)bh * nblk + key / JA_QK_BLOCK] : 1.f;

@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 
 #include "joint_attn.h"
 #include "ja_launch.h"
@@ -23,6 +24,22 @@ int hip_status(hipError_t e) {
     g_last_hip_error = static_cast<int>(e);
     return JA_EHIP;
 }
+
+// Test hook for the launch-failure path: with JOINT_ATTN_SIMULATE_HIP_ERROR set to a
+// positive hipError_t code, every call that passes validation reports that code as a
+// launch failure (JA_EHIP) without enqueuing anything.
+hipError_t simulated_hip_error() {
+    const char* s = std::getenv("JOINT_ATTN_SIMULATE_HIP_ERROR");
+    if (s == nullptr || *s == '\0') return hipSuccess;
+    const long v = std::strtol(s, nullptr, 10);
+    return v > 0 && v < 100000 ? static_cast<hipError_t>(v) : hipSuccess;
+}
+
+#define JA_LAUNCH(expr)                                        \
+    do {                                                        \
+        const hipError_t sim_ = simulated_hip_error();          \
+        return hip_status(sim_ != hipSuccess ? sim_ : (expr));  \
+    } while (0)
 
 // Shared checks of the attention-shaped calls: sizes, pitch, and that every launch
 // dimension and 32-bit in-kernel index stays in range.
@@ -119,8 +136,8 @@ int joint_attn_pack(int n_streams, const void* const* src, const int64_t* lens, 
     if (cols > 0 && !aligned16(dst)) return JA_EUNSUPPORTED;
     for (int s = 0; s <= n_streams; ++s) offsets[s] = off[s];
     if (cols == 0) return JA_OK;
-    return hip_status(ja::launch_pack(n_streams, src, off, B, H, D, layout, ld, dst,
-                                      static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_pack(n_streams, src, off, B, H, D, layout, ld, dst,
+                              static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_fwd_bf16(const void* q, const void* k, const void* vt, int B, int H, int64_t N,
@@ -133,8 +150,8 @@ int joint_attn_fwd_bf16(const void* q, const void* k, const void* vt, int B, int
     if (!q || !k || !vt || !o) return JA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return JA_EUNSUPPORTED;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
-    return hip_status(ja::launch_fwd_bf16(q, k, vt, B, H, (int)N, D, ldv, softmax_scale, o, lse,
-                                          static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_fwd_bf16(q, k, vt, B, H, (int)N, D, ldv, softmax_scale, o, lse,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_fwd_bf16_sparse(const void* q, const void* k, const void* vt, int B, int H,
@@ -148,9 +165,9 @@ int joint_attn_fwd_bf16_sparse(const void* q, const void* k, const void* vt, int
     if (!q || !k || !vt || !o || !block_mask) return JA_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return JA_EUNSUPPORTED;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
-    return hip_status(ja::launch_fwd_bf16_sparse(q, k, vt, block_mask, B, H, (int)N, D, ldv,
-                                                 softmax_scale, o, lse,
-                                                 static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_fwd_bf16_sparse(q, k, vt, block_mask, B, H, (int)N, D, ldv,
+                                         softmax_scale, o, lse,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int64_t joint_attn_fwd_bf16_splitkv_workspace(int B, int H, int64_t N, int D, int n_split) {
@@ -215,9 +232,9 @@ int joint_attn_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, in
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = o_part + (int64_t)n_split * split_tiles * br * D;
-    return hip_status(ja::launch_fwd_bf16_splitkv(q, k, vt, B, H, (int)N, D, ldv, softmax_scale,
-                                                  n_split, slots, o_part, lse_part, o, lse,
-                                                  static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_fwd_bf16_splitkv(q, k, vt, B, H, (int)N, D, ldv, softmax_scale,
+                                          n_split, slots, o_part, lse_part, o, lse,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_fwd_bf16_streams(int n_streams, const void* const* q, const void* const* k,
@@ -237,8 +254,8 @@ int joint_attn_fwd_bf16_streams(int n_streams, const void* const* q, const void*
     if (!o) return JA_EINVAL;
     if (!aligned16(o)) return JA_EUNSUPPORTED;
     if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
-    return hip_status(ja::launch_fwd_bf16_streams(st, B, H, (int)N, D, softmax_scale, o, lse,
-                                                  static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_fwd_bf16_streams(st, B, H, (int)N, D, softmax_scale, o, lse,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int64_t N,
@@ -254,9 +271,9 @@ int joint_attn_quant_fp8(const void* q, const void* k, const void* vt, int B, in
                                         hi_idx, ch_amax);
     if (ost != JA_OK) return ost;
     if (!aligned16(q) || !aligned16(k) || !aligned16(vt)) return JA_EUNSUPPORTED;
-    return hip_status(ja::launch_quant_fp8(q, k, vt, B, H, (int)N, D, ldv, mode, q8, k8, v8t,
-                                           q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
-                                           ch_amax, static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_quant_fp8(q, k, vt, B, H, (int)N, D, ldv, mode, q8, k8, v8t,
+                                   q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
+                                   ch_amax, static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_quant_fp8_streams(int n_streams, const void* const* q, const void* const* k,
@@ -278,9 +295,9 @@ int joint_attn_quant_fp8_streams(int n_streams, const void* const* q, const void
     const int ost = check_quant_outputs(mode, q8, k8, v8t, q_scale, k_scale, v_scale, q_hi, k_hi,
                                         hi_idx, ch_amax);
     if (ost != JA_OK) return ost;
-    return hip_status(ja::launch_quant_fp8_streams(st, B, H, (int)N, D, ldv, mode, q8, k8, v8t,
-                                                   q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
-                                                   ch_amax, static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_quant_fp8_streams(st, B, H, (int)N, D, ldv, mode, q8, k8, v8t,
+                                           q_scale, k_scale, v_scale, q_hi, k_hi, hi_idx,
+                                           ch_amax, static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* q_scale,
@@ -301,9 +318,9 @@ int joint_attn_fwd_fp8(const void* q8, const void* k8, const void* v8t, const fl
           reinterpret_cast<uintptr_t>(v_scale)) & 3u) ||
         (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return JA_EUNSUPPORTED;
-    return hip_status(ja::launch_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, B, H, (int)N, D,
-                                         ldv, softmax_scale, mode, q_hi, k_hi, o, lse,
-                                         static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_fwd_fp8(q8, k8, v8t, q_scale, k_scale, v_scale, B, H, (int)N, D,
+                                 ldv, softmax_scale, mode, q_hi, k_hi, o, lse,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 int64_t joint_attn_fwd_fp8_splitkv_workspace(int B, int H, int64_t N, int D, int n_split) {
@@ -379,10 +396,10 @@ int joint_attn_fwd_fp8_splitkv(const void* q8, const void* k8, const void* v8t,
         return JA_EUNSUPPORTED;
     float* o_part = static_cast<float*>(workspace);
     float* lse_part = o_part + (int64_t)n_split * split_tiles * br * D;
-    return hip_status(ja::launch_fwd_fp8_splitkv(q8, k8, v8t, q_scale, k_scale, v_scale, B, H,
-                                                 (int)N, D, ldv, softmax_scale, mode, q_hi, k_hi,
-                                                 n_split, slots, o_part, lse_part, o, lse,
-                                                 static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_fwd_fp8_splitkv(q8, k8, v8t, q_scale, k_scale, v_scale, B, H,
+                                         (int)N, D, ldv, softmax_scale, mode, q_hi, k_hi,
+                                         n_split, slots, o_part, lse_part, o, lse,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int64_t joint_attn_repair_count(int64_t N, double rho) {
@@ -411,10 +428,10 @@ int joint_attn_quant_fp8_repair(const void* q, const void* k, const void* vt, in
     if (!aligned4(q_err) || !aligned4(k_err) || (n_repair > 0 && (!aligned4(q_sel) ||
                                                                    !aligned4(k_sel))))
         return JA_EUNSUPPORTED;
-    return hip_status(ja::launch_quant_fp8_repair(q, k, vt, B, H, (int)N, D, ldv, (int)n_repair,
-                                                  q8, k8, v8t, q_scale, k_scale, v_scale, q_err,
-                                                  k_err, q_sel, k_sel, v8t_sel,
-                                                  static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_quant_fp8_repair(q, k, vt, B, H, (int)N, D, ldv, (int)n_repair,
+                                          q8, k8, v8t, q_scale, k_scale, v_scale, q_err,
+                                          k_err, q_sel, k_sel, v8t_sel,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_fwd_fp8_repair(const void* q8, const void* k8, const void* v8t,
@@ -439,10 +456,10 @@ int joint_attn_fwd_fp8_repair(const void* q8, const void* k8, const void* v8t,
         !aligned4(lse) || (n_repair > 0 && (!aligned4(q_sel) || !aligned4(k_sel) ||
                                             !aligned16(v8t_sel))))
         return JA_EUNSUPPORTED;
-    return hip_status(ja::launch_fwd_fp8_repair(q8, k8, v8t, q_scale, k_scale, v_scale, q, k,
-                                                q_sel, k_sel, v8t_sel, (int)n_repair, B, H, (int)N, D,
-                                                ldv, softmax_scale, o, lse,
-                                                static_cast<hipStream_t>(stream)));
+    JA_LAUNCH(ja::launch_fwd_fp8_repair(q8, k8, v8t, q_scale, k_scale, v_scale, q, k,
+                                        q_sel, k_sel, v8t_sel, (int)n_repair, B, H, (int)N, D,
+                                        ldv, softmax_scale, o, lse,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -12,6 +12,9 @@ import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attention_ref.c")
+# ORACLE_ATTENTION_LIB loads another build of the same source instead (the sanitizer
+# test builds one with AddressSanitizer / UndefinedBehaviorSanitizer)
+_LIB_OVERRIDE = os.environ.get("ORACLE_ATTENTION_LIB")
 _LIB = os.path.join(_HERE, "liboracle_attention.so")
 _lock = threading.Lock()
 _lib = None
@@ -34,8 +37,11 @@ def lib() -> ctypes.CDLL:
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            h = ctypes.CDLL(_LIB)
+            if _LIB_OVERRIDE:
+                h = ctypes.CDLL(_LIB_OVERRIDE)
+            else:
+                build()
+                h = ctypes.CDLL(_LIB)
             h.oracle_attention_rows.restype = ctypes.c_int
             h.oracle_attention_rows.argtypes = [
                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,

@@ -82,3 +82,51 @@ def gather_rows(o_tok: np.ndarray, sel: np.ndarray) -> np.ndarray:
 
 def softmax_scale(D: int) -> float:
     return 1.0 / math.sqrt(D)
+
+
+def splitkv_geometry(precision: str, D: int):
+    """(query rows per tile, workgroups resident at once) of a split-KV forward on the
+    current device, read back from the library's workspace-size query: the workspace holds
+    rows * (D + 1) floats per tile and range, for min(tiles, slots) tiles."""
+    import joint_attention_amd as ja
+    lib = ja.load()
+    f = (lib.joint_attn_fwd_bf16_splitkv_workspace if precision == "bf16"
+         else lib.joint_attn_fwd_fp8_splitkv_workspace)
+    per_row = (D + 1) * 4
+    br = int(f(1, 1, 1, D, 1)) // per_row
+    slots = int(f(1, 65535, br, D, 1)) // (br * per_row)
+    return br, slots
+
+
+def split_tile_rows(w, br: int, slots: int) -> np.ndarray:
+    """(b, h, i) of every query row in the tiles of the last, partial round of workgroups:
+    the tiles that a split-KV forward cuts into key ranges and merges.  Tile u covers rows
+    qt*br .. of slice (b, h), u = (b*H + h) * ceil(N/br) + qt; whole rounds of `slots`
+    tiles come first."""
+    nq = -(-w.N // br)
+    units = nq * w.B * w.H
+    rows = []
+    for u in range(units - units % slots, units):
+        bh, qt = divmod(u, nq)
+        b, h = divmod(bh, w.H)
+        rows.extend((b, h, i) for i in range(qt * br, min(w.N, (qt + 1) * br)))
+    return np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+
+
+def with_split_tile_rows(w, sel: np.ndarray, precision: str, n_rows: int = 128,
+                         seed: int = 0):
+    """`sel` plus up to n_rows rows drawn from the split tiles (each split tile's first and
+    last row always included); returns (rows sorted by (b, h, i), how many are in split
+    tiles)."""
+    br, slots = splitkv_geometry(precision, w.D)
+    split = split_tile_rows(w, br, slots)
+    if len(split) == 0:
+        return sel, 0
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(len(split), min(n_rows, len(split)), replace=False)
+    ends = np.flatnonzero((split[:, 2] % br == 0) | (split[:, 2] % br == br - 1) |
+                          (split[:, 2] == w.N - 1))
+    extra = split[np.union1d(pick, ends)]
+    rows = np.unique(np.concatenate([sel, extra]), axis=0)
+    in_split = len(set(map(tuple, split.tolist())) & set(map(tuple, rows.tolist())))
+    return rows, in_split

@@ -255,3 +255,106 @@ def test_fp8_splitkv_sizes_and_validation(lib):
     assert f(*a(mode=1)) == 1                                  # split mode needs q_hi, k_hi
     assert f(*a(mode=2)) == 2                                  # repair has its own entry point
     assert f(*a(w=fake + 4)) == 2
+
+
+def test_launch_failure_is_reported(lib, monkeypatch):
+    # every entry point, called with valid arguments, reports a launch failure as JA_EHIP
+    # and keeps the HIP error for joint_attn_last_hip_error (the library's test hook
+    # JOINT_ATTN_SIMULATE_HIP_ERROR stands in for the runtime's refusal; nothing is
+    # launched)
+    fake = 0x10000
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    monkeypatch.setenv("JOINT_ATTN_SIMULATE_HIP_ERROR", "98")
+    two = (P * 2)(fake, fake)
+    lens = (I64 * 2)(32, 96)
+    offs = (I64 * 3)()
+    N, ldv = 128, 128
+    ws_bf = lib.joint_attn_fwd_bf16_splitkv_workspace(1, 2, N, 128, 2)
+    ws_f8 = lib.joint_attn_fwd_fp8_splitkv_workspace(1, 2, N, 128, 2)
+    calls = {
+        "pack": lambda: lib.joint_attn_pack(2, two, lens, 1, 2, 128, 1, ldv, fake, offs, None),
+        "fwd_bf16": lambda: lib.joint_attn_fwd_bf16(fake, fake, fake, 1, 2, N, 128, ldv, 0.1,
+                                                    fake, fake, None),
+        "fwd_bf16_sparse": lambda: lib.joint_attn_fwd_bf16_sparse(
+            fake, fake, fake, 1, 2, N, 128, ldv, fake, 0.1, fake, None, None),
+        "fwd_bf16_splitkv": lambda: lib.joint_attn_fwd_bf16_splitkv(
+            fake, fake, fake, 1, 2, N, 128, ldv, 0.1, 2, fake, ws_bf, fake, None, None),
+        "fwd_bf16_streams": lambda: lib.joint_attn_fwd_bf16_streams(
+            2, two, two, two, lens, 1, 2, 128, 0.1, fake, None, offs, None),
+        "quant_fp8": lambda: lib.joint_attn_quant_fp8(
+            fake, fake, fake, 1, 2, N, 128, ldv, 1, fake, fake, fake, fake, fake, fake, fake,
+            fake, fake, fake, None),
+        "quant_fp8_streams": lambda: lib.joint_attn_quant_fp8_streams(
+            2, two, two, two, lens, 1, 2, 128, ldv, 0, fake, fake, fake, fake, fake, fake, None,
+            None, None, None, offs, None),
+        "fwd_fp8": lambda: lib.joint_attn_fwd_fp8(fake, fake, fake, fake, fake, fake, 1, 2, N, 128,
+                                                  ldv, 0.1, 1, fake, fake, fake, None, None),
+        "fwd_fp8_splitkv": lambda: lib.joint_attn_fwd_fp8_splitkv(
+            fake, fake, fake, fake, fake, fake, 1, 2, N, 128, ldv, 0.1, 0, None, None, 2, fake,
+            ws_f8, fake, None, None),
+        "quant_fp8_repair": lambda: lib.joint_attn_quant_fp8_repair(
+            fake, fake, fake, 1, 2, N, 128, ldv, 3, fake, fake, fake, fake, fake, fake, fake, fake,
+            fake, fake, fake, None),
+        "fwd_fp8_repair": lambda: lib.joint_attn_fwd_fp8_repair(
+            fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, 3, 1, 2, N, 128, ldv,
+            0.1, fake, fake, None),
+    }
+    for name, call in calls.items():
+        assert call() == 3, name
+        assert lib.joint_attn_last_hip_error() == 98, name
+    assert offs[:] == [0, 32, 128]                # outputs of the host side are still written
+    assert b"HIP" in lib.joint_attn_strerror(3)
+    err = _abi.JointAttnError("joint_attn_fwd_bf16", 3, 98)
+    assert "hipError 98" in str(err) and err.status == 3
+    # an invalid argument is still reported as such, before the hook
+    assert lib.joint_attn_fwd_bf16(None, fake, fake, 1, 2, N, 128, ldv, 0.1, fake, None, None) == 1
+
+
+@pytest.mark.skipif(os.environ.get("JOINT_ATTN_STUB_LAUNCHERS") != "1",
+                    reason="valid calls would launch kernels; runs only against the "
+                           "host-only build with stand-in launchers (sanitizer test)")
+def test_valid_calls_reach_the_launchers(lib, monkeypatch):
+    # the same valid calls as above, without the failure hook: each passes validation and
+    # reaches its launcher (the stand-ins check the invariants the kernels rely on)
+    monkeypatch.delenv("JOINT_ATTN_SIMULATE_HIP_ERROR", raising=False)
+    fake = 0x10000
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    two = (P * 2)(fake, fake)
+    lens = (I64 * 2)(32, 96)
+    offs = (I64 * 3)()
+    for N, D, B, H in ((128, 128, 1, 2), (300, 64, 2, 3), (16896, 128, 2, 24)):
+        ldv = (N + 15) // 16 * 16
+        lens[0], lens[1] = 32, N - 32
+        assert lib.joint_attn_pack(2, two, lens, B, H, D, 1, ldv, fake, offs, None) == 0
+        assert offs[:] == [0, 32, N]
+        assert lib.joint_attn_fwd_bf16(fake, fake, fake, B, H, N, D, ldv, 0.1, fake, fake,
+                                       None) == 0
+        for n_split in (1, 2, 5, 64):
+            ws = lib.joint_attn_fwd_bf16_splitkv_workspace(B, H, N, D, n_split)
+            assert lib.joint_attn_fwd_bf16_splitkv(fake, fake, fake, B, H, N, D, ldv, 0.1,
+                                                   n_split, fake, ws, fake, None, None) == 0
+            for mode in (0, 1):
+                ws8 = lib.joint_attn_fwd_fp8_splitkv_workspace(B, H, N, D, n_split)
+                assert lib.joint_attn_fwd_fp8_splitkv(
+                    fake, fake, fake, fake, fake, fake, B, H, N, D, ldv, 0.1, mode, fake, fake,
+                    n_split, fake, ws8, fake, None, None) == 0
+        assert lib.joint_attn_fwd_bf16_streams(2, two, two, two, lens, B, H, D, 0.1, fake,
+                                               None, offs, None) == 0
+        for mode in (0, 1):
+            assert lib.joint_attn_quant_fp8(fake, fake, fake, B, H, N, D, ldv, mode, fake, fake,
+                                            fake, fake, fake, fake, fake, fake, fake, fake,
+                                            None) == 0
+            assert lib.joint_attn_quant_fp8_streams(
+                2, two, two, two, lens, B, H, D, ldv, mode, fake, fake, fake, fake, fake, fake,
+                fake, fake, fake, fake, offs, None) == 0
+            assert lib.joint_attn_fwd_fp8(fake, fake, fake, fake, fake, fake, B, H, N, D, ldv,
+                                          0.1, mode, fake, fake, fake, None, None) == 0
+        n = lib.joint_attn_repair_count(N, 0.005)
+        assert lib.joint_attn_quant_fp8_repair(fake, fake, fake, B, H, N, D, ldv, n, fake, fake,
+                                               fake, fake, fake, fake, fake, fake, fake, fake,
+                                               fake, None) == 0
+        assert lib.joint_attn_fwd_fp8_repair(fake, fake, fake, fake, fake, fake, fake, fake,
+                                             fake, fake, fake, n, B, H, N, D, ldv, 0.1, fake,
+                                             fake, None) == 0
+        assert lib.joint_attn_fwd_bf16_sparse(fake, fake, fake, B, H, N, D, ldv, fake, 0.1,
+                                              fake, None, None) == 0

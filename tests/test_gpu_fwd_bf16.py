@@ -2,8 +2,9 @@
 
 Bar: relative Frobenius error <= 5e-3 and max |err| <= 2e-2 over the compared rows.
 Small and ragged shapes compare every output row; the full-size workloads compare a
-row sample (every row within two tokens of each stream boundary plus random rows),
-in the same launch configuration the benchmark times.
+row sample (every row within two tokens of each stream boundary plus random rows) of
+the plain forward.  The split-KV forward that the benchmark's step times is compared at
+full size, including rows of its split tiles, in test_gpu_splitkv.py.
 """
 import math
 

@@ -3,7 +3,8 @@ the oracle at each path's own bar.
 
 - sparse and token repair: exactly their declared maxima, JA_SPARSE_MAX_N and
   JA_REPAIR_MAX_N (131072 tokens);
-- fp8 plain and split: 131072 - 45 tokens (a ragged last tile), plain and split-KV calls;
+- fp8 plain and split: 130771 tokens (a ragged last tile; 511 query tiles, so the split-KV
+  call splits the 255 of its last round), plain and split-KV calls;
 - dense bf16: 2^20 + 77 tokens, through the plain, split-KV and in-place stream calls.
 
 The dense bf16 length is 16 times the longest workload on the pages (66048 tokens) and an
@@ -23,6 +24,7 @@ import test_gpu_fwd_bf16
 import test_gpu_fwd_streams
 import test_gpu_sparse
 import test_gpu_splitkv
+from _common import with_split_tile_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -45,8 +47,9 @@ def test_bf16_longest_splitkv():
     w = LONG_BF16
     n = ja.load().joint_attn_fwd_bf16_splitkv_suggest(w.B, w.H, w.N, w.D)
     n = n if n > 1 else 5
-    sel = _sample(w, 48, 5)
-    print("bf16 split-KV N", w.N, "split", n, flush=True)
+    sel, n_in = with_split_tile_rows(w, _sample(w, 48, 5), "bf16", n_rows=48, seed=5)
+    print("bf16 split-KV N %d split %d: %d of %d compared rows in split tiles"
+          % (w.N, n, n_in, len(sel)), flush=True)
     test_gpu_splitkv._assert("split-KV N=%d split %d" % (w.N, n),
                              *test_gpu_splitkv._run(w, n, sel)[:4])
 
@@ -72,15 +75,19 @@ def test_sparse_longest():
 @pytest.mark.parametrize("mode", [0, 1])
 def test_fp8_longest(mode, split_kv):
     w = synth.custom("long_fp8", B=1, H=1, D=128,
-                     stream_lens=(512, ja.JA_REPAIR_MAX_N - 45 - 512), outliers=4, seed=103)
+                     stream_lens=(512, ja.JA_REPAIR_MAX_N - 301 - 512), outliers=4, seed=103)
     n = None
+    sel = _sample(w, 64, 8)
     if split_kv:
         n = ja.load().joint_attn_fwd_fp8_splitkv_suggest(w.B, w.H, w.N, w.D, mode)
         n = n if n > 1 else 5
-    sel = _sample(w, 64, 8)
+        sel, n_in = with_split_tile_rows(w, sel, "fp8", n_rows=48, seed=8)
+        print("fp8 N %d: %d of %d compared rows in split tiles" % (w.N, n_in, len(sel)),
+              flush=True)
+        assert n_in > 0
     print("fp8 N", w.N, "mode", mode, "split", n, flush=True)
     test_gpu_fp8._assert_fp8("fp8 N=%d split %s" % (w.N, n), mode,
-                             *test_gpu_fp8._fwd_fp8(w, mode, sel, n_split=n))
+                             *test_gpu_fp8._fwd_fp8(w, mode, sel, n_split=n), outliers=True)
 
 
 def test_repair_longest():
@@ -96,4 +103,4 @@ def test_repair_longest():
     print("repair N", w.N, "rows", len(sel), flush=True)
     c = test_gpu_fp8_repair._compare(w, 0.005, sel)
     assert c["n"] == 656 and c["rep_row"].sum() >= len(extra)
-    test_gpu_fp8_repair._assert_repair("repair N=%d" % w.N, c)
+    test_gpu_fp8_repair._assert_repair("repair N=%d" % w.N, c, outliers=True)

@@ -9,7 +9,8 @@ import oracle
 from joint_attention_amd import synth
 
 from _common import (BF16_MAX_ABS, BF16_REL_F, device_packed, from_device_bf16, gather_rows,
-                     host_streams, max_abs, packed_host, rel_frobenius, widen_bf16)
+                     host_streams, max_abs, packed_host, rel_frobenius, widen_bf16,
+                     with_split_tile_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +70,12 @@ def test_splitkv_full_size(shape):
     # the suggested split, or 5 where the library suggests none (all tiles then split)
     n = ja.load().joint_attn_fwd_bf16_splitkv_suggest(w.B, w.H, w.N, w.D)
     n = n if n > 1 else 5
+    # random rows of 4 slices, plus rows of the last round's tiles: the ones cut into key
+    # ranges and merged (at 2048^2: slice (1, 22) from row 9216 on and all of (1, 23))
     sel = synth.row_sample(w, 256, seed=23, n_pairs=min(4, w.B * w.H))
+    sel, n_in = with_split_tile_rows(w, sel, "bf16", n_rows=160, seed=23)
+    print("%s: %d of %d compared rows in split tiles" % (shape, n_in, len(sel)), flush=True)
+    assert n_in > 0
     _assert("%s split %d" % (shape, n), *_run(w, n, sel)[:4])
 
 
