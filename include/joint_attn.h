@@ -51,6 +51,7 @@ extern "C" {
 #define JA_EINVAL 1        /* NULL pointer, non-positive size, inconsistent sizes, overflow */
 #define JA_EUNSUPPORTED 2  /* head size not 64/128, misaligned pointer, too many streams */
 #define JA_EHIP 3          /* the HIP runtime refused a launch; see joint_attn_last_hip_error */
+#define JA_ESCRATCH 4      /* more scratch than JA_SCRATCH_BYTES (joint_attn_fwd_bf16_splitkv_noalloc) */
 
 #define JA_LAYOUT_BHND 0
 #define JA_LAYOUT_BHDN 1
@@ -69,6 +70,8 @@ extern "C" {
 
 #define JA_REPAIR_MAX_N 131072    /* longest sequence of joint_attn_fwd_fp8_repair */
 #define JA_REPAIR_TILE 64         /* v8t_sel row pitch: n_repair rounded up to this */
+
+#define JA_SCRATCH_BYTES (64 << 20)  /* static scratch of joint_attn_fwd_bf16_splitkv_noalloc, per device */
 
 /* Human-readable name of a status code (static string). */
 const char *joint_attn_strerror(int status);
@@ -165,6 +168,30 @@ int joint_attn_fwd_bf16_splitkv(const void *q, const void *k, const void *vt,
                                 float softmax_scale, int n_split,
                                 void *workspace, int64_t workspace_bytes,
                                 void *o, float *lse, void *stream);
+
+/*
+ * joint_attn_fwd_bf16_splitkv_noalloc -- joint_attn_fwd_bf16_splitkv without a workspace
+ * argument and without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The partial results go to a static scratch array of JA_SCRATCH_BYTES inside the
+ * library instead: each GPU the library runs on holds one (until the process ends),
+ * looked up on the first call on that GPU.  Same operation, layouts, arguments, results
+ * (bit for bit) and errors as joint_attn_fwd_bf16_splitkv, plus:
+ *   JA_ESCRATCH  the split tiles' partials do not fit: tail * min(n_split, ceil(N/32))
+ *                * rows * (D + 1) * 4 bytes > JA_SCRATCH_BYTES, where tail = the query
+ *                tiles of the last, partial round (B*H*ceil(N/rows) modulo the
+ *                workgroups resident at once, rows = 256 at D = 128, 128 at D = 64).
+ *                2048x2048 T2I at the suggested split (5) needs 63.4 MB.  Nothing is
+ *                launched; the workspace variant takes any size.
+ * Every call on one GPU shares that GPU's scratch array: calls that overlap on one GPU
+ * (on different streams, or from several host threads) race and must not be issued;
+ * calls ordered on one stream are safe.  No state needs clearing between calls (every
+ * partial a call reads was written by that call).
+ */
+int joint_attn_fwd_bf16_splitkv_noalloc(const void *q, const void *k, const void *vt,
+                                        int B, int H, int64_t N, int D, int64_t ldv,
+                                        float softmax_scale, int n_split,
+                                        void *o, float *lse, void *stream);
 
 /*
  * joint_attn_fwd_bf16_streams -- the same attention as joint_attn_fwd_bf16, reading Q, K

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 # JOINT_ATTN_LIB overrides the shared object (e.g. an alternative build of the kernels)
 LIB_PATH = os.environ.get("JOINT_ATTN_LIB") or os.path.join(HERE, "libjoint_attn.so")
 
-JA_OK, JA_EINVAL, JA_EUNSUPPORTED, JA_EHIP = 0, 1, 2, 3
+JA_OK, JA_EINVAL, JA_EUNSUPPORTED, JA_EHIP, JA_ESCRATCH = 0, 1, 2, 3, 4
 JA_LAYOUT_BHND, JA_LAYOUT_BHDN = 0, 1
 JA_MAX_STREAMS = 16
 JA_MAX_HEAD_ELEMS = 1 << 30
@@ -26,11 +26,12 @@ JA_SPARSE_BLOCK, JA_SPARSE_MAX_N = 128, 131072
 JA_FP8_PLAIN, JA_FP8_SPLIT, JA_FP8_REPAIR = 0, 1, 2
 JA_REPAIR_MAX_N = 131072
 JA_REPAIR_TILE = 64
+JA_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
            "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse",
            "joint_attn_fwd_bf16_splitkv", "joint_attn_fwd_bf16_splitkv_workspace",
-           "joint_attn_fwd_bf16_splitkv_suggest",
+           "joint_attn_fwd_bf16_splitkv_suggest", "joint_attn_fwd_bf16_splitkv_noalloc",
            "joint_attn_fwd_bf16_streams",
            "joint_attn_quant_fp8", "joint_attn_quant_fp8_streams",
            "joint_attn_fwd_fp8", "joint_attn_fwd_fp8_splitkv", "joint_attn_fwd_fp8_splitkv_workspace",
@@ -60,6 +61,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         if not os.path.exists(path):
             raise RuntimeError("libjoint_attn.so is not built (%s); run "
                                "`python -m joint_attention_amd.build`" % path)
+        # torch first: it ships its own HIP runtime under the same soname as the system's,
+        # and the first one loaded serves the whole process (the library's dependency
+        # resolved first would leave torch without a usable runtime)
+        import torch  # noqa: F401
         h = ctypes.CDLL(path)
         P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
         h.joint_attn_strerror.restype = ctypes.c_char_p
@@ -81,6 +86,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_fwd_bf16_splitkv.restype = I
         h.joint_attn_fwd_bf16_splitkv.argtypes = [P, P, P, I, I, I64, I, I64, F, I, P, I64, P, P,
                                                   P]
+        h.joint_attn_fwd_bf16_splitkv_noalloc.restype = I
+        h.joint_attn_fwd_bf16_splitkv_noalloc.argtypes = [P, P, P, I, I, I64, I, I64, F, I, P, P,
+                                                          P]
         h.joint_attn_fwd_bf16_streams.restype = I
         h.joint_attn_fwd_bf16_streams.argtypes = [I, P, P, P, P, I, I, I, F,
                                                   P, P, P, P]
@@ -263,6 +271,33 @@ def joint_attn_fwd_bf16_splitkv(q, k, vt, softmax_scale: float | None = None,
                                          out.data_ptr(), _ptr(lse), _stream(q))
     _check("joint_attn_fwd_bf16_splitkv", st)
     return (out, lse) if return_lse else out
+
+
+def joint_attn_fwd_bf16_splitkv_noalloc(q, k, vt, softmax_scale: float | None = None,
+                                        n_split: int | None = None, out=None, lse=None):
+    """joint_attn_fwd_bf16_splitkv with the partial results in the library's static scratch
+    (no workspace; the library allocates nothing).  Pass `out` (and `lse`, fp32
+    [B, H, N], if wanted) to allocate nothing here either."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, N, D = q.shape
+    if tuple(k.shape) != (B, H, N, D) or vt.shape[:3] != (B, H, D):
+        raise ValueError("k must match q; vt must be [B, H, D, ldv]")
+    lib = load()
+    if n_split is None:
+        n_split = lib.joint_attn_fwd_bf16_splitkv_suggest(B, H, N, D)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out", 4)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", 3)
+    st = lib.joint_attn_fwd_bf16_splitkv_noalloc(q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H,
+                                                 N, D, int(vt.shape[3]), scale, int(n_split),
+                                                 out.data_ptr(), _ptr(lse), _stream(q))
+    _check("joint_attn_fwd_bf16_splitkv_noalloc", st)
+    return out
 
 
 def joint_attn_fwd_bf16_streams(q_streams, k_streams, v_streams,

@@ -43,6 +43,7 @@
 // cross-lane step and the rescale of O are rare; the numerators stay below 2^16.  The row
 // sum accumulates the bf16-rounded numerators with v_dot2 (the same values that
 // enter P V).
+#include <mutex>
 #include <type_traits>
 
 #include "ja_device.h"
@@ -887,6 +888,52 @@ hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt,
     using I4 = std::integral_constant<int, 4>;
     using INW = std::integral_constant<int, FWD_NW>;
     return D == 64 ? go(I64{}, I4{}) : go(I128{}, INW{});
+}
+
+// ---- allocation-free split-KV: the partial outputs and log-sum-exps live in this
+//      file-scope device array instead of a caller workspace.  Every device the library
+//      runs on holds its own copy (until the process ends) at its own address, looked up
+//      once per device with that device current; host code passes that address to the
+//      kernels, never the array's name (whose host-side value is only a stand-in).
+namespace {
+static __device__ __align__(256) float scratch[JA_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_fwd_bf16_splitkv_noalloc(const void* q, const void* k, const void* vt, int B,
+                                           int H, int N, int D, int64_t ldv, float softmax_scale,
+                                           int n_split, int slots, int64_t parts, void* o,
+                                           float* lse, hipStream_t stream) {
+    // parts = split tiles x key ranges, checked by the caller against JA_SCRATCH_BYTES:
+    // O partials [parts][rows][D], then lse partials [parts][rows]
+    void* base = nullptr;
+    if (parts > 0) {
+        const hipError_t e = scratch_address(&base);
+        if (e != hipSuccess) return e;
+    }
+    float* o_part = static_cast<float*>(base);
+    float* lse_part = parts > 0 ? o_part + parts * splitkv_rows_per_tile(D) * D : nullptr;
+    return launch_fwd_bf16_splitkv(q, k, vt, B, H, N, D, ldv, softmax_scale, n_split, slots,
+                                   o_part, lse_part, o, lse, stream);
 }
 
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,

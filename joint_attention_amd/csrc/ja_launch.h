@@ -41,6 +41,13 @@ hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt,
                                    int slots, float* o_part, float* lse_part, void* o,
                                    float* lse, hipStream_t stream);
 
+// the same with the partial results in the library's static per-device scratch array
+// (parts = split tiles x key ranges, within JA_SCRATCH_BYTES; 0 runs the plain forward)
+hipError_t launch_fwd_bf16_splitkv_noalloc(const void* q, const void* k, const void* vt, int B,
+                                           int H, int N, int D, int64_t ldv, float softmax_scale,
+                                           int n_split, int slots, int64_t parts, void* o,
+                                           float* lse, hipStream_t stream);
+
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,
                                    float softmax_scale, void* o, float* lse,
                                    hipStream_t stream);

@@ -105,6 +105,9 @@ const char* joint_attn_strerror(int status) {
         case JA_EINVAL: return "invalid argument";
         case JA_EUNSUPPORTED: return "unsupported argument (head size, alignment, stream count or mode)";
         case JA_EHIP: return "HIP runtime error";
+        case JA_ESCRATCH:
+            return "partial results larger than the static scratch buffer (JA_SCRATCH_BYTES); "
+                   "use joint_attn_fwd_bf16_splitkv with a workspace, or a smaller n_split";
         default: return "unknown status";
     }
 }
@@ -235,6 +238,32 @@ int joint_attn_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, in
     JA_LAUNCH(ja::launch_fwd_bf16_splitkv(q, k, vt, B, H, (int)N, D, ldv, softmax_scale,
                                           n_split, slots, o_part, lse_part, o, lse,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int joint_attn_fwd_bf16_splitkv_noalloc(const void* q, const void* k, const void* vt, int B,
+                                        int H, int64_t N, int D, int64_t ldv,
+                                        float softmax_scale, int n_split, void* o, float* lse,
+                                        void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (n_split <= 0 || n_split > 64) return JA_EINVAL;
+    if (N == 0) return JA_OK;
+    if (!q || !k || !vt || !o) return JA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o))
+        return JA_EUNSUPPORTED;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
+    // the split tiles are those of the last, partial round (as in the workspace variant);
+    // each of their key ranges needs rows * (D + 1) floats of scratch
+    const int slots = ja::splitkv_slots(D);
+    const int64_t br = ja::splitkv_rows_per_tile(D);
+    const int64_t ranges = std::min<int64_t>(n_split, (N + 31) / 32);
+    const int64_t tail = (N + br - 1) / br * B * H % slots;
+    const int64_t parts = (ranges <= 1 || tail == 0) ? 0 : tail * ranges;
+    if (parts * br * (D + 1) * (int64_t)sizeof(float) > JA_SCRATCH_BYTES) return JA_ESCRATCH;
+    JA_LAUNCH(ja::launch_fwd_bf16_splitkv_noalloc(q, k, vt, B, H, (int)N, D, ldv, softmax_scale,
+                                                  n_split, slots, parts, o, lse,
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 int joint_attn_fwd_bf16_streams(int n_streams, const void* const* q, const void* const* k,

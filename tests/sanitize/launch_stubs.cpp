@@ -69,6 +69,16 @@ hipError_t launch_fwd_bf16_splitkv(const void*, const void*, const void*, int B,
     return shape_ok(B, H, N, D);
 }
 
+hipError_t launch_fwd_bf16_splitkv_noalloc(const void*, const void*, const void*, int B, int H,
+                                           int N, int D, int64_t ldv, float, int n_split,
+                                           int slots, int64_t parts, void*, float*, hipStream_t) {
+    const int64_t bytes = parts * splitkv_rows_per_tile(D) * (D + 1) * (int64_t)sizeof(float);
+    if (n_split < 1 || slots != splitkv_slots(D) || parts < 0 || bytes > JA_SCRATCH_BYTES ||
+        ldv < N)
+        return hipErrorInvalidValue;
+    return shape_ok(B, H, N, D);
+}
+
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D, float,
                                    void* o, float*, hipStream_t) {
     if (!o) return hipErrorInvalidValue;

@@ -279,6 +279,8 @@ def test_launch_failure_is_reported(lib, monkeypatch):
             fake, fake, fake, 1, 2, N, 128, ldv, fake, 0.1, fake, None, None),
         "fwd_bf16_splitkv": lambda: lib.joint_attn_fwd_bf16_splitkv(
             fake, fake, fake, 1, 2, N, 128, ldv, 0.1, 2, fake, ws_bf, fake, None, None),
+        "fwd_bf16_splitkv_noalloc": lambda: lib.joint_attn_fwd_bf16_splitkv_noalloc(
+            fake, fake, fake, 1, 2, N, 128, ldv, 0.1, 2, fake, None, None),
         "fwd_bf16_streams": lambda: lib.joint_attn_fwd_bf16_streams(
             2, two, two, two, lens, 1, 2, 128, 0.1, fake, None, offs, None),
         "quant_fp8": lambda: lib.joint_attn_quant_fp8(
@@ -338,6 +340,9 @@ def test_valid_calls_reach_the_launchers(lib, monkeypatch):
                 assert lib.joint_attn_fwd_fp8_splitkv(
                     fake, fake, fake, fake, fake, fake, B, H, N, D, ldv, 0.1, mode, fake, fake,
                     n_split, fake, ws8, fake, None, None) == 0
+        for n_split in (1, 2, 5):
+            assert lib.joint_attn_fwd_bf16_splitkv_noalloc(fake, fake, fake, B, H, N, D, ldv, 0.1,
+                                                           n_split, fake, fake, None) == 0
         assert lib.joint_attn_fwd_bf16_streams(2, two, two, two, lens, B, H, D, 0.1, fake,
                                                None, offs, None) == 0
         for mode in (0, 1):
@@ -358,3 +363,29 @@ def test_valid_calls_reach_the_launchers(lib, monkeypatch):
                                              fake, None) == 0
         assert lib.joint_attn_fwd_bf16_sparse(fake, fake, fake, B, H, N, D, ldv, fake, 0.1,
                                               fake, None, None) == 0
+
+
+def test_noalloc_validation(lib):
+    # the allocation-free split-KV call: the usual argument checks, and partials beyond the
+    # static scratch rejected before anything is launched (256 slots without a GPU)
+    fake = 0x10000
+    f = lib.joint_attn_fwd_bf16_splitkv_noalloc
+    assert f(fake, fake, fake, 1, 2, 64, 96, 64, 0.1, 2, fake, None, None) == 2        # D
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 0, fake, None, None) == 1       # n_split
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 65, fake, None, None) == 1
+    assert f(None, fake, fake, 1, 2, 64, 128, 64, 0.1, 2, fake, None, None) == 1
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, 0.1, 2, fake + 8, None, None) == 2
+    assert f(None, None, None, 1, 2, 0, 128, 0, 0.1, 2, None, None, None) == 0        # N == 0
+    # one GPU's share of a 4-way head split of 2048^2: 140 split tiles x 7 ranges x 256 rows
+    # x 129 floats = 129 MB > JA_SCRATCH_BYTES
+    assert f(fake, fake, fake, 1, 6, 16896, 128, 16896, 0.1, 7, fake, None, None) == 4
+    assert b"scratch" in lib.joint_attn_strerror(4)
+    # 2048^2 T2I at the suggested split: 96 x 5 x 256 x 129 x 4 = 63.4 MB fits (reaches the
+    # launch: the failure hook stands in for it here)
+    import os
+    os.environ["JOINT_ATTN_SIMULATE_HIP_ERROR"] = "98"
+    try:
+        assert f(fake, fake, fake, 2, 24, 16896, 128, 16896, 0.1, 5, fake, None, None) == 3
+        assert 96 * 5 * 256 * 129 * 4 <= _abi.JA_SCRATCH_BYTES
+    finally:
+        del os.environ["JOINT_ATTN_SIMULATE_HIP_ERROR"]
