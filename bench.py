@@ -78,6 +78,113 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock (the starred level of the kernel driver's
+    pp_dpm_sclk) every `period` seconds in a background thread.  Reports None where the
+    file is missing.  (amdsmi's gpu_metrics refreshes about once a second.)"""
+
+    def __init__(self, period: float = 0.005):
+        import threading
+        self.period, self.samples, self.err = period, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        self.path = self._find()
+
+    def _find(self):
+        import glob
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if len(cards) > 1:
+            try:                                   # the card torch's device 0 sits on
+                import torch
+                bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+                if bus is not None:
+                    cards = [c for c in cards
+                             if os.path.realpath(os.path.dirname(c)).endswith(":%02x:00.0" % bus)]
+            except Exception as e:
+                self.err = repr(e)
+        if len(cards) != 1:
+            self.err = self.err or "pp_dpm_sclk: %d candidate files" % len(cards)
+            return None
+        return cards[0]
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if "*" in line:
+                    mhz = line.split(":", 1)[1].strip().rstrip("*").strip()
+                    return float(mhz.lower().replace("mhz", ""))
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None and v > 0:
+                    self.samples.append(v)
+            except Exception as e:
+                self.err = repr(e)
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self.path is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def result(self):
+        if not self.samples:
+            return {"clock_ghz": None, "clock_source": "unavailable (%s)" % self.err}
+        import statistics
+        return {"clock_ghz": round(statistics.fmean(self.samples) / 1000.0, 4),
+                "clock_ghz_min": round(min(self.samples) / 1000.0, 4),
+                "clock_ghz_max": round(max(self.samples) / 1000.0, 4),
+                "clock_samples": len(self.samples),
+                "clock_source": "%s (current level), sampled every %d ms"
+                                % (self.path, int(self.period * 1000))}
+
+
+def sustained_clock(step, ms_per_step: float, seconds: float = 1.0, settle: float = 0.3):
+    import torch
+    n = int((settle + seconds + 0.3) * 1000.0 / max(ms_per_step, 0.05)) + 1
+    for _ in range(n):                 # queued: the GPU runs them back to back
+        step(False)
+    time.sleep(settle)
+    sampler = ClockSampler()
+    with sampler:
+        time.sleep(seconds)
+    torch.cuda.synchronize()
+    r = sampler.result()
+    r["clock_load"] = "%d untimed steps queued back to back; sampled after %.1f s for %.1f s" % (
+        n, settle, seconds)
+    return r
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def device_name() -> str:
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return "%s (%s, %d CUs)" % (p.name, getattr(p, "gcnArchName", "?"), p.multi_processor_count)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,14 +215,15 @@ def cpu_baseline(w, host, target_s: float):
     n = int(max(256, min(200000, 256 * target_s / max(t_probe, 1e-6))))
     sel = synth.row_sample(w, n, seed=8)
     t0 = time.perf_counter()
-    oracle.attention_rows(qh, kh, vh, scale, sel, threads)
+    ref, _ = oracle.attention_rows(qh, kh, vh, scale, sel, threads)
     dt = time.perf_counter() - t0
     flops = 4.0 * w.N * w.D * len(sel)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "%d query rows (every row near a stream boundary + random rows, "
                       "row_sample seed 8) of %s: B=%d H=%d N=%d D=%d, fp64, %.1f s"
                       % (len(sel), w.name, w.B, w.H, w.N, w.D, dt),
-            "seconds": dt}
+            "seconds": dt, "rows": sel, "ref": ref}
 
 
 def main():
@@ -206,6 +314,7 @@ def main():
     log("timing bf16 path (split-KV, n_split %d): %d warmup + %d steps"
         % (ns_main, args.warmup, args.steps))
     wall, durs = timed(step_bf16, args.steps, args.warmup)
+    o_timed = o.clone()            # the timed step's output, compared with the oracle below
     ms_step = wall * 1e3 / args.steps
     pack_ms, fwd_ms = durs.mean(axis=0)
     flops = float(w.flops)
@@ -231,7 +340,15 @@ def main():
         "kernels_ms": {"pack_qkv": round(float(pack_ms), 4),
                        "fwd_bf16_splitkv": round(float(fwd_ms), 4)},
         "pct_of_bf16_peak_step": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "device": device_name(),
     }
+    # the shader clock under this load: the same step queued for ~1.6 s (untimed); the
+    # driver's current clock level is sampled for 1 s after a 0.3 s settle
+    out.update(sustained_clock(step_bf16, ms_step))
+    if out.get("clock_ghz"):
+        # the dense bf16 peak at the clock these steps ran at (4096 flop/clk/CU, 256 CUs)
+        out["roofline"]["frac_of_peak_at_measured_clock"] = round(
+            achieved / (PEAK_BF16_TFLOPS * out["clock_ghz"] / 2.4), 4)
 
     # the same step with the plain forward (every query tile over all keys)
     log("timing bf16 path with the plain forward")
@@ -293,6 +410,7 @@ def main():
         "speedup_vs_dense": round(fwd_p / sp_ms, 3),
     }
 
+    fp8_outputs = {}
     if not args.skip_fp8:
         out["fp8"] = {}
         for mode, name in ((ja.JA_FP8_SPLIT, "split"), (ja.JA_FP8_PLAIN, "plain")):
@@ -322,6 +440,7 @@ def main():
 
             log("timing fp8 path, mode %d (%s), split-KV n_split %d" % (mode, name, ns8))
             wall8, durs8 = timed(step_fp8, args.steps, args.warmup)
+            fp8_outputs[name] = o.clone()
             ms8 = wall8 * 1e3 / args.steps
             p8, qn8, f8 = durs8.mean(axis=0)
 
@@ -492,9 +611,39 @@ def main():
         vh, _ = oracle.pack_tokens(st.v)
         cb = cpu_baseline(w, (qh, kh, vh), args.cpu_seconds)
         cb.pop("seconds")
+        rows, ref = cb.pop("rows"), cb.pop("ref")
         out["cpu_baseline"] = {k2: (round(v2, 6) if isinstance(v2, float) else v2)
                                for k2, v2 in cb.items()}
+
+        # parity of the timed steps' outputs on the same oracle rows (bf16 bar: rel_F <=
+        # 5e-3, max|err| <= 2e-2; fp8 against the unquantised fp64 oracle: rel_F <= 5e-2
+        # for the split mode, the plain mode's recipe loss reported)
+        def rows_of(t):
+            bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+            bits = bits[rows[:, 0], rows[:, 2], rows[:, 1], :]
+            return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+        def parity(t):
+            got = rows_of(t)
+            return {"rows": int(len(rows)),
+                    "rel_F": float("%.4g" % (np.linalg.norm(got - ref) / np.linalg.norm(ref))),
+                    "max_abs_err": float("%.4g" % np.abs(got - ref).max())}
+        out["parity"] = {"reference": "fp64 oracle, the cpu_baseline rows",
+                         "bf16_step": parity(o_timed)}
+        out["parity"]["bf16_step"]["within_bar"] = bool(
+            out["parity"]["bf16_step"]["rel_F"] <= 5e-3 and
+            out["parity"]["bf16_step"]["max_abs_err"] <= 2e-2)
+        for name, t in fp8_outputs.items():
+            out["parity"]["fp8_%s_step" % name] = parity(t)
     print(json.dumps(out), flush=True)
+    try:                       # anything this process started that is still alive
+        import psutil
+        kids = psutil.Process().children(recursive=True)
+        if kids:
+            log("child processes still alive at exit: %s"
+                % ", ".join("%d %s" % (c.pid, " ".join(c.cmdline()[:4])) for c in kids))
+    except Exception as e:
+        log("child-process check failed: %r" % (e,))
 
 
 if __name__ == "__main__":

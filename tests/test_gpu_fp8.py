@@ -193,7 +193,10 @@ def _assert_fp8(tag, mode, got, ref8, ref64, got_lse, lse8, flip, *, outliers: b
         assert ma <= FP8_PLAIN_MAX_ABS, (tag, ma)
     bar_f = FP8_REL_F if tight else FP8_PLAIN_REL_F
     assert vs64 <= recipe + bar_f, (tag, vs64, recipe)
-    if mode == 1:
+    if mode == 1 and outliers:
+        # the fp8 bar against fp64 is the outlier workloads' (2048^2 inputs); without
+        # outliers e4m3's own rounding of the inputs is already about that large, and the
+        # kernel is held to its fp8 reference above
         assert vs64 <= FP8_VS_FP64, (tag, vs64)
     assert lse_err <= 1e-3 * max(1.0, float(np.abs(lse8).max())), (tag, lse_err)
 

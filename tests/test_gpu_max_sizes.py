@@ -90,6 +90,25 @@ def test_fp8_longest(mode, split_kv):
                              *test_gpu_fp8._fwd_fp8(w, mode, sel, n_split=n), outliers=True)
 
 
+@pytest.mark.parametrize("split_kv", [False, True])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_fp8_beyond_one_scale_table(mode, split_kv):
+    # more than 2048 K scale blocks (the fp8 forward's LDS table of block scales is
+    # refilled on the way): 2048 * 128 + 12345 keys, ragged last tile
+    w = synth.custom("long_fp8_tab", B=1, H=1, D=128, stream_lens=(512, 2048 * 128 + 12345 - 512),
+                     outliers=4, seed=105)
+    n = None
+    sel = _sample(w, 48, 10)
+    if split_kv:
+        n = ja.load().joint_attn_fwd_fp8_splitkv_suggest(w.B, w.H, w.N, w.D, mode)
+        n = n if n > 1 else 5
+        sel, n_in = with_split_tile_rows(w, sel, "fp8", n_rows=32, seed=10)
+        assert n_in > 0
+    print("fp8 N", w.N, "mode", mode, "split", n, flush=True)
+    test_gpu_fp8._assert_fp8("fp8 N=%d split %s" % (w.N, n), mode,
+                             *test_gpu_fp8._fwd_fp8(w, mode, sel, n_split=n), outliers=True)
+
+
 def test_repair_longest():
     w = synth.custom("long_rep", B=1, H=1, D=128,
                      stream_lens=(512, ja.JA_REPAIR_MAX_N - 512), outliers=4, seed=104)
