@@ -30,12 +30,14 @@
 // the matrix cores run P(j-1) V(j-1) and Q K(j+1)^T; the three are independent, and
 // the loop body is written as an explicit sequence of steps (one LDS operand read, one
 // or two MFMAs and a slice of the softmax each) separated by scheduling fences.  K and
-// V^T tiles are double-buffered in LDS; each lane stages one 16-byte chunk per tile in
-// registers a full iteration ahead and writes it to LDS after the iteration's single
-// barrier (direct global->LDS loads would force every LDS-operand wait to drain them).
-// Chunks are XOR-swizzled by row so that the 16-byte operand reads of 16 consecutive
-// lanes (16 different rows) hit distinct banks; the swizzle is applied on the global
-// side of the loads, so each LDS store is a linear 16-byte write.
+// V^T tiles are double-buffered in LDS with one barrier per iteration.  The packed
+// variants load them straight from HBM into LDS (global_load_lds_dwordx4, issued after
+// the barrier that frees the slot); the stream gather stages K and a token-major V
+// tile in registers one iteration ahead, writes K linearly and transposes V through LDS.
+// Chunks are XOR-swizzled by row so that every LDS access is conflict-free on gfx950
+// (a read serves 256 bytes per clock: 16 lanes of a 16-byte read; a write 128 bytes: 8
+// lanes of a 16-byte write); for the loaded tiles the swizzle is applied on the global
+// side, so each chunk lands lane-linear.
 //
 // Softmax details.  Scores are scaled to base 2 (c2 = scale * log2 e) in the FMA that
 // subtracts the running offset m.  m is raised (to the exact row maximum, combining the
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     constexpr int NOB = D / 32;                  // 32-channel blocks of the output
     constexpr int VCPR = BC / 8;                 // 16-byte chunks per V^T row
     constexpr int VRPB = 256 / (2 * BC);         // V^T rows per 256 bytes (all 64 banks)
+    static_assert(VCPR >= 4, "the V^T swizzle below uses two chunk bits");
     constexpr int TILE_ELEMS = BC * D;           // bf16 elements of one K or V^T tile
     constexpr int LOADS = TILE_ELEMS * 2 / 1024 / (NTHREADS / 64);   // 1 KB loads per wave
     static_assert(LOADS >= 1, "tile smaller than one load per wave");
@@ -125,6 +128,11 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) __bf16 st0[GATHER ? TILE_ELEMS : 8];
     __shared__ __attribute__((aligned(1024))) __bf16 st1[GATHER ? TILE_ELEMS : 8];
 
+    // V^T rows: 16-byte chunk u of row r sits at chunk u ^ vswz(r).  A 16-byte operand
+    // read serves 16 rows at once (VRPB rows per 256-byte bank line: (r / VRPB) picks
+    // distinct chunks), a 16-byte LDS write 8 rows in a 128-byte window (the (r / 2) bit
+    // separates rows r and r + 2, which share that window's banks)
+    auto vswz = [](int r) { return ((r / VRPB) % VCPR) ^ (((r / 2) & 1) << 1); };
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept scalar
     const int r32 = lane & 31, hh = lane >> 5;
@@ -284,7 +292,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
             // (key / GRPL) % GSEG (conflict-free for the transposing reads)
             return ((off % (2 * D)) / 16) ^ ((((off / (2 * D)) / GRPL) % GSEG) * 4);
         }
-        return ((off % (2 * BC)) / 16) ^ (((off / (2 * BC)) / VRPB) % VCPR);
+        return ((off % (2 * BC)) / 16) ^ vswz(off / (2 * BC));
     };
     uint32_t k_off[LOADS], v_off[LOADS];
 #pragma unroll
@@ -394,7 +402,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     auto transpose_write = [&](const uint4& x, __bf16* vs) {
         const int grp = tid >> 4, i16 = tid & 15;
         const int row = (grp % (D / 16)) * 16 + i16, u = grp / (D / 16);
-        *reinterpret_cast<uint4*>(vs + row * BC + ((u ^ ((row / VRPB) % VCPR)) * 8)) = x;
+        *reinterpret_cast<uint4*>(vs + row * BC + ((u ^ vswz(row)) * 8)) = x;
     };
     auto store_v = [&](__bf16* slot) {
 #pragma unroll
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         const int vrow = ob * 32 + r32;
         const int u = 2 * t + hh;
         return *reinterpret_cast<const bf16x8*>(
-            &vs[vrow * BC + ((u ^ ((vrow / VRPB) % VCPR)) * 8)]);
+            &vs[vrow * BC + ((u ^ vswz(vrow)) * 8)]);
     };
     auto qk_operand = [&](const __bf16* ks, int i) {
         const int c = i / KB, kb = i % KB;

@@ -17,8 +17,10 @@
 // explicit sequence of steps (operand reads a few steps ahead, one MFMA and a slice of
 // the softmax each) separated by scheduling fences.  K, V^T (and the kept channels of
 // the split mode) are staged in registers one iteration ahead and double-buffered in
-// LDS, with one barrier per iteration.  LDS rows are XOR-swizzled so that the operand
-// reads of each lane group hit distinct banks.
+// LDS, with one barrier per iteration.  LDS rows are XOR-swizzled so that each LDS
+// access is conflict-free on gfx950: a read serves 256 bytes per clock (16 lanes of a
+// 16-byte read, 32 of an 8-byte one), a write 128 bytes (8 lanes of a 16-byte write), and
+// the lanes served together must hit distinct 4-byte banks of that window.
 //
 // Softmax.  The running maximum M is an integer (base 2), raised only when some score
 // of the tile exceeds it (a wave-uniform ballot; the two wave halves are combined and O
@@ -342,8 +344,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     constexpr int KRPB = 256 / KROWB;        // K rows per 256-byte line of the 64 LDS banks
     constexpr int NQC = D / 64;              // k-steps of the QK product (64 channels each)
     constexpr int NOB = D / 32;              // 32-channel output blocks
-    constexpr int VU = BC / 8;               // 8-byte units per V^T row
-    constexpr int VRPB = 256 / BC;           // V^T rows per 256-byte line
+    constexpr int VCPR = BC / 16;            // 16-byte chunks per V^T row
     constexpr int HC = JA_HI_CHANNELS;       // kept channels (bf16), 2 x 16 bytes per key
     constexpr int KCH = BC * DC / NTHREADS;  // 16-byte K chunks per thread and tile
     constexpr int VCH = D * (BC / 16) / NTHREADS;
@@ -404,9 +405,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     }
 
     // ---- staging: chunk x = tid + i * NTHREADS of a tile is K row x / DC, 16-byte
-    //      chunk x % DC, and V^T row x / 4, keys 16 (x % 4) ..; threads t < 128 also
-    //      own half a kept-channel row
+    //      chunk x % DC, and V^T row x / 4, keys 16 (x % 4) .. + 15; threads t < 128
+    //      also own half a kept-channel row
     uint4 kst[KCH], vst[VCH], hst = make_uint4(0, 0, 0, 0);
+    // V^T in LDS: chunk c = 2 hh + jj of row vr holds the keys that lane half hh feeds
+    // to the PV product as its 16-byte piece jj, keys 32 jj + 8 hh + (0..7) and 32 jj +
+    // 16 + 8 hh + (0..7), so an operand is two 16-byte reads; it sits at chunk
+    // c ^ vswz(vr).  The 16 lanes of such a read (16 rows, four per 256-byte bank line)
+    // then meet four distinct swizzles, and the 16 lanes of an 8-byte staging write (rows
+    // vr .. vr + 3 in a 128-byte window) put rows vr and vr + 2 in different chunks.
+    auto vswz = [](int r) { return ((r / 4) % VCPR) ^ (((r / 2) & 1) << 1); };
     auto load_k = [&](int kt) {
         const int k0 = (t_begin + kt) * BC;
 #pragma unroll
@@ -422,25 +430,37 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
                 hst = *reinterpret_cast<const uint4*>(KHbh + (int64_t)hkey * HC + (tid % 2) * 8);
         }
     };
+    // 8 bytes of V^T row vr from key `key` (a multiple of 8): keys at or past N read as zero
+    auto v_piece = [&](int vr, int key) {
+        uint2 piece = make_uint2(0, 0);
+        if (key < N) {
+            // key < N, key % 8 == 0 and ldv % 16 == 0 keep the 8 bytes in the row
+            const uint2 v = *reinterpret_cast<const uint2*>(Vbh + (int64_t)vr * ldv + key);
+            uint32_t wv[2] = {v.x, v.y};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (key + e >= N) wv[e / 4] &= ~(0xFFu << (8 * (e % 4)));
+            piece = make_uint2(wv[0], wv[1]);
+        }
+        return piece;
+    };
     auto load_v = [&](int kt) {
+        const int k0 = (t_begin + kt) * BC;
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
-            const int x = tid + i * NTHREADS, vr = x / (BC / 16), vj = x % (BC / 16);
-            const int key = (t_begin + kt) * BC + 16 * vj;
-            if (key + 16 <= N) {
-                vst[i] = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
+            const int x = tid + i * NTHREADS, vr = x / VCPR, c = x % VCPR;
+            // keys 16 c .. 16 c + 15: the pieces of chunks (jj = c / 2, hh = 0 and 1)
+            const int key0 = k0 + 16 * c;
+            uint2 p0, p1;
+            if (key0 + 16 <= N) {
+                const uint4 v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key0);
+                p0 = make_uint2(v.x, v.y);
+                p1 = make_uint2(v.z, v.w);
             } else {
-                vst[i] = make_uint4(0, 0, 0, 0);
-                if (key < N) {
-                    // key < N, key % 16 == 0 and ldv % 16 == 0 keep the 16 bytes in the row
-                    uint4 v = *reinterpret_cast<const uint4*>(Vbh + (int64_t)vr * ldv + key);
-                    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (key + e >= N) wv[e / 4] &= ~(0xFFu << (8 * (e % 4)));
-                    vst[i] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                }
+                p0 = v_piece(vr, key0);
+                p1 = v_piece(vr, key0 + 8);
             }
+            vst[i] = make_uint4(p0.x, p0.y, p1.x, p1.y);
         }
     };
     auto store_k = [&](int slot) {
@@ -456,17 +476,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
         }
     };
     auto store_v = [&](int slot) {
-        // 16 keys of channel vr as two 8-byte units, so that lane half hh later finds
-        // its keys {16 u + 8 hh + e} as unit 2u + hh of the row
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
-            const int x = tid + i * NTHREADS, vr = x / (BC / 16), vj = x % (BC / 16);
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int unit = (2 * vj + half) ^ ((vr / VRPB) % VU);
-                *reinterpret_cast<uint2*>(&sv[slot][vr * BC + unit * 8]) =
-                    half ? make_uint2(vst[i].z, vst[i].w) : make_uint2(vst[i].x, vst[i].y);
-            }
+            const int x = tid + i * NTHREADS, vr = x / VCPR, c = x % VCPR;
+            // keys 16 c ..: half 0 -> chunk (hh 0, jj c / 2), half 1 -> chunk (hh 1, jj c / 2),
+            // each at byte 8 (c % 2) of the chunk
+            uint8_t* row = &sv[slot][vr * BC + 8 * (c % 2)];
+            *reinterpret_cast<uint2*>(row + ((c / 2) ^ vswz(vr)) * 16) = make_uint2(vst[i].x, vst[i].y);
+            *reinterpret_cast<uint2*>(row + ((2 + c / 2) ^ vswz(vr)) * 16) =
+                make_uint2(vst[i].z, vst[i].w);
         }
     };
 
@@ -501,16 +519,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     constexpr int NHI = HI ? KB : 0;
     constexpr int NQ = NQK + NHI;
     auto pv_operand = [&](int slot, int i) {
-        const int vrow = i * 32 + r32;
-        intx8 av;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int unit = (2 * u + hh) ^ ((vrow / VRPB) % VU);
-            const uint2 x = *reinterpret_cast<const uint2*>(&sv[slot][vrow * BC + unit * 8]);
-            av[2 * u] = (int)x.x;
-            av[2 * u + 1] = (int)x.y;
-        }
-        return av;
+        // lane half hh: keys {16 u + 8 hh + (0..7)}, u = 0..3, as chunks 2 hh and 2 hh + 1
+        const int vrow = i * 32 + r32, z = vswz(vrow);
+        const uint4 x0 = *reinterpret_cast<const uint4*>(&sv[slot][vrow * BC + (((2 * hh) ^ z) * 16)]);
+        const uint4 x1 =
+            *reinterpret_cast<const uint4*>(&sv[slot][vrow * BC + (((2 * hh + 1) ^ z) * 16)]);
+        return intx8{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     };
     auto q_operand = [&](int slot, int i) {
         intx8 av;
