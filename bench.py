@@ -12,8 +12,11 @@ with the library's suggested split (the query tiles of the last, partial round o
 workgroups split into key ranges; workspace allocated before timing).  The same step with
 the plain joint_attn_fwd_bf16 is reported under "plain_bf16".
 The same attention through joint_attn_fwd_bf16_streams (streams read in place, no pack)
-is timed in its own loop and reported under "fused_bf16"; the block-sparse forward with a
-structured block mask under "sparse_bf16".
+is timed in its own loop and reported under "fused_bf16", and through
+joint_attn_fwd_bf16_streams_splitkv (Q and K in place; V^T packed inside the call, or V in
+place too) under "fused_bf16_splitkv" and "fused_bf16_splitkv_inplace", each checked to
+equal the timed step's output bit for bit; the block-sparse forward with a structured block
+mask under "sparse_bf16".
 The fp8 path (pack x3 -> joint_attn_quant_fp8 -> joint_attn_fwd_fp8_splitkv, the plain
 joint_attn_fwd_fp8 timed beside it) on the same inputs is timed the same way in its own
 loop and reported under "fp8", for both modes, from the streams, and with token repair
@@ -384,6 +387,39 @@ def main():
         "frac_of_bf16_peak": round(flops / (float(durs_f.mean()) * 1e-3) / 1e12
                                    / PEAK_BF16_TFLOPS, 4),
     }
+
+    # the split-KV step over the streams: Q and K read in place, V either transposed into
+    # the workspace by the call (pack_v 1) or read in place too (pack_v 0); workspaces
+    # allocated before timing.  Its output must equal the timed bf16 step's bit for bit.
+    for pack_v, key, what in ((1, "fused_bf16_splitkv", "Q, K in place, V^T packed in the call"),
+                              (0, "fused_bf16_splitkv_inplace", "Q, K, V all in place")):
+        ws_s = torch.empty((max(int(ja.load().joint_attn_fwd_bf16_streams_splitkv_workspace(
+            B, H, N, D, ns_main, pack_v)), 16),), dtype=torch.uint8, device="cuda")
+
+        def step_fused_split(rec, pack_v=pack_v, ws_s=ws_s):
+            e0, e1 = (ev(), ev()) if rec else (None, None)
+            if rec:
+                e0.record(stream)
+            ja.joint_attn_fwd_bf16_streams_splitkv(qs_d, ks_d, vs_d, scale, n_split=ns_main,
+                                                   pack_v=pack_v, workspace=ws_s, out=o)
+            if rec:
+                e1.record(stream)
+            return (e0, e1)
+
+        log("timing fused bf16 split-KV path (%s)" % what)
+        wall_fs, durs_fs = timed(step_fused_split, args.steps, args.warmup)
+        ms_fs = wall_fs * 1e3 / args.steps
+        same = bool(torch.equal(o.view(torch.int16), o_timed.view(torch.int16)))
+        out[key] = {
+            "step": "fwd_bf16_streams_splitkv, pack_v %d (%s), n_split %d" % (pack_v, what,
+                                                                             ns_main),
+            "value": round(flops / (ms_fs * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_fs, 4),
+            "call_ms": round(float(durs_fs.mean()), 4),
+            "call_tflops": round(flops / (float(durs_fs.mean()) * 1e-3) / 1e12, 2),
+            "equals_bf16_step_output": same,
+        }
+        del ws_s
 
     # block-sparse forward with a structured 128x128 block mask (text rows and columns,
     # a band of 2 blocks around the diagonal, 15 % of the other image blocks)

@@ -11,8 +11,8 @@
  * This library computes it as unmasked scaled-dot-product attention,
  *     O = softmax(Q K^T * softmax_scale) V        (per batch b and head h),
  * in four calls: pack the streams, then either the bf16 forward, or the fp8 quantiser
- * followed by the fp8 forward; joint_attn_fwd_bf16_streams does pack and bf16 forward in
- * one call, reading the streams in place.
+ * followed by the fp8 forward; joint_attn_fwd_bf16_streams (and its split-KV form) does
+ * pack and bf16 forward in one call, reading the streams in place.
  *
  * Conventions for every call.
  *   - Tensor pointers are DEVICE pointers (HBM) owned by the caller; the library never
@@ -216,6 +216,37 @@ int joint_attn_fwd_bf16_streams(int n_streams, const void *const *q, const void 
                                 const void *const *v, const int64_t *lens,
                                 int B, int H, int D, float softmax_scale,
                                 void *o, float *lse, int64_t *offsets, void *stream);
+
+/*
+ * joint_attn_fwd_bf16_streams_splitkv -- joint_attn_fwd_bf16_streams with the query tiles
+ * of the last, partial round split into key ranges and merged, as joint_attn_fwd_bf16_splitkv
+ * does for packed operands (the log-sum-exp merge of the split-KV comment above).  Q and K
+ * are always read in place from the streams (the joint sequence of the VisualGen FLUX 3
+ * article, everytik.com translation, section 使用 TensorRT LLM VisualGen 进行 FLUX 3 推理).
+ *   n_streams .. offsets   as for joint_attn_fwd_bf16_streams
+ *   n_split           as for joint_attn_fwd_bf16_splitkv (the same suggestion applies)
+ *   pack_v            0: V is read in place too and transposed in LDS (no copy of V);
+ *                     1: V is first transposed into the workspace (BHDN, pitch
+ *                     joint_attn_vt_ld(N)) by the pack kernel, and the forward loads
+ *                     its V^T tiles from there (faster forward, B*H*D*ld*2 more bytes)
+ *   workspace         device scratch owned by the caller, 16-byte aligned, at least
+ *                     joint_attn_fwd_bf16_streams_splitkv_workspace() bytes (asked on the
+ *                     device the call runs on): the V^T copy (pack_v = 1), then the split
+ *                     tiles' fp32 partials; its contents on entry do not matter
+ * Results are bit-identical to joint_attn_pack (x3) followed by joint_attn_fwd_bf16_splitkv
+ * with the same n_split, for either pack_v.  Errors as joint_attn_fwd_bf16_streams and
+ * joint_attn_fwd_bf16_splitkv (JA_EINVAL also for pack_v not 0 or 1).  Calls that share a
+ * workspace must not overlap.
+ */
+int64_t joint_attn_fwd_bf16_streams_splitkv_workspace(int B, int H, int64_t N, int D,
+                                                      int n_split, int pack_v);
+int joint_attn_fwd_bf16_streams_splitkv(int n_streams, const void *const *q,
+                                        const void *const *k, const void *const *v,
+                                        const int64_t *lens, int B, int H, int D,
+                                        float softmax_scale, int n_split, int pack_v,
+                                        void *workspace, int64_t workspace_bytes,
+                                        void *o, float *lse, int64_t *offsets,
+                                        void *stream);
 
 /*
  * joint_attn_quant_fp8 -- quantise packed bf16 Q, K, V to e4m3 with dequantisation

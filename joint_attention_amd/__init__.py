@@ -7,6 +7,7 @@ synthetic-input generator used by the tests and the benchmark.
 from ._abi import (JointAttnError, Fp8Tensors, load, joint_attn_vt_ld, joint_attn_pack,
                    joint_attn_fwd_bf16, joint_attn_fwd_bf16_sparse, joint_attn_fwd_bf16_splitkv,
                    joint_attn_fwd_bf16_streams, joint_attn_fwd_bf16_splitkv_noalloc,
+                   joint_attn_fwd_bf16_streams_splitkv,
                    joint_attn_quant_fp8,
                    joint_attn_quant_fp8_streams, joint_attn_fwd_fp8, joint_attn_fwd_fp8_splitkv,
                    joint_attn_repair_count,
@@ -17,6 +18,7 @@ from ._abi import (JointAttnError, Fp8Tensors, load, joint_attn_vt_ld, joint_att
 __all__ = ["JointAttnError", "Fp8Tensors", "load", "joint_attn_vt_ld", "joint_attn_pack",
            "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse", "joint_attn_fwd_bf16_splitkv",
            "joint_attn_fwd_bf16_streams", "joint_attn_fwd_bf16_splitkv_noalloc",
+           "joint_attn_fwd_bf16_streams_splitkv",
            "joint_attn_quant_fp8",
            "joint_attn_quant_fp8_streams", "joint_attn_fwd_fp8", "joint_attn_fwd_fp8_splitkv",
            "joint_attn_repair_count",

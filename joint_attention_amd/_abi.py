@@ -32,7 +32,8 @@ EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld
            "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse",
            "joint_attn_fwd_bf16_splitkv", "joint_attn_fwd_bf16_splitkv_workspace",
            "joint_attn_fwd_bf16_splitkv_suggest", "joint_attn_fwd_bf16_splitkv_noalloc",
-           "joint_attn_fwd_bf16_streams",
+           "joint_attn_fwd_bf16_streams", "joint_attn_fwd_bf16_streams_splitkv",
+           "joint_attn_fwd_bf16_streams_splitkv_workspace",
            "joint_attn_quant_fp8", "joint_attn_quant_fp8_streams",
            "joint_attn_fwd_fp8", "joint_attn_fwd_fp8_splitkv", "joint_attn_fwd_fp8_splitkv_workspace",
            "joint_attn_fwd_fp8_splitkv_suggest", "joint_attn_repair_count",
@@ -92,6 +93,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_fwd_bf16_streams.restype = I
         h.joint_attn_fwd_bf16_streams.argtypes = [I, P, P, P, P, I, I, I, F,
                                                   P, P, P, P]
+        h.joint_attn_fwd_bf16_streams_splitkv_workspace.restype = I64
+        h.joint_attn_fwd_bf16_streams_splitkv_workspace.argtypes = [I, I, I64, I, I, I]
+        h.joint_attn_fwd_bf16_streams_splitkv.restype = I
+        h.joint_attn_fwd_bf16_streams_splitkv.argtypes = [I, P, P, P, P, I, I, I, F, I, I, P, I64,
+                                                          P, P, P, P]
         h.joint_attn_quant_fp8.restype = I
         h.joint_attn_quant_fp8.argtypes = [P, P, P, I, I, I64, I, I64, I, P, P, P, P, P, P,
                                            P, P, P, P, P]
@@ -300,11 +306,9 @@ def joint_attn_fwd_bf16_splitkv_noalloc(q, k, vt, softmax_scale: float | None = 
     return out
 
 
-def joint_attn_fwd_bf16_streams(q_streams, k_streams, v_streams,
-                                softmax_scale: float | None = None, out=None,
-                                return_lse: bool = False):
-    """Attention over the concatenation of per-stream bf16 [B, L_s, H, D] tensors, read in
-    place.  Returns (O [B, N, H, D], offsets) (and lse [B, H, N] if asked)."""
+def _streams(q_streams, k_streams, v_streams):
+    """Checks of per-stream bf16 [B, L_s, H, D] tensors; returns (lists, B, H, D, N, ctypes
+    pointer arrays and lengths)."""
     torch = _torch()
     qs, ks, vs = list(q_streams), list(k_streams), list(v_streams)
     n = len(qs)
@@ -319,19 +323,66 @@ def joint_attn_fwd_bf16_streams(q_streams, k_streams, v_streams,
                     or t.device != dev:
                 raise ValueError("streams must share B, H, D, lengths per stream and device")
     N = sum(int(x.shape[1]) for x in qs)
+    ptr = lambda lst: (ctypes.c_void_p * n)(*[x.data_ptr() if x.numel() else None for x in lst])
+    lens = (ctypes.c_int64 * n)(*[int(x.shape[1]) for x in qs])
+    return qs, B, H, D, N, dev, ptr(qs), ptr(ks), ptr(vs), lens
+
+
+def joint_attn_fwd_bf16_streams(q_streams, k_streams, v_streams,
+                                softmax_scale: float | None = None, out=None,
+                                return_lse: bool = False):
+    """Attention over the concatenation of per-stream bf16 [B, L_s, H, D] tensors, read in
+    place.  Returns (O [B, N, H, D], offsets) (and lse [B, H, N] if asked)."""
+    torch = _torch()
+    qs, B, H, D, N, dev, pq, pk, pv, lens = _streams(q_streams, k_streams, v_streams)
+    n = len(qs)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
     _need(out, torch.bfloat16, "out", 4)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
-    ptr = lambda lst: (ctypes.c_void_p * n)(*[x.data_ptr() if x.numel() else None for x in lst])
-    lens = (ctypes.c_int64 * n)(*[int(x.shape[1]) for x in qs])
     offs = (ctypes.c_int64 * (n + 1))()
-    st = load().joint_attn_fwd_bf16_streams(n, ptr(qs), ptr(ks), ptr(vs), lens, B, H, D, scale,
+    st = load().joint_attn_fwd_bf16_streams(n, pq, pk, pv, lens, B, H, D, scale,
                                             out.data_ptr() if out.numel() else None,
                                             lse.data_ptr() if lse is not None else None, offs,
                                             _stream(out))
     _check("joint_attn_fwd_bf16_streams", st)
+    return (out, list(offs), lse) if return_lse else (out, list(offs))
+
+
+def joint_attn_fwd_bf16_streams_splitkv(q_streams, k_streams, v_streams,
+                                        softmax_scale: float | None = None,
+                                        n_split: int | None = None, pack_v: int = 1,
+                                        workspace=None, out=None, return_lse: bool = False):
+    """joint_attn_fwd_bf16_streams with split keys.  pack_v = 1 transposes V into the
+    workspace first (faster forward), 0 reads V in place too.  n_split defaults to the
+    library's suggestion; the workspace is allocated here if not given.  Returns
+    (O, offsets) (and lse if asked)."""
+    torch = _torch()
+    qs, B, H, D, N, dev, pq, pk, pv, lens = _streams(q_streams, k_streams, v_streams)
+    n = len(qs)
+    lib = load()
+    if n_split is None:
+        n_split = lib.joint_attn_fwd_bf16_splitkv_suggest(B, H, N, D)
+    need = int(lib.joint_attn_fwd_bf16_streams_splitkv_workspace(B, H, N, D, int(n_split),
+                                                                 int(pack_v)))
+    if need < 0:
+        raise ValueError("invalid sizes, n_split or pack_v")
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out", 4)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if return_lse else None
+    offs = (ctypes.c_int64 * (n + 1))()
+    st = lib.joint_attn_fwd_bf16_streams_splitkv(
+        n, pq, pk, pv, lens, B, H, D, scale, int(n_split), int(pack_v), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), out.data_ptr() if out.numel() else None,
+        lse.data_ptr() if lse is not None else None, offs, _stream(out))
+    _check("joint_attn_fwd_bf16_streams_splitkv", st)
     return (out, list(offs), lse) if return_lse else (out, list(offs))
 
 

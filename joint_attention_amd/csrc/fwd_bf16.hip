@@ -9,8 +9,8 @@
 // waves share a SIMD, and Q, O, two score tiles and two P tiles stay in its 256 VGPRs.
 // Keys are consumed in tiles of BC = 32, loaded once per workgroup into LDS.
 //
-// Variants of the same kernel: GATHER reads Q, K and V in place from the per-stream
-// tensors (no pack step); SPARSE visits only the key blocks that an input block mask
+// Variants of the same kernel: GATHER reads Q and K (and, in mode 1, V) in place from the
+// per-stream tensors (no pack step for them); SPARSE visits only the key blocks that an input block mask
 // allows; PARTIAL splits the keys of the last round's query tiles into ranges whose
 // partial results splitkv_merge_kernel combines (split-KV).
 //
@@ -86,9 +86,11 @@ __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | (
 // 256 rows) and fills a CU at two waves per SIMD; with NW * QB = 4 two 128-row workgroups
 // share a CU (D = 64, and the block-sparse forward, whose workgroups then match its mask
 // blocks).
-// GATHER: Q, K and V are read in place from the per-stream tensors of `st` (token-major
-// [B][L_s][H][D]) instead of the packed Q, K (BHND) and V^T (BHDN); V tiles are then kept
-// token-major in LDS and read with transposing LDS loads.
+// GATHER = 1: Q, K and V are read in place from the per-stream tensors of `st`
+// (token-major [B][L_s][H][D]) instead of the packed Q, K (BHND) and V^T (BHDN); V tiles
+// are then kept token-major in LDS and read with transposing LDS loads.
+// GATHER = 2: Q and K are read in place from the streams (K tiles by LDS DMA, each key
+// row being D contiguous elements of its stream's row), V^T from a packed copy (BHDN).
 // SPARSE: only the key blocks that a block mask (uint8 [B][H][nqb][nkb], 128 x 128 blocks)
 // allows for at least one of the workgroup's query blocks are visited; a wave whose own
 // query block does not see a visited block gives it zero weight.
@@ -97,14 +99,17 @@ __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | (
 // into n_split ranges of whole tiles, one workgroup per (query tile, range), each writing
 // its normalised fp32 partial output and lse (OP [part][BR][D], LP [part][BR], part =
 // (tile - n_full) * n_split + range) for the merge kernel below.
-template <int D, int NW, int QB, int BC, bool GATHER, bool SPARSE, bool PARTIAL = false>
+template <int D, int NW, int QB, int BC, int GATHER, bool SPARSE, bool PARTIAL = false>
 __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ VT,
     const StreamTable st, const uint8_t* __restrict__ MASK, int H, int N, int64_t ldv, float c2,
     __bf16* __restrict__ O, float* __restrict__ LSE, int n_qtiles, int total,
     int n_split = 1, float* __restrict__ OP = nullptr, float* __restrict__ LP = nullptr,
     int n_full = 0) {
-    static_assert(int(GATHER) + int(SPARSE) + int(PARTIAL) <= 1, "one variant at a time");
+    static_assert(GATHER >= 0 && GATHER <= 2, "gather mode");
+    static_assert(!(SPARSE && (GATHER || PARTIAL)), "the block-sparse forward runs alone");
+    constexpr bool GQK = GATHER != 0;            // Q and K read from the streams
+    constexpr bool GV = GATHER == 1;             // V read from the streams (transposed in LDS)
     constexpr int NTHREADS = NW * 64;
     constexpr int BR = NW * QB * 32;             // query rows per workgroup
     constexpr int KB = BC / 32;                  // 32-key blocks per tile
@@ -124,9 +129,9 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     __shared__ __attribute__((aligned(1024))) __bf16 sk1[TILE_ELEMS];
     __shared__ __attribute__((aligned(1024))) __bf16 sv0[TILE_ELEMS];
     __shared__ __attribute__((aligned(1024))) __bf16 sv1[TILE_ELEMS];
-    // GATHER: token-major V tiles, transposed into sv0 / sv1 one iteration later
-    __shared__ __attribute__((aligned(1024))) __bf16 st0[GATHER ? TILE_ELEMS : 8];
-    __shared__ __attribute__((aligned(1024))) __bf16 st1[GATHER ? TILE_ELEMS : 8];
+    // GATHER = 1: token-major V tiles, transposed into sv0 / sv1 one iteration later
+    __shared__ __attribute__((aligned(1024))) __bf16 st0[GV ? TILE_ELEMS : 8];
+    __shared__ __attribute__((aligned(1024))) __bf16 st1[GV ? TILE_ELEMS : 8];
 
     // V^T rows: 16-byte chunk u of row r sits at chunk u ^ vswz(r).  A 16-byte operand
     // read serves 16 rows at once (VRPB rows per 256-byte bank line: (r / VRPB) picks
@@ -249,17 +254,19 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         return static_cast<const __bf16*>(src[s]) +
                (((int64_t)b * L + (n - st.off[s])) * H + h) * (int64_t)D;
     };
-    const int64_t row_pitch = GATHER ? (int64_t)H * D : D;   // elements between tokens
+    const int64_t row_pitch = GQK ? (int64_t)H * D : D;   // elements between Q / K tokens
     // GATHER: tiles are visited in order, so each tensor keeps a cursor on the stream that
     // holds its current tile; the stream table is read only when a tile crosses into the
     // next stream (reads of it inside the loop would also stall the LDS-operand waits)
     struct Cursor {
         int s, start, end;               // stream s holds packed tokens [start, end)
         const __bf16* row0;              // its row for packed token `start`
+        int next;                        // packed token whose row `ptr` is (-1: none)
+        const __bf16* ptr;
     };
     auto cursor_init = [&](const void* const* src) {
-        Cursor c{0, 0, (int)st.off[1], nullptr};
-        if (GATHER) c.row0 = stream_row(src, 0, 0);
+        Cursor c{0, 0, (int)st.off[1], nullptr, 0, nullptr};
+        if (GQK) c.row0 = c.ptr = stream_row(src, 0, 0);
         return c;
     };
     auto advance = [&](Cursor& c, const void* const* src, int key) {   // key >= c.start
@@ -268,7 +275,20 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
             c.start = c.end;
             c.end = (int)st.off[c.s + 1];
             c.row0 = stream_row(src, c.s, c.start);
+            c.next = -1;
         }
+    };
+    // the row of packed token k0 (a tile's first key) when the whole tile lies in one
+    // stream, else nullptr (it straddles streams or N); tiles come in order, so the row
+    // pointer normally just moves on by one tile (a multiply only after a jump)
+    auto tile_base = [&](Cursor& c, const void* const* src, int k0) -> const __bf16* {
+        advance(c, src, k0);                                    // wave-uniform
+        if (k0 + BC > c.end) return nullptr;
+        if (k0 != c.next) c.ptr = c.row0 + (int64_t)(k0 - c.start) * row_pitch;
+        const __bf16* p = c.ptr;
+        c.ptr = p + BC * row_pitch;
+        c.next = k0 + BC;
+        return p;
     };
     Cursor kcur = cursor_init(st.k), vcur = cursor_init(st.v);
 
@@ -283,11 +303,11 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     };
     auto v_row = [&](int i) {
         const int off = (w * LOADS + i) * 1024 + lane * 16;
-        return GATHER ? off / (2 * D) : off / (2 * BC);
+        return GV ? off / (2 * D) : off / (2 * BC);
     };
     auto v_chunk = [&](int i) {
         const int off = (w * LOADS + i) * 1024 + lane * 16;
-        if constexpr (GATHER) {
+        if constexpr (GV) {
             // token-major V tile: the 64-byte segments of each key row are rotated by
             // (key / GRPL) % GSEG (conflict-free for the transposing reads)
             return ((off % (2 * D)) / 16) ^ ((((off / (2 * D)) / GRPL) % GSEG) * 4);
@@ -298,17 +318,15 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         k_off[i] = (uint32_t)(k_row(i) * row_pitch + k_chunk(i) * 8) * 2u;
-        v_off[i] = GATHER ? (uint32_t)(v_row(i) * row_pitch + v_chunk(i) * 8) * 2u
+        v_off[i] = GV ? (uint32_t)(v_row(i) * row_pitch + v_chunk(i) * 8) * 2u
                           : (uint32_t)(v_row(i) * (int)ldv + v_chunk(i) * 8) * 2u;
     }
     uint4 kst[LOADS], vst[LOADS];                 // staged tiles (global -> registers)
-    auto load_k = [&](int kt) {                  // GATHER only (the others load K by DMA)
+    auto load_k = [&](int kt) {                  // GATHER = 1 only (the others load K by DMA)
         const int k0 = tile_k0(kt);
-        if constexpr (GATHER) {
-            advance(kcur, st.k, k0);                            // wave-uniform
-            if (k0 + BC <= kcur.end) {                          // the tile lies in one stream
-                const char* base = reinterpret_cast<const char*>(
-                    kcur.row0 + (int64_t)(k0 - kcur.start) * row_pitch);
+        if constexpr (GV) {
+            if (const __bf16* row = tile_base(kcur, st.k, k0)) {  // the tile lies in one stream
+                const char* base = reinterpret_cast<const char*>(row);
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i)
                     kst[i] = *reinterpret_cast<const uint4*>(base + k_off[i]);
@@ -324,13 +342,11 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     };
     auto load_v = [&](int kt) {
         const int k0 = tile_k0(kt);
-        if constexpr (GATHER) {
+        if constexpr (GV) {
             // token-major rows as for K; rows past N repeat row N-1 (finite, and their
             // probabilities are exactly zero)
-            advance(vcur, st.v, k0);
-            if (k0 + BC <= vcur.end) {
-                const char* base = reinterpret_cast<const char*>(
-                    vcur.row0 + (int64_t)(k0 - vcur.start) * row_pitch);
+            if (const __bf16* row = tile_base(vcur, st.v, k0)) {
+                const char* base = reinterpret_cast<const char*>(row);
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i)
                     vst[i] = *reinterpret_cast<const uint4*>(base + v_off[i]);
@@ -375,12 +391,12 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         for (int i = 0; i < LOADS; ++i)
             *reinterpret_cast<uint4*>(slot + (w * LOADS + i) * 512 + lane * 8) = kst[i];
     };
-    // GATHER: V^T chunk (row c, keys 8u .. 8u + 7) of a token-major tile in `ts`, one per
+    // GATHER = 1: V^T chunk (row c, keys 8u .. 8u + 7) of a token-major tile in `ts`, one per
     // thread: in each 16-lane group, lane k points at key 8u + 4 half + (k >> 2), channels
     // 4 (k & 3) .. + 3 of the group's 16 channels; the transposing read hands lane r the 4
     // keys of channel c0 + r.  Written later to `vs` in the V^T layout of the operand reads
     // (the write waits for the reads, so it is placed a few MFMA steps after them).
-    static_assert(!GATHER || NTHREADS * 8 == TILE_ELEMS,
+    static_assert(!GV || NTHREADS * 8 == TILE_ELEMS,
                   "the transpose moves one 16-byte V^T chunk per thread");
     auto transpose_read = [&](const __bf16* ts) {
         typedef short v4s __attribute__((ext_vector_type(4)));
@@ -410,11 +426,11 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
             *reinterpret_cast<uint4*>(slot + (w * LOADS + i) * 512 + lane * 8) = vst[i];
     };
 
-    // direct global -> LDS loads (gfx950 global_load_lds_dwordx4; not for GATHER, whose V
-    // goes through a transpose): each wave's 16-byte chunks land lane-linear in the slot,
+    // direct global -> LDS loads (gfx950 global_load_lds_dwordx4; not for GATHER = 1, whose
+    // V goes through a transpose): each wave's 16-byte chunks land lane-linear in the slot,
     // the layout store_k / store_v write (the swizzle lives in the global offsets), with
     // no staging registers and no LDS store instructions
-    constexpr bool DMA = !GATHER;
+    constexpr bool DMA = !GV;
     auto dma16 = [&](const void* src, __bf16* dst) {
         __builtin_amdgcn_global_load_lds(
             (const __attribute__((address_space(1))) void*)src,
@@ -422,6 +438,23 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     };
     auto dma_k = [&](int kt, __bf16* slot) {
         const int k0 = tile_k0(kt);
+        if constexpr (GQK) {
+            // stream rows: a tile inside one stream from the cursor's scalar base, one that
+            // straddles streams (or N) row by row
+            if (const __bf16* row = tile_base(kcur, st.k, k0)) {
+                const char* base = reinterpret_cast<const char*>(row);
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) dma16(base + k_off[i], slot + (w * LOADS + i) * 512);
+            } else {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+                    const int key = min(k0 + k_row(i), N - 1);  // rows past N: any finite row
+                    dma16(stream_row(st.k, stream_of(key), key) + k_chunk(i) * 8,
+                          slot + (w * LOADS + i) * 512);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
             const char* src;
@@ -458,7 +491,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int q_ld = min(q_base + 32 * qb, N - 1);
-        const __bf16* qrow = GATHER ? stream_row(st.q, stream_of(q_ld), q_ld)
+        const __bf16* qrow = GQK ? stream_row(st.q, stream_of(q_ld), q_ld)
                                     : Qbh + (int64_t)q_ld * D;
 #pragma unroll
         for (int c = 0; c < NQC; ++c)
@@ -589,7 +622,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     }
     __syncthreads();
     qk_all(sk0, sA);
-    if constexpr (GATHER) {
+    if constexpr (GV) {
         load_k(min(2, nkt - 1));
         // V_0 token-major before the first barrier; V_1 staged for iteration 0
         load_v(0);
@@ -614,7 +647,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         dma_wait();
         __syncthreads();
         // DMA: K_{j+2} and V_j go straight to the slots freed by the barrier and land
-        // before the next one.  GATHER: the staged K_{j+2} goes there, then K_{j+3} is
+        // before the next one.  GATHER = 1: the staged K_{j+2} goes there, then K_{j+3} is
         // staged (indices past the end reload the last tile, unused); V_{j+1} goes
         // token-major into the free staging slot and V_j (staged last iteration) is read
         // transposed now, then written to the V^T slot during the steps
@@ -691,7 +724,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
             for (int e = 0; e < NEXP; ++e) exp_pair(s_in, p_out, e, nm, l);
             if constexpr (HAS_PV) pv_all(rd_v, p_in);
             if constexpr (HAS_QK) qk_all(rd_k, s_out);
-            if constexpr (GATHER) transpose_write(vtr, my_v);
+            if constexpr (GV) transpose_write(vtr, my_v);
         } else {
             bf16x8 opnd[LEAD + 1];
 #pragma unroll
@@ -705,7 +738,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                 } else {
                     if (qk_on) mfma_qk(st - NPV, opnd[k % (LEAD + 1)], s_out);
                 }
-                if (GATHER && k == (NST > FWD_TW ? FWD_TW : NST - 1)) transpose_write(vtr, my_v);
+                if (GV && k == (NST > FWD_TW ? FWD_TW : NST - 1)) transpose_write(vtr, my_v);
                 // softmax slice: offset check first, then numerators
                 if (k < QB) check(k);
                 if (k >= FIRST && sm_on) {
@@ -802,7 +835,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     }
 }
 
-template <int D, int NW, int QB, int BC, bool GATHER, bool SPARSE = false>
+template <int D, int NW, int QB, int BC, int GATHER, bool SPARSE = false>
 hipError_t launch_d(const void* q, const void* k, const void* vt, const StreamTable& st, int B,
                     int H, int N, int64_t ldv, float softmax_scale, void* o, float* lse,
                     hipStream_t stream, const uint8_t* mask = nullptr) {
@@ -824,9 +857,9 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, 
                            hipStream_t stream) {
     // head size 64 (4 KB tiles) keeps 4 waves so that each wave still moves whole 1 KB loads
     const StreamTable none{};
-    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, false>(q, k, vt, none, B, H, N, ldv,
+    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, 0>(q, k, vt, none, B, H, N, ldv,
                                                             softmax_scale, o, lse, stream)
-                   : launch_d<128, FWD_NW, FWD_QB, FWD_BC, false>(q, k, vt, none, B, H, N, ldv,
+                   : launch_d<128, FWD_NW, FWD_QB, FWD_BC, 0>(q, k, vt, none, B, H, N, ldv,
                                                                   softmax_scale, o, lse, stream);
 }
 
@@ -834,10 +867,10 @@ hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
                                   const uint8_t* mask, int B, int H, int N, int D, int64_t ldv,
                                   float softmax_scale, void* o, float* lse, hipStream_t stream) {
     const StreamTable none{};
-    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, false, true>(q, k, vt, none, B, H, N, ldv,
+    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, 0, true>(q, k, vt, none, B, H, N, ldv,
                                                                   softmax_scale, o, lse, stream,
                                                                   mask)
-                   : launch_d<128, FWD_NW_SPARSE, FWD_QB, FWD_BC, false, true>(
+                   : launch_d<128, FWD_NW_SPARSE, FWD_QB, FWD_BC, 0, true>(
                          q, k, vt, none, B, H, N, ldv, softmax_scale, o, lse, stream, mask);
 }
 
@@ -850,9 +883,9 @@ int splitkv_slots(int D) {
         cus = 256;
     hipError_t e = D == 64
         ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &per, fwd_bf16_kernel<64, 4, FWD_QB, FWD_BC, false, false, true>, 4 * 64, 0)
+              &per, fwd_bf16_kernel<64, 4, FWD_QB, FWD_BC, 0, false, true>, 4 * 64, 0)
         : hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &per, fwd_bf16_kernel<128, FWD_NW, FWD_QB, FWD_BC, false, false, true>, FWD_NW * 64,
+              &per, fwd_bf16_kernel<128, FWD_NW, FWD_QB, FWD_BC, 0, false, true>, FWD_NW * 64,
               0);
     if (e != hipSuccess || per < 1) per = 1;
     return cus * per;
@@ -860,28 +893,35 @@ int splitkv_slots(int D) {
 
 int splitkv_rows_per_tile(int D) { return D == 64 ? 4 * FWD_QB * 32 : FWD_NW * FWD_QB * 32; }
 
-hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
-                                   int N, int D, int64_t ldv, float softmax_scale, int n_split,
-                                   int slots, float* o_part, float* lse_part, void* o,
-                                   float* lse, hipStream_t stream) {
+namespace {
+// split-KV launch for gather mode G (0: packed Q, K, V^T; 1: all three from the streams;
+// 2: Q and K from the streams, V^T packed): the split kernel and the merge, or the plain
+// forward when nothing is split
+template <int G>
+hipError_t launch_splitkv_mode(const void* q, const void* k, const void* vt,
+                               const StreamTable& st, int B, int H, int N, int D, int64_t ldv,
+                               float softmax_scale, int n_split, int slots, float* o_part,
+                               float* lse_part, void* o, float* lse, hipStream_t stream) {
     const int tiles = (N + FWD_BC - 1) / FWD_BC;
     n_split = n_split < tiles ? n_split : tiles;               // every key range non-empty
     const int BRr = splitkv_rows_per_tile(D);
     const int n_units = (N + BRr - 1) / BRr * B * H;
     const int tail = n_units % slots;                         // tiles of the last, partial round
-    if (n_split <= 1 || tail == 0) return launch_fwd_bf16(q, k, vt, B, H, N, D, ldv, softmax_scale,
-                                                           o, lse, stream);
+    if (n_split <= 1 || tail == 0)
+        return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, G>(q, k, vt, st, B, H, N, ldv,
+                                                            softmax_scale, o, lse, stream)
+                       : launch_d<128, FWD_NW, FWD_QB, FWD_BC, G>(q, k, vt, st, B, H, N, ldv,
+                                                                  softmax_scale, o, lse, stream);
     const int n_full = n_units - tail;
-    const StreamTable none{};
     auto go = [&](auto d_tag, auto nw_tag) -> hipError_t {
         constexpr int DD = decltype(d_tag)::value, NWW = decltype(nw_tag)::value;
         constexpr int BR = NWW * FWD_QB * 32;
         constexpr int RPB = 256 / (DD / 4);
         const int n_qtiles = (N + BR - 1) / BR;
         const int total = n_full + tail * n_split;
-        hipLaunchKernelGGL((fwd_bf16_kernel<DD, NWW, FWD_QB, FWD_BC, false, false, true>),
+        hipLaunchKernelGGL((fwd_bf16_kernel<DD, NWW, FWD_QB, FWD_BC, G, false, true>),
                            dim3(total), dim3(NWW * 64), 0, stream, static_cast<const __bf16*>(q),
-                           static_cast<const __bf16*>(k), static_cast<const __bf16*>(vt), none,
+                           static_cast<const __bf16*>(k), static_cast<const __bf16*>(vt), st,
                            nullptr, H, N, ldv, softmax_scale * kLog2e, static_cast<__bf16*>(o),
                            lse, n_qtiles, total, n_split, o_part, lse_part, n_full);
         hipError_t e = hipGetLastError();
@@ -896,6 +936,28 @@ hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt,
     using I4 = std::integral_constant<int, 4>;
     using INW = std::integral_constant<int, FWD_NW>;
     return D == 64 ? go(I64{}, I4{}) : go(I128{}, INW{});
+}
+}  // namespace
+
+hipError_t launch_fwd_bf16_splitkv(const void* q, const void* k, const void* vt, int B, int H,
+                                   int N, int D, int64_t ldv, float softmax_scale, int n_split,
+                                   int slots, float* o_part, float* lse_part, void* o,
+                                   float* lse, hipStream_t stream) {
+    const StreamTable none{};
+    return launch_splitkv_mode<0>(q, k, vt, none, B, H, N, D, ldv, softmax_scale, n_split, slots,
+                                  o_part, lse_part, o, lse, stream);
+}
+
+hipError_t launch_fwd_bf16_streams_splitkv(const StreamTable& st, const void* vt, int64_t ldv,
+                                           int B, int H, int N, int D, float softmax_scale,
+                                           int n_split, int slots, float* o_part,
+                                           float* lse_part, void* o, float* lse,
+                                           hipStream_t stream) {
+    return vt == nullptr
+        ? launch_splitkv_mode<1>(nullptr, nullptr, nullptr, st, B, H, N, D, 0, softmax_scale,
+                                 n_split, slots, o_part, lse_part, o, lse, stream)
+        : launch_splitkv_mode<2>(nullptr, nullptr, vt, st, B, H, N, D, ldv, softmax_scale,
+                                 n_split, slots, o_part, lse_part, o, lse, stream);
 }
 
 // ---- allocation-free split-KV: the partial outputs and log-sum-exps live in this
@@ -947,11 +1009,11 @@ hipError_t launch_fwd_bf16_splitkv_noalloc(const void* q, const void* k, const v
 hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, int D,
                                    float softmax_scale, void* o, float* lse,
                                    hipStream_t stream) {
-    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, true>(nullptr, nullptr, nullptr, st, B, H, N,
-                                                           0, softmax_scale, o, lse, stream)
-                   : launch_d<128, FWD_NW, FWD_QB, FWD_BC, true>(nullptr, nullptr, nullptr, st, B,
-                                                                 H, N, 0, softmax_scale, o, lse,
-                                                                 stream);
+    return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, 1>(nullptr, nullptr, nullptr, st, B, H, N,
+                                                        0, softmax_scale, o, lse, stream)
+                   : launch_d<128, FWD_NW, FWD_QB, FWD_BC, 1>(nullptr, nullptr, nullptr, st, B,
+                                                              H, N, 0, softmax_scale, o, lse,
+                                                              stream);
 }
 
 }  // namespace ja

@@ -52,6 +52,15 @@ hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, i
                                    float softmax_scale, void* o, float* lse,
                                    hipStream_t stream);
 
+// split-KV over the streams: with vt == nullptr Q, K and V are all read in place (V
+// transposed in LDS); otherwise Q and K are read in place and V^T from the packed copy
+// vt (BHDN, pitch ldv).  o_part / lse_part as for launch_fwd_bf16_splitkv.
+hipError_t launch_fwd_bf16_streams_splitkv(const StreamTable& st, const void* vt, int64_t ldv,
+                                           int B, int H, int N, int D, float softmax_scale,
+                                           int n_split, int slots, float* o_part,
+                                           float* lse_part, void* o, float* lse,
+                                           hipStream_t stream);
+
 hipError_t launch_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int N,
                             int D, int64_t ldv, int mode, void* q8, void* k8, void* v8t,
                             float* q_scale, float* k_scale, float* v_scale, void* q_hi,

@@ -287,6 +287,66 @@ int joint_attn_fwd_bf16_streams(int n_streams, const void* const* q, const void*
                                           static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// bytes of the packed V^T copy at the head of the streams split-KV workspace (256-aligned)
+int64_t streams_vt_bytes(int B, int H, int64_t N, int D) {
+    return ((int64_t)B * H * D * joint_attn_vt_ld(N) * 2 + 255) / 256 * 256;
+}
+}  // namespace
+
+int64_t joint_attn_fwd_bf16_streams_splitkv_workspace(int B, int H, int64_t N, int D,
+                                                      int n_split, int pack_v) {
+    if (pack_v != 0 && pack_v != 1) return -1;
+    const int64_t part = joint_attn_fwd_bf16_splitkv_workspace(B, H, N, D, n_split);
+    if (part < 0) return -1;
+    return part + (pack_v ? streams_vt_bytes(B, H, N, D) : 0);
+}
+
+int joint_attn_fwd_bf16_streams_splitkv(int n_streams, const void* const* q,
+                                        const void* const* k, const void* const* v,
+                                        const int64_t* lens, int B, int H, int D,
+                                        float softmax_scale, int n_split, int pack_v,
+                                        void* workspace, int64_t workspace_bytes, void* o,
+                                        float* lse, int64_t* offsets, void* stream) {
+    ja::StreamTable st{};
+    const int tst = stream_table(n_streams, q, k, v, lens, st);
+    if (tst != JA_OK) return tst;
+    const int64_t N = st.off[n_streams];
+    const int64_t ldv = joint_attn_vt_ld(N);
+    const int sh = check_shape(B, H, N, D, ldv);
+    if (sh != JA_OK) return sh;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (n_split <= 0 || n_split > 64 || (pack_v != 0 && pack_v != 1)) return JA_EINVAL;
+    if (offsets)
+        for (int s = 0; s <= n_streams; ++s) offsets[s] = st.off[s];
+    if (N == 0) return JA_OK;
+    if (!o || !workspace) return JA_EINVAL;
+    // one device query sizes the workspace check, the partial layout and the launch
+    const int slots = ja::splitkv_slots(D);
+    const int64_t br = ja::splitkv_rows_per_tile(D);
+    const int64_t split_tiles = std::min<int64_t>((N + br - 1) / br * B * H, slots);
+    const int64_t vt_bytes = pack_v ? streams_vt_bytes(B, H, N, D) : 0;
+    const int64_t part_floats = (int64_t)n_split * split_tiles * br * (D + 1);
+    if (workspace_bytes < vt_bytes + part_floats * (int64_t)sizeof(float)) return JA_EINVAL;
+    if (!aligned16(o) || !aligned16(workspace)) return JA_EUNSUPPORTED;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
+    char* ws = static_cast<char*>(workspace);
+    void* vt = pack_v ? ws : nullptr;
+    float* o_part = reinterpret_cast<float*>(ws + vt_bytes);
+    float* lse_part = o_part + (int64_t)n_split * split_tiles * br * D;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t sim = simulated_hip_error();       // (test hook: nothing is launched)
+    if (sim != hipSuccess) return hip_status(sim);
+    if (pack_v) {
+        const hipError_t e = ja::launch_pack(n_streams, v, st.off, B, H, D, JA_LAYOUT_BHDN, ldv,
+                                             vt, hs);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(ja::launch_fwd_bf16_streams_splitkv(st, vt, ldv, B, H, (int)N, D,
+                                                          softmax_scale, n_split, slots, o_part,
+                                                          lse_part, o, lse, hs));
+}
+
 int joint_attn_quant_fp8(const void* q, const void* k, const void* vt, int B, int H, int64_t N,
                          int D, int64_t ldv, int mode, void* q8, void* k8, void* v8t,
                          float* q_scale, float* k_scale, float* v_scale, void* q_hi, void* k_hi,

@@ -86,6 +86,17 @@ hipError_t launch_fwd_bf16_streams(const StreamTable& st, int B, int H, int N, i
     return e != hipSuccess ? e : shape_ok(B, H, N, D);
 }
 
+hipError_t launch_fwd_bf16_streams_splitkv(const StreamTable& st, const void* vt, int64_t ldv,
+                                           int B, int H, int N, int D, float, int n_split,
+                                           int slots, float* o_part, float* lse_part, void* o,
+                                           float*, hipStream_t) {
+    if (!o || n_split < 1 || slots != splitkv_slots(D) || !o_part || !lse_part ||
+        (vt && ldv < N))
+        return hipErrorInvalidValue;
+    const hipError_t e = table_ok(st, N);
+    return e != hipSuccess ? e : shape_ok(B, H, N, D);
+}
+
 hipError_t launch_quant_fp8(const void*, const void*, const void*, int B, int H, int N, int D,
                             int64_t ldv, int mode, void*, void*, void*, float*, float*, float*,
                             void* q_hi, void* k_hi, int32_t* hi_idx, float* ch_amax,

@@ -149,6 +149,47 @@ def test_fwd_streams_validation(lib):
     assert st == 0 and offs == [0, 0, 0, 0]
 
 
+def test_streams_splitkv_validation(lib, monkeypatch):
+    fake = 0x10000
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    ws_query = lib.joint_attn_fwd_bf16_streams_splitkv_workspace
+    # the workspace: the split partials, plus (pack_v = 1) the V^T copy, 256-byte rounded
+    part = lib.joint_attn_fwd_bf16_splitkv_workspace(1, 2, 300, 128, 3)
+    vt = -(-(1 * 2 * 128 * 304 * 2) // 256) * 256
+    assert ws_query(1, 2, 300, 128, 3, 0) == part
+    assert ws_query(1, 2, 300, 128, 3, 1) == part + vt
+    assert ws_query(1, 2, 300, 128, 3, 2) == -1 and ws_query(1, 2, 300, 96, 3, 0) == -1
+
+    def call(lens=(100, 200), n_split=3, pack_v=1, ws=fake, ws_bytes=None, o=fake, D=128,
+             q=None):
+        two = (P * 2)(*(q or [fake, fake]))
+        ln = (I64 * 2)(*lens)
+        offs = (I64 * 3)()
+        need = ws_query(1, 2, sum(lens), D, max(n_split, 1), pack_v if pack_v in (0, 1) else 0)
+        st = lib.joint_attn_fwd_bf16_streams_splitkv(
+            2, two, two, two, ln, 1, 2, D, 0.1, n_split, pack_v, ws,
+            need if ws_bytes is None else ws_bytes, o, None, offs, None)
+        return st, list(offs)
+
+    assert call(n_split=0)[0] == 1 and call(n_split=65)[0] == 1
+    assert call(pack_v=2)[0] == 1 and call(pack_v=-1)[0] == 1
+    assert call(ws=None)[0] == 1 and call(o=None)[0] == 1
+    assert call(ws=fake + 8)[0] == 2 and call(o=fake + 2)[0] == 2
+    assert call(D=96)[0] == 2
+    assert call(q=[fake, None])[0] == 1                                   # NULL non-empty q
+    # a workspace one byte short of the V^T copy plus the partials
+    need = ws_query(1, 2, 300, 128, 3, 1)
+    assert call(ws_bytes=need - 1)[0] == 1
+    # too small for the V^T copy is still enough without it (it passes validation and
+    # reaches the launch, which the library's failure hook refuses: nothing is launched)
+    monkeypatch.setenv("JOINT_ATTN_SIMULATE_HIP_ERROR", "98")
+    assert call(pack_v=0, ws_bytes=ws_query(1, 2, 300, 128, 3, 0))[0] == 3
+    monkeypatch.delenv("JOINT_ATTN_SIMULATE_HIP_ERROR")
+    # empty streams: a successful no-op that reports the offsets
+    st, offs = call(lens=(0, 0), ws=None, o=None)
+    assert st == 0 and offs == [0, 0, 0]
+
+
 def test_quant_streams_validation(lib):
     fake = 0x10000
     P, I64 = ctypes.c_void_p, ctypes.c_int64
@@ -283,6 +324,10 @@ def test_launch_failure_is_reported(lib, monkeypatch):
             fake, fake, fake, 1, 2, N, 128, ldv, 0.1, 2, fake, None, None),
         "fwd_bf16_streams": lambda: lib.joint_attn_fwd_bf16_streams(
             2, two, two, two, lens, 1, 2, 128, 0.1, fake, None, offs, None),
+        "fwd_bf16_streams_splitkv": lambda: lib.joint_attn_fwd_bf16_streams_splitkv(
+            2, two, two, two, lens, 1, 2, 128, 0.1, 2, 1, fake,
+            lib.joint_attn_fwd_bf16_streams_splitkv_workspace(1, 2, N, 128, 2, 1), fake, None,
+            offs, None),
         "quant_fp8": lambda: lib.joint_attn_quant_fp8(
             fake, fake, fake, 1, 2, N, 128, ldv, 1, fake, fake, fake, fake, fake, fake, fake,
             fake, fake, fake, None),
@@ -345,6 +390,13 @@ def test_valid_calls_reach_the_launchers(lib, monkeypatch):
                                                            n_split, fake, fake, None) == 0
         assert lib.joint_attn_fwd_bf16_streams(2, two, two, two, lens, B, H, D, 0.1, fake,
                                                None, offs, None) == 0
+        for n_split in (1, 2, 5):
+            for pack_v in (0, 1):
+                ws = lib.joint_attn_fwd_bf16_streams_splitkv_workspace(B, H, N, D, n_split,
+                                                                       pack_v)
+                assert lib.joint_attn_fwd_bf16_streams_splitkv(
+                    2, two, two, two, lens, B, H, D, 0.1, n_split, pack_v, fake, ws, fake,
+                    None, offs, None) == 0
         for mode in (0, 1):
             assert lib.joint_attn_quant_fp8(fake, fake, fake, B, H, N, D, ldv, mode, fake, fake,
                                             fake, fake, fake, fake, fake, fake, fake, fake,
