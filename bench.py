@@ -57,10 +57,10 @@ PEAK_HBM_GBS = 8000.0
 # change reports null.
 MEASURED_TRAFFIC = {
     "workload": "t2i_2048_bf16",
-    "bytes": 1898099395,
+    "bytes": 1898158669,
     "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/splitkv_merge.h",
                 "joint_attention_amd/csrc/ja_device.h"),
-    "sha256_16": "17f063fbb50fe0be",
+    "sha256_16": "37582b1d2ae27fa3",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
 

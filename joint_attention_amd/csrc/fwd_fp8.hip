@@ -391,6 +391,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
         t_begin = (int)((int64_t)split * all / n_split);
         nkt = (int)((int64_t)(split + 1) * all / n_split) - t_begin;
     }
+    // keys of this workgroup: [t_begin * BC, kend).  A range of one tile runs as two, the
+    // second masked out entirely (its P is exactly zero), so that every workgroup takes the
+    // one pipelined path (a separate one-tile path kept values live across both and made
+    // the compiler spill them)
+    const int kend = min(N, (t_begin + nkt) * BC);
+    nkt = max(nkt, 2);
     // RROWS: which of this workgroup's rows are listed (left to the row recomputation)
     __shared__ uint32_t rmask[RROWS ? NW : 1];
     if constexpr (RROWS) {
@@ -607,17 +613,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
 #pragma unroll
             for (int a = 0; a < 16; ++a) {
                 const int key = k0 + kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8);
-                if (key >= N) s[kb][a] = -INFINITY;
+                if (key >= kend) s[kb][a] = -INFINITY;
             }
     };
 
     // prologue: K_0, K_1 -> LDS; S_0; stage K_2 and V_0
     load_k(0);
     store_k(0);
-    if (nkt > 1) {
-        load_k(1);
-        store_k(1);
-    }
+    load_k(1);
+    store_k(1);
     __syncthreads();
     q_all(0, sA);
     load_k(min(2, nkt - 1));
@@ -634,14 +638,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
         floatx16 (&s_out)[KB] = P ? sA : sB;      // S_{j+1}
         intx8& p_out = P ? pB : pA;               // P_j
         intx8& p_in = P ? pA : pB;                // P_{j-1}
-        if (!HAS_QK && (N % BC) != 0) mask_tail(s_in, j);
+        // only a range's first tile (when it is also its last) and its last can reach kend
+        if ((!HAS_QK || !HAS_PV) && (t_begin + j + 1) * BC > kend) mask_tail(s_in, j);
         __syncthreads();
         if (HAS_QK) store_k(MY);
         store_v(MY);
         if (HAS_QK) load_k(min(j + 3, nkt - 1));
         load_v(min(j + 1, nkt - 1));
 
-        const float f = qsc2 * KSbh[((t_begin + j) * BC) / JA_QK_BLOCK];
+        // (the masked-out tile of a one-tile range may start past the last scale block)
+        const float f = qsc2 * KSbh[min(((t_begin + j) * BC) / JA_QK_BLOCK, nblk - 1)];
         float bias = 0.f, alpha = 1.f;
         bool grow = false;
         // raise M only if some score of the tile exceeds it (a wave-uniform branch)
@@ -680,13 +686,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
         auto load_op = [&](int st) -> intx8 {
             return st < NPV ? pv_operand(RD, st) : q_operand(RD, st - NPV);
         };
-        if constexpr (NST <= FIRST) {
-            check();
-#pragma unroll
-            for (int e = 0; e < NQUAD; ++e) exp_quad(s_in, p_out, e, f, bias, l);
-            if constexpr (HAS_PV) pv_all(RD, p_in);
-            if constexpr (HAS_QK) q_all(RD, s_out);
-        } else {
+        static_assert(NST > FIRST, "every iteration has a product to overlap");
+        {
             intx8 opnd[LEAD + 1];
 #pragma unroll
             for (int k = 0; k < LEAD; ++k) opnd[k] = load_op(step_id(k));
@@ -720,9 +721,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
     using T = std::true_type;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    if (nkt == 1) {
-        iteration(0, P0{}, F{}, F{});
-    } else {
+    {
         iteration(0, P0{}, F{}, T{});
         int j = 1;
         for (; j + 2 <= nkt - 1; j += 2) {

@@ -208,8 +208,8 @@ def test_fp8_tiny_every_row(mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("lens,D", [((1,), 128), ((63,), 64), ((100, 29), 128),
-                                    ((129, 64, 66), 128), ((127, 2, 0, 1), 64)])
+@pytest.mark.parametrize("lens,D", [((1,), 128), ((63,), 64), ((64,), 128), ((32, 32), 64),
+                                    ((100, 29), 128), ((129, 64, 66), 128), ((127, 2, 0, 1), 64)])
 def test_fp8_ragged_every_row(lens, D, mode):
     w = synth.custom("fp8r", B=2, H=2, D=D, stream_lens=lens, outliers=4 if D == 128 else 0,
                      seed=3 + sum(lens))
