@@ -53,7 +53,7 @@ namespace ja {
 namespace {
 
 #ifndef FP8_LEAD
-#define FP8_LEAD 1
+#define FP8_LEAD 2          // operand reads this many MFMA steps ahead
 #endif
 #ifndef FP8_NW128
 #define FP8_NW128 8
