@@ -233,6 +233,13 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
             return;
         }
     }
+    // keys of this workgroup end at kend (N, or the end of a split range).  A workgroup with
+    // one key tile runs two, the second masked out entirely (its P is exactly zero), so that
+    // every workgroup takes the one pipelined path (a separate one-tile path kept values
+    // live across both and cost registers).  (SPARSE: one visited tile is only possible in
+    // the last mask block, and its next tile starts at or past N.)
+    const int kend = (PARTIAL && part_wg) ? min(N, (t_begin + nkt) * BC) : N;
+    nkt = max(nkt, 2);
     auto tile_k0 = [&](int t) -> int {           // first key of (visited) key tile t
         if constexpr (SPARSE) return (ktab[t / TPB] & 0xFFFF) * JA_SPARSE_BLOCK + (t % TPB) * BC;
         return (t_begin + t) * BC;
@@ -603,22 +610,20 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
 #pragma unroll
                 for (int a = 0; a < 16; ++a) {
                     const int key = k0 + kb * 32 + 16 * (a / 8) + 8 * hh + (a % 8);
-                    if (key >= N) s[qb][kb][a] = -INFINITY;
+                    if (key >= kend) s[qb][kb][a] = -INFINITY;
                 }
     };
 
     // prologue: K_0, K_1 -> LDS; S_0; (register path) stage K_2 and V_0
     if constexpr (DMA) {
         dma_k(0, sk0);
-        if (nkt > 1) dma_k(1, sk1);
+        dma_k(1, sk1);
         dma_wait();
     } else {
         load_k(0);
         store_k(sk0);
-        if (nkt > 1) {
-            load_k(1);
-            store_k(sk1);
-        }
+        load_k(1);
+        store_k(sk1);
     }
     __syncthreads();
     qk_all(sk0, sA);
@@ -643,7 +648,8 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         floatx16 (&s_out)[QB][KB] = P ? sA : sB;   // S_{j+1}
         bf16x8 (&p_out)[QB][2 * KB] = P ? pB : pA; // P_j
         bf16x8 (&p_in)[QB][2 * KB] = P ? pA : pB;  // P_{j-1}
-        if (!HAS_QK && (N % BC) != 0) mask_tail(s_in, j);
+        // only the first tile (when it is also the last) and the last can reach kend
+        if ((!HAS_QK || !HAS_PV) && tile_k0(j) + BC > kend) mask_tail(s_in, j);
         dma_wait();
         __syncthreads();
         // DMA: K_{j+2} and V_j go straight to the slots freed by the barrier and land
@@ -717,15 +723,8 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
         auto load_op = [&](int st) -> bf16x8 {
             return st < NPV ? pv_operand(rd_v, st) : qk_operand(rd_k, st - NPV);
         };
-        if constexpr (NST <= FIRST) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) check(qb);
-#pragma unroll
-            for (int e = 0; e < NEXP; ++e) exp_pair(s_in, p_out, e, nm, l);
-            if constexpr (HAS_PV) pv_all(rd_v, p_in);
-            if constexpr (HAS_QK) qk_all(rd_k, s_out);
-            if constexpr (GV) transpose_write(vtr, my_v);
-        } else {
+        static_assert(NST > FIRST, "every iteration has products to overlap");
+        {
             bf16x8 opnd[LEAD + 1];
 #pragma unroll
             for (int k = 0; k < LEAD; ++k) opnd[k] = load_op(step_id(k));
@@ -766,9 +765,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     using T = std::true_type;
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
-    if (nkt == 1) {
-        iteration(0, P0{}, F{}, F{});
-    } else {
+    {
         iteration(0, P0{}, F{}, T{});
         int j = 1;
         for (; j + 2 <= nkt - 1; j += 2) {
