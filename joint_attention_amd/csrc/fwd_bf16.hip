@@ -177,16 +177,24 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     //      per query block of the workgroup), compacted by wave 0 with ballots
     constexpr int TPB = JA_SPARSE_BLOCK / BC;    // key tiles per mask block
     __shared__ int ktab[SPARSE ? JA_SPARSE_MAX_N / JA_SPARSE_BLOCK : 1];
-    __shared__ int ktab_n;
+    __shared__ int ktab_n, ktab_rot;
     int sp_group = 0;                            // this wave's query block in the workgroup
+    // SPARSE: the visit starts at the first active block at or past 2 x (first query block)
+    // and wraps around.  Workgroups that run together on an XCD hold neighbouring query
+    // blocks, so they move through the key blocks together and share them in L2 (in the
+    // given order every one starts at block 0 and they drift apart).  A workgroup that
+    // sees every block keeps the plain order; a last block that runs past N stays last
+    // (only the full blocks n_rot rotate), so that only the last tiles need the tail mask.
+    int rot = 0, n_rot = 0;
     if constexpr (SPARSE) {
         constexpr int QBW = BR / JA_SPARSE_BLOCK;
         static_assert(QBW >= 1 && QBW * JA_SPARSE_BLOCK == BR, "workgroup rows per mask block");
         const int nb = (N + JA_SPARSE_BLOCK - 1) / JA_SPARSE_BLOCK;
         const int qb0 = qt * QBW;
+        const int start = (2 * qb0) % nb;
         sp_group = (w * QB * 32) / JA_SPARSE_BLOCK;
         if (w == 0) {
-            int count = 0;
+            int count = 0, below_start = 0;
             for (int base = 0; base < nb; base += 64) {
                 const int kb = base + lane;
                 int flags = 0;
@@ -197,6 +205,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                             flags |= 1 << g;
                 }
                 const uint64_t bal = __ballot(flags != 0);
+                below_start += __popcll(__ballot(flags != 0 && kb < start));
                 if (flags) {
                     const int below = __builtin_amdgcn_mbcnt_hi(
                         (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
@@ -204,10 +213,17 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
                 }
                 count += __popcll(bal);
             }
-            if (lane == 0) ktab_n = count;
+            if (lane == 0) {
+                ktab_n = count;
+                ktab_rot = below_start;
+            }
         }
         __syncthreads();
         const int nact = ktab_n;
+        const bool tail_last = nact > 0 && (N % JA_SPARSE_BLOCK) != 0 &&
+                               (ktab[nact - 1] & 0xFFFF) == nb - 1;
+        n_rot = nact - (tail_last ? 1 : 0);
+        rot = (nact < nb && ktab_rot < n_rot) ? ktab_rot : 0;
         nkt = nact * TPB;
         if (nact > 0) {
             // only the last mask block runs past N: drop its tiles that start at or past N
@@ -241,11 +257,25 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const int kend = (PARTIAL && part_wg) ? min(N, (t_begin + nkt) * BC) : N;
     nkt = max(nkt, 2);
     auto tile_k0 = [&](int t) -> int {           // first key of (visited) key tile t
-        if constexpr (SPARSE) return (ktab[t / TPB] & 0xFFFF) * JA_SPARSE_BLOCK + (t % TPB) * BC;
+        if constexpr (SPARSE) {
+            int e = t / TPB;
+            if (e < n_rot) {
+                e += rot;
+                if (e >= n_rot) e -= n_rot;
+            }
+            return (ktab[e] & 0xFFFF) * JA_SPARSE_BLOCK + (t % TPB) * BC;
+        }
         return (t_begin + t) * BC;
     };
     auto tile_on = [&](int t) -> bool {          // SPARSE: this wave's query block sees tile t
-        if constexpr (SPARSE) return ((ktab[t / TPB] >> (16 + sp_group)) & 1) != 0;
+        if constexpr (SPARSE) {
+            int e = t / TPB;
+            if (e < n_rot) {
+                e += rot;
+                if (e >= n_rot) e -= n_rot;
+            }
+            return ((ktab[e] >> (16 + sp_group)) & 1) != 0;
+        }
         return true;
     };
 
