@@ -196,10 +196,12 @@ int joint_attn_fwd_bf16_splitkv_suggest(int B, int H, int64_t N, int D) {
     // fixed cost per workgroup (prologue, epilogue), plus reading its fp32 partials back
     // in the merge (at ~4 TB/s, against a round of ~1 PFLOP/s work; their writes overlap
     // the forward).  A split
-    // is suggested only where it should save over a tenth of a round (measured at 2048^2
-    // and 1024^2 T2I and head-split shares of 2048^2).
+    // is suggested only where it should save over a twentieth of a round (measured on 9
+    // shapes from 1024^2 T2I to 2048^2 I2I and head-split shares of 2048^2: at this
+    // threshold the pick is the fastest split measured or within 0.7 % of it; at a tenth, a
+    // grid of one partial round, 198 tiles, kept the plain forward, 17 % slower than 5 ranges).
     const double round_s = (double)slots * br * tiles * 32.0 * 4.0 * D / 1.0e15;
-    double best = 0.9;
+    double best = 0.95;
     int best_s = 1;
     for (int s = 2; s <= 16 && s <= tiles; ++s) {
         const double rounds = (double)((tail * s + slots - 1) / slots);

@@ -236,7 +236,7 @@ def test_splitkv_sizes_and_validation(lib):
     # without a GPU the plan assumes 256 slots (one 8-wave workgroup per CU)
     assert sug(2, 24, 4608, 128) == 2           # 864 tiles: 96 in the last round
     assert sug(1, 6, 16896, 128) == 7           # 396 tiles: 140 in the last round
-    assert sug(1, 3, 16896, 128) == 1           # 198 tiles, all in one round: not worth it
+    assert sug(1, 3, 16896, 128) == 5           # 198 tiles, all in one round
     assert sug(1, 8, 16896, 128) == 16          # 528 tiles: 16 in the last round
     assert sug(2, 24, 16896, 128) == 5          # 3168 tiles: 96 in the last round
     assert sug(2, 24, 512, 128) == 1            # 16 key tiles: the fixed cost dominates
