@@ -290,6 +290,8 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
     static_assert(NT % (D / 8) == 0 && (JA_QK_BLOCK * D / 8) % NT == 0, "chunk mapping");
     __shared__ float red[NT / 64];
     __shared__ uint32_t mask[D / 32];
+    // SPLIT: the block's kept values / scale, [row][rank of the channel among the kept]
+    __shared__ uint4 hi_tab[SPLIT ? JA_QK_BLOCK * JA_HI_CHANNELS / 8 : 1];
     const uint16_t* x = blockIdx.z ? k : q;
     uint8_t* y = blockIdx.z ? k8 : q8;
     float* sc = blockIdx.z ? ks : qs;
@@ -331,9 +333,12 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
 
     // NT is a multiple of D / 8, so a thread's chunks all cover the same 8 channels
     uint32_t keep = 0;
+    int rank0 = 0;                                      // kept channels below this thread's 8
     if (SPLIT) {
         const int c0 = (threadIdx.x % (D / 8)) * 8;
         keep = (mask[c0 / 32] >> (c0 % 32)) & 0xFFu;
+        for (int w = 0; w < c0 / 32; ++w) rank0 += __popc(mask[w]);
+        rank0 += __popc(mask[c0 / 32] & ((1u << (c0 % 32)) - 1u));
     }
     uint2* dst = reinterpret_cast<uint2*>(y + base);
     const float scale = ldexpf(1.f, e);
@@ -342,6 +347,18 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
         const int c = threadIdx.x + i * NT;
         const uint2 code = quant8(reg[i], inv, keep);
         if (c < nch) dst[c] = code;
+        if (SPLIT && keep) {
+            // hi_idx is ascending, so a kept channel's slot is its rank among the kept
+            uint16_t* row = reinterpret_cast<uint16_t*>(hi_tab) + (c / (D / 8)) * JA_HI_CHANNELS;
+            const uint32_t w[4] = {reg[i].x, reg[i].y, reg[i].z, reg[i].w};
+            int j = rank0;
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2)
+                if (keep & (1u << e2)) {
+                    const float v = __uint_as_float(e2 % 2 ? w[e2 / 2] & 0xFFFF0000u : w[e2 / 2] << 16);
+                    row[j++] = (uint16_t)(__float_as_uint(v * inv) >> 16);  // exact 2^-e rescale
+                }
+        }
         if constexpr (ERR) {
             // residuals of this chunk's 8 channels; the D / 8 chunks of a token sit in
             // D / 8 consecutive lanes of one wave
@@ -363,14 +380,11 @@ __global__ __launch_bounds__(NT) void quant_qk_kernel(const uint16_t* __restrict
         }
     }
     if (SPLIT) {
-        uint16_t* hi = (blockIdx.z ? k_hi : q_hi) + ((int64_t)bh * N + t0) * JA_HI_CHANNELS;
-        const int32_t* sel = hi_idx + (int64_t)bh * JA_HI_CHANNELS;
-        for (int i = threadIdx.x; i < rows * JA_HI_CHANNELS; i += NT) {
-            const int r = i / JA_HI_CHANNELS, j = i % JA_HI_CHANNELS;
-            const float v =
-                __uint_as_float((uint32_t)row_ptr(rm, st, xs, b, h, H, D, t0, r)[sel[j]] << 16);
-            hi[i] = (uint16_t)(__float_as_uint(v * inv) >> 16);   // exact power-of-two rescale
-        }
+        // rows x 16 values, contiguous in q_hi / k_hi: copied out 16 bytes a lane
+        __syncthreads();
+        uint4* hi = reinterpret_cast<uint4*>((blockIdx.z ? k_hi : q_hi) +
+                                             ((int64_t)bh * N + t0) * JA_HI_CHANNELS);
+        for (int i = threadIdx.x; i < rows * JA_HI_CHANNELS / 8; i += NT) hi[i] = hi_tab[i];
     }
 }
 
