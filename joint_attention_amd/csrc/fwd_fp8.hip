@@ -23,12 +23,13 @@
 // the lanes served together must hit distinct 4-byte banks of that window.
 //
 // Softmax.  The running maximum M is an integer (base 2), raised only when some score
-// of the tile exceeds it (a wave-uniform ballot; the two wave halves are combined and O
-// rescaled only then), so every rescale is an exact power of two and P's e4m3 rounding
-// does not depend on the order keys arrive in.  P is stored as e4m3(2^8 * 2^(t - M)),
-// at most 256, with the 2^8 folded into the exponent; the row sum takes the same
-// unrounded fp32 numerators and the 2^8 cancels in O = acc / l.  The per-channel V
-// scale is applied in the epilogue.
+// of the tile exceeds it by more than 0.75 (a wave-uniform ballot; the two wave halves
+// are combined and O rescaled only then), and then to one above the tile's integer
+// maximum.  Every rescale is an exact power of two, and above e4m3's subnormal range P's
+// rounding depends neither on M nor on the order keys arrive in.  P is stored as
+// e4m3(2^8 * 2^(t - M)), below 2^8.75, with the 2^8 folded into the exponent; the row
+// sum takes the same unrounded fp32 numerators and the 2^8 cancels in O = acc / l.  The
+// per-channel V scale is applied in the epilogue.
 //
 // Split mode (HI): the 16 kept channels of Q and K (bf16, already divided by their
 // power-of-two block scales) add one v_mfma_f32_32x32x16_bf16 per 32x32 score block
@@ -38,9 +39,10 @@
 // runs unchanged on the codes and writes O and lse; fwd_fp8_keyfix_kernel then replaces,
 // in every row, each listed key's code term by its exact-value term: with the row's
 // total L = e^lse it adds (e4m3(2^(8 + t~ - M')) - e4m3(2^(8 + t^ - M'))) 2^(M' - 8) v
-// to L O and 2^t~ - 2^t^ to L, for an integer M' (the e4m3 rounding of a power-of-two
-// shift is the same for any integer M below the subnormal range, so the loop's code
-// term cancels to within 2^-14 of the row maximum).  Workgroups appended to the main grid
+// to L O and 2^t~ - 2^t^ to L, for an integer M' (shifting by an integer power of two
+// leaves e4m3 rounding unchanged while the value stays above the subnormal range, so
+// the loop's code term cancels exactly for every key whose weight is within 2^-12 of
+// the row maximum's, the loop's M being at most two above that maximum).  Workgroups appended to the main grid
 // (repair_rows) recompute the listed query rows from their exact values; the main and the
 // correction kernels leave those rows alone.
 #include <type_traits>
@@ -57,6 +59,15 @@ namespace {
 #endif
 #ifndef FP8_NW128
 #define FP8_NW128 8
+#endif
+// the running maximum M rises only when some logit exceeds it by more than FP8_GROW_SLACK
+// (P = e4m3(2^(8 + t - M)) then stays below 2^8.75 < 448), and then to FP8_GROW_HEADROOM
+// above the tile's integer maximum, so that fewer tiles pay for a rescale of O
+#ifndef FP8_GROW_SLACK
+#define FP8_GROW_SLACK 0.75f
+#endif
+#ifndef FP8_GROW_HEADROOM
+#define FP8_GROW_HEADROOM 1.f
 #endif
 
 __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
@@ -658,10 +669,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_fp8_kernel(
 #pragma unroll
                 for (int a = 0; a < 16; ++a) mx = fmaxf(mx, s_in[kb][a]);
             const float tmax = mx * f;
-            grow = __ballot(tmax > m) != 0;
+            grow = __ballot(tmax > m + FP8_GROW_SLACK) != 0;
             if (grow) {
                 asm volatile("");
-                const float m_new = fmaxf(m, ceilf(wave_halves_max(tmax)));
+                const float m_new = fmaxf(m, ceilf(wave_halves_max(tmax)) + FP8_GROW_HEADROOM);
                 alpha = (m == -INFINITY) ? 0.f : ldexpf(1.f, (int)(m - m_new));
                 m = m_new;
                 l *= alpha;
