@@ -42,12 +42,13 @@ def _widen_f32(bits):
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _quant_both(w, mode, bh=None):
+def _quant_both(w, mode, bh=None, streams=None):
     """Quantise on the GPU and fetch the results, restricted to slice (b, h) if given,
-    together with the matching token-major host inputs."""
+    together with the matching token-major host inputs (the workload's seeded streams
+    unless `streams` is given)."""
     import joint_attention_amd as ja
     import torch
-    st = host_streams(w)
+    st = host_streams(w) if streams is None else streams
     q, k, vt, offs = device_packed(st)
     t = ja.joint_attn_quant_fp8(q, k, vt, mode)
     torch.cuda.synchronize()
@@ -132,14 +133,14 @@ def test_quant_split_channels_cover_the_outliers():
             assert set(st.outlier_channels.tolist()) <= set(res["got"]["hi_idx"][b, h].tolist())
 
 
-def _fwd_fp8(w, mode, sel=None, n_split=None):
+def _fwd_fp8(w, mode, sel=None, n_split=None, streams=None):
     """GPU fp8 forward (the split-KV call when n_split is given) vs the oracle's fp8
     attention and its fp64 attention.  The oracle side runs per (b, h) slice (the method
     is independent per slice), so full-size workloads only quantise the slices that the
     sampled rows touch."""
     import joint_attention_amd as ja
     import torch
-    res = _quant_both(w, mode)
+    res = _quant_both(w, mode, streams=streams)
     t = res["dev"][3]
     scale = 1.0 / math.sqrt(w.D)
     if n_split is None:
@@ -240,6 +241,51 @@ def test_fp8_t2i_2048_sampled_rows(mode):
     w = synth.WORKLOADS["t2i_2048_fp8"]
     sel = synth.row_sample(w, 256, seed=12, n_pairs=3)
     _assert_fp8("fp8 t2i_2048", mode, *_fwd_fp8(w, mode, sel), outliers=True)
+
+
+def _drifting_streams(w, pattern, seed):
+    """Streams whose logits drift along the keys, so that each row's running maximum moves
+    the way `pattern` says: "rise" (slowly, by about a third of a base-2 unit per 64-key
+    tile, with two steps of two to three units), "fall" (largest at the first keys) or
+    "jump" (flat, then a step of about ten units over the last 40 keys).  Q and K share a direction u;
+    the keys' component along it follows the pattern, plus noise."""
+    rng = np.random.default_rng(seed)
+    n, shape = w.N, (w.B, w.N, w.H, w.D)
+    u = rng.standard_normal(w.D)
+    u /= np.linalg.norm(u)
+    if pattern == "rise":
+        a = np.linspace(0.0, 8.0, n)
+        a[n // 3:] += 6.0
+        a[2 * n // 3:] += 9.0
+    elif pattern == "fall":
+        a = np.linspace(20.0, 0.0, n)
+    else:
+        a = np.zeros(n)
+        a[n - 40:] = 30.0
+    q = 0.5 * rng.standard_normal(shape) + 3.0 * u
+    k = 0.5 * rng.standard_normal(shape) + a[None, :, None, None] * u
+    v = rng.standard_normal(shape)
+    st = synth.Streams(w)
+    t0 = 0
+    for L in w.stream_lens:
+        for dst, x in ((st.q, q), (st.k, k), (st.v, v)):
+            dst.append(synth.f32_to_bf16_bits(np.ascontiguousarray(x[:, t0:t0 + L], np.float32)))
+        t0 += L
+    return st
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("pattern", ["rise", "fall", "jump"])
+def test_fp8_drifting_maximum_every_row(pattern, mode):
+    # the running maximum rises by less than the kernel's slack in many tiles and by
+    # several units twice, never rises after the first tile, or rises once by about ten
+    # units at the end: every row against the oracle's fp8 attention (M = ceil(max t))
+    w = synth.custom("fp8drift", B=1, H=2, D=128, stream_lens=(64, 589), outliers=0, seed=31)
+    st = _drifting_streams(w, pattern, seed=31)
+    _assert_fp8("fp8 drifting maximum %s" % pattern, mode, *_fwd_fp8(w, mode, streams=st),
+                outliers=False)
+    _assert_fp8("fp8 drifting maximum %s, split-KV" % pattern, mode,
+                *_fwd_fp8(w, mode, n_split=3, streams=st), outliers=False)
 
 
 def test_fp8_deterministic():
