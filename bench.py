@@ -83,15 +83,28 @@ def log(msg):
 
 class ClockSampler:
     """Samples the GPU's current shader clock (the starred level of the kernel driver's
-    pp_dpm_sclk) every `period` seconds in a background thread.  Reports None where the
-    file is missing.  (amdsmi's gpu_metrics refreshes about once a second.)"""
+    pp_dpm_sclk) every `period` seconds in a background thread, and the board power
+    (hwmon power1_input) beside it.  Reports None where the files are missing.  (amdsmi's
+    gpu_metrics refreshes about once a second.)"""
 
     def __init__(self, period: float = 0.005):
         import threading
         self.period, self.samples, self.err = period, [], None
+        self.power, self.power_cap = [], None
         self._stop = threading.Event()
         self._thread = None
         self.path = self._find()
+        self.power_path = None
+        if self.path is not None:
+            import glob
+            hw = sorted(glob.glob(os.path.join(os.path.dirname(self.path), "hwmon", "hwmon*")))
+            if hw and os.path.exists(os.path.join(hw[0], "power1_input")):
+                self.power_path = os.path.join(hw[0], "power1_input")
+                try:
+                    with open(os.path.join(hw[0], "power1_cap")) as f:
+                        self.power_cap = float(f.read()) / 1e6
+                except Exception:
+                    self.power_cap = None
 
     def _find(self):
         import glob
@@ -124,6 +137,9 @@ class ClockSampler:
                 v = self._read()
                 if v is not None and v > 0:
                     self.samples.append(v)
+                if self.power_path is not None:
+                    with open(self.power_path) as f:
+                        self.power.append(float(f.read()) / 1e6)
             except Exception as e:
                 self.err = repr(e)
                 return
@@ -146,12 +162,16 @@ class ClockSampler:
         if not self.samples:
             return {"clock_ghz": None, "clock_source": "unavailable (%s)" % self.err}
         import statistics
-        return {"clock_ghz": round(statistics.fmean(self.samples) / 1000.0, 4),
-                "clock_ghz_min": round(min(self.samples) / 1000.0, 4),
-                "clock_ghz_max": round(max(self.samples) / 1000.0, 4),
-                "clock_samples": len(self.samples),
-                "clock_source": "%s (current level), sampled every %d ms"
-                                % (self.path, int(self.period * 1000))}
+        r = {"clock_ghz": round(statistics.fmean(self.samples) / 1000.0, 4),
+             "clock_ghz_min": round(min(self.samples) / 1000.0, 4),
+             "clock_ghz_max": round(max(self.samples) / 1000.0, 4),
+             "clock_samples": len(self.samples),
+             "clock_source": "%s (current level), sampled every %d ms"
+                             % (self.path, int(self.period * 1000))}
+        if self.power:
+            r["board_power_w"] = round(statistics.fmean(self.power), 1)
+            r["board_power_cap_w"] = self.power_cap
+        return r
 
 
 def sustained_clock(step, ms_per_step: float, seconds: float = 1.0, settle: float = 0.3):
@@ -576,6 +596,37 @@ def main():
             "frac_of_fp8_peak": round(flops / (f8r * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
         }
         del t8r
+
+    # context for the roofline: a plain library GEMM (torch.matmul -> hipBLASLt) on random
+    # bf16 operands, under the same board power limit, and the clock and power it runs at
+    log("timing the reference bf16 GEMM (torch.matmul, 8192^3)")
+    g_n = 8192
+    ga = torch.randn((g_n, g_n), device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    gb = torch.randn((g_n, g_n), device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    gc = torch.empty((g_n, g_n), device="cuda", dtype=torch.bfloat16)
+
+    def step_gemm(rec=True):
+        torch.matmul(ga, gb, out=gc)
+        return []
+
+    for _ in range(5):
+        step_gemm()
+    torch.cuda.synchronize()
+    g_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    g_ev[0].record()
+    for _ in range(20):
+        step_gemm()
+    g_ev[1].record()
+    torch.cuda.synchronize()
+    g_ms = g_ev[0].elapsed_time(g_ev[1]) / 20
+    g_tf = 2.0 * g_n ** 3 / (g_ms * 1e-3) / 1e12
+    out["reference_gemm"] = {
+        "op": "torch.matmul, bf16 %d x %d x %d, random normal operands (vendor GEMM)" % (g_n, g_n, g_n),
+        "ms": round(g_ms, 4), "tflops": round(g_tf, 1),
+        "frac_of_bf16_peak": round(g_tf / PEAK_BF16_TFLOPS, 4),
+        "timed_forward_over_gemm": round(achieved / g_tf, 4)}
+    out["reference_gemm"].update(sustained_clock(step_gemm, g_ms))
+    del ga, gb, gc
 
     if not args.skip_shapes:
         # forward-only throughput of the other shapes: 1024^2 T2I and 2048^2 I2I from the
