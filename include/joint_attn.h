@@ -63,6 +63,7 @@ extern "C" {
 
 #define JA_SPARSE_BLOCK 128       /* query rows and keys per block of the sparse mask */
 #define JA_SPARSE_MAX_N 131072    /* longest sequence of joint_attn_fwd_bf16_sparse */
+#define JA_SPARSE_PLAN_MAX 2097152 /* B * H * ceil(N / JA_SPARSE_BLOCK) limit of a sparse plan */
 
 #define JA_FP8_PLAIN 0      /* fp8 mode 0: every Q/K channel in e4m3 */
 #define JA_FP8_SPLIT 1      /* fp8 mode 1: JA_HI_CHANNELS outlier channels in bf16 */
@@ -138,6 +139,46 @@ int joint_attn_fwd_bf16_sparse(const void *q, const void *k, const void *vt,
                                int B, int H, int64_t N, int D, int64_t ldv,
                                const uint8_t *block_mask, float softmax_scale,
                                void *o, float *lse, void *stream);
+
+/*
+ * joint_attn_sparse_plan -- the order in which joint_attn_fwd_bf16_sparse_planned starts
+ * the workgroups of a block mask (one per 128-row query block; the operation is that of
+ * joint_attn_fwd_bf16_sparse, which this only schedules).  The workgroups are dealt to
+ * the GPU's eight XCDs in eight contiguous shares; within each share the query blocks
+ * whose mask row allows more than twice the share's mean number of key blocks (in a
+ * joint sequence, the text rows, which see every block) are moved to the front, the
+ * others keep their order.  Long workgroups then start first instead of trailing the
+ * share, while consecutive short ones still share one (b, h)'s keys in L2.
+ *
+ *   block_mask   device uint8 [B][H][nb][nb] as for joint_attn_fwd_bf16_sparse
+ *   plan         device int32 buffer of at least joint_attn_sparse_plan_bytes() bytes,
+ *                owned by the caller, 4-byte aligned; receives a permutation of
+ *                0 .. B*H*nb - 1 (entry p = the query block, b*H*nb + h*nb + i, that
+ *                workgroup position p runs).  Its contents on entry do not matter.
+ *   B*H*nb       at most JA_SPARSE_PLAN_MAX (JA_EUNSUPPORTED otherwise); N at most
+ *                JA_SPARSE_MAX_N
+ * Two kernels on `stream`; a plan stays valid for as long as the mask and B, H, N do not
+ * change, so one plan can serve every forward over that mask.
+ */
+int64_t joint_attn_sparse_plan_bytes(int B, int H, int64_t N);
+int joint_attn_sparse_plan(const uint8_t *block_mask, int B, int H, int64_t N,
+                           int32_t *plan, int64_t plan_bytes, void *stream);
+
+/*
+ * joint_attn_fwd_bf16_sparse_planned -- joint_attn_fwd_bf16_sparse with its workgroups
+ * started in the order of a plan from joint_attn_sparse_plan for the same block_mask,
+ * B, H and N.  Same arguments, plus:
+ *   plan         device int32 [B*H*nb], read only.  Each workgroup computes its query
+ *                block exactly as the unplanned call does, so the results are bit for bit
+ *                those of joint_attn_fwd_bf16_sparse.  A buffer that is not such a
+ *                permutation is not detected: entries are clamped to the valid range, so
+ *                reads and writes stay inside the tensors, but rows of query blocks it
+ *                omits are left unwritten.
+ */
+int joint_attn_fwd_bf16_sparse_planned(const void *q, const void *k, const void *vt,
+                                       int B, int H, int64_t N, int D, int64_t ldv,
+                                       const uint8_t *block_mask, const int32_t *plan,
+                                       float softmax_scale, void *o, float *lse, void *stream);
 
 /*
  * joint_attn_fwd_bf16_splitkv -- joint_attn_fwd_bf16 with the query tiles of the last,

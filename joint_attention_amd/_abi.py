@@ -23,6 +23,7 @@ JA_MAX_HEAD_ELEMS = 1 << 30
 JA_QK_BLOCK = 128
 JA_HI_CHANNELS = 16
 JA_SPARSE_BLOCK, JA_SPARSE_MAX_N = 128, 131072
+JA_SPARSE_PLAN_MAX = 2097152
 JA_FP8_PLAIN, JA_FP8_SPLIT, JA_FP8_REPAIR = 0, 1, 2
 JA_REPAIR_MAX_N = 131072
 JA_REPAIR_TILE = 64
@@ -30,6 +31,8 @@ JA_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("joint_attn_strerror", "joint_attn_last_hip_error", "joint_attn_vt_ld",
            "joint_attn_pack", "joint_attn_fwd_bf16", "joint_attn_fwd_bf16_sparse",
+           "joint_attn_sparse_plan_bytes", "joint_attn_sparse_plan",
+           "joint_attn_fwd_bf16_sparse_planned",
            "joint_attn_fwd_bf16_splitkv", "joint_attn_fwd_bf16_splitkv_workspace",
            "joint_attn_fwd_bf16_splitkv_suggest", "joint_attn_fwd_bf16_splitkv_noalloc",
            "joint_attn_fwd_bf16_streams", "joint_attn_fwd_bf16_streams_splitkv",
@@ -80,6 +83,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         h.joint_attn_fwd_bf16.argtypes = [P, P, P, I, I, I64, I, I64, F, P, P, P]
         h.joint_attn_fwd_bf16_sparse.restype = I
         h.joint_attn_fwd_bf16_sparse.argtypes = [P, P, P, I, I, I64, I, I64, P, F, P, P, P]
+        h.joint_attn_sparse_plan_bytes.restype = I64
+        h.joint_attn_sparse_plan_bytes.argtypes = [I, I, I64]
+        h.joint_attn_sparse_plan.restype = I
+        h.joint_attn_sparse_plan.argtypes = [P, I, I, I64, P, I64, P]
+        h.joint_attn_fwd_bf16_sparse_planned.restype = I
+        h.joint_attn_fwd_bf16_sparse_planned.argtypes = [P, P, P, I, I, I64, I, I64, P, P, F, P,
+                                                         P, P]
         h.joint_attn_fwd_bf16_splitkv_workspace.restype = I64
         h.joint_attn_fwd_bf16_splitkv_workspace.argtypes = [I, I, I64, I, I]
         h.joint_attn_fwd_bf16_splitkv_suggest.restype = I
@@ -242,6 +252,57 @@ def joint_attn_fwd_bf16_sparse(q, k, vt, block_mask, softmax_scale: float | None
                                            int(vt.shape[3]), block_mask.data_ptr(), scale,
                                            out.data_ptr(), _ptr(lse), _stream(q))
     _check("joint_attn_fwd_bf16_sparse", st)
+    return (out, lse) if return_lse else out
+
+
+def joint_attn_sparse_plan(block_mask, N: int, out=None):
+    """Dispatch plan of joint_attn_fwd_bf16_sparse_planned for a uint8 block mask
+    [B, H, nb, nb] (nb = ceil(N / JA_SPARSE_BLOCK)): an int32 tensor [B * H * nb]."""
+    torch = _torch()
+    _need(block_mask, torch.uint8, "block_mask", 4)
+    B, H, nb = int(block_mask.shape[0]), int(block_mask.shape[1]), -(-int(N) // JA_SPARSE_BLOCK)
+    if tuple(block_mask.shape) != (B, H, nb, nb):
+        raise ValueError("block_mask must be [B, H, %d, %d]" % (nb, nb))
+    nbytes = int(load().joint_attn_sparse_plan_bytes(B, H, int(N)))
+    if nbytes < 0:
+        raise ValueError("no plan for B=%d H=%d N=%d (limits JA_SPARSE_MAX_N, JA_SPARSE_PLAN_MAX)"
+                         % (B, H, N))
+    if out is None:
+        out = torch.empty((nbytes // 4,), dtype=torch.int32, device=block_mask.device)
+    _need(out, torch.int32, "out", 1)
+    st = load().joint_attn_sparse_plan(block_mask.data_ptr(), B, H, int(N), out.data_ptr(),
+                                       out.numel() * 4, _stream(block_mask))
+    _check("joint_attn_sparse_plan", st)
+    return out
+
+
+def joint_attn_fwd_bf16_sparse_planned(q, k, vt, block_mask, plan,
+                                       softmax_scale: float | None = None, out=None,
+                                       return_lse: bool = False):
+    """joint_attn_fwd_bf16_sparse with the workgroup order of joint_attn_sparse_plan
+    (same results, bit for bit).  plan: int32 [B * H * nb] from that call."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (vt, "vt")):
+        _need(t, torch.bfloat16, n, 4)
+    B, H, N, D = q.shape
+    nb = -(-N // JA_SPARSE_BLOCK)
+    _need(block_mask, torch.uint8, "block_mask", 4)
+    _need(plan, torch.int32, "plan", 1)
+    if tuple(block_mask.shape) != (B, H, nb, nb):
+        raise ValueError("block_mask must be [B, H, %d, %d]" % (nb, nb))
+    if plan.numel() != B * H * nb:
+        raise ValueError("plan must have B * H * nb = %d entries" % (B * H * nb))
+    if tuple(k.shape) != (B, H, N, D) or vt.shape[:3] != (B, H, D):
+        raise ValueError("k must match q; vt must be [B, H, D, ldv]")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((B, N, H, D), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out", 4)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if return_lse else None
+    st = load().joint_attn_fwd_bf16_sparse_planned(
+        q.data_ptr(), k.data_ptr(), vt.data_ptr(), B, H, N, D, int(vt.shape[3]),
+        block_mask.data_ptr(), plan.data_ptr(), scale, out.data_ptr(), _ptr(lse), _stream(q))
+    _check("joint_attn_fwd_bf16_sparse_planned", st)
     return (out, lse) if return_lse else out
 
 

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     const StreamTable st, const uint8_t* __restrict__ MASK, int H, int N, int64_t ldv, float c2,
     __bf16* __restrict__ O, float* __restrict__ LSE, int n_qtiles, int total,
     int n_split = 1, float* __restrict__ OP = nullptr, float* __restrict__ LP = nullptr,
-    int n_full = 0) {
+    int n_full = 0, const int32_t* __restrict__ ORDER = nullptr) {
     static_assert(GATHER >= 0 && GATHER <= 2, "gather mode");
     static_assert(!(SPARSE && (GATHER || PARTIAL)), "the block-sparse forward runs alone");
     constexpr bool GQK = GATHER != 0;            // Q and K read from the streams
@@ -150,6 +150,9 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
     // consecutive workgroups share (b, h); in PARTIAL those past n_full are the ranges of
     // one query tile
     int unit = wg, split = 0;
+    // SPARSE with a dispatch plan: position wg runs query block ORDER[wg] (clamped, so that
+    // a plan that is not a permutation can only leave rows unwritten, never reach outside)
+    if (SPARSE && ORDER != nullptr) unit = min(max(ORDER[wg], 0), total - 1);
     bool part_wg = false;
     if constexpr (PARTIAL) {
         if (wg >= n_full) {
@@ -865,7 +868,8 @@ __global__ __launch_bounds__(NW * 64, 8 / (NW * QB)) void fwd_bf16_kernel(
 template <int D, int NW, int QB, int BC, int GATHER, bool SPARSE = false>
 hipError_t launch_d(const void* q, const void* k, const void* vt, const StreamTable& st, int B,
                     int H, int N, int64_t ldv, float softmax_scale, void* o, float* lse,
-                    hipStream_t stream, const uint8_t* mask = nullptr) {
+                    hipStream_t stream, const uint8_t* mask = nullptr,
+                    const int32_t* order = nullptr) {
     constexpr int BR = NW * QB * 32;
     const int n_qtiles = (N + BR - 1) / BR;
     const int total = n_qtiles * B * H;
@@ -873,7 +877,7 @@ hipError_t launch_d(const void* q, const void* k, const void* vt, const StreamTa
                        dim3(NW * 64), 0, stream, static_cast<const __bf16*>(q),
                        static_cast<const __bf16*>(k), static_cast<const __bf16*>(vt), st, mask, H,
                        N, ldv, softmax_scale * kLog2e, static_cast<__bf16*>(o), lse, n_qtiles,
-                       total);
+                       total, 1, nullptr, nullptr, 0, order);
     return hipGetLastError();
 }
 
@@ -892,13 +896,110 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, 
 
 hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
                                   const uint8_t* mask, int B, int H, int N, int D, int64_t ldv,
-                                  float softmax_scale, void* o, float* lse, hipStream_t stream) {
+                                  float softmax_scale, void* o, float* lse, hipStream_t stream,
+                                  const int32_t* plan) {
+    // a plan entry names one workgroup: both head sizes run 128-row workgroups
+    static_assert(FWD_NW_SPARSE * FWD_QB * 32 == JA_SPARSE_BLOCK && 4 * FWD_QB * 32 == JA_SPARSE_BLOCK,
+                  "one workgroup per query block of the mask");
     const StreamTable none{};
     return D == 64 ? launch_d<64, 4, FWD_QB, FWD_BC, 0, true>(q, k, vt, none, B, H, N, ldv,
                                                                   softmax_scale, o, lse, stream,
-                                                                  mask)
+                                                                  mask, plan)
                    : launch_d<128, FWD_NW_SPARSE, FWD_QB, FWD_BC, 0, true>(
-                         q, k, vt, none, B, H, N, ldv, softmax_scale, o, lse, stream, mask);
+                         q, k, vt, none, B, H, N, ldv, softmax_scale, o, lse, stream, mask, plan);
+}
+
+namespace {
+
+// ---- dispatch plan of the block-sparse forward.  Workgroup position p (after xcd_remap)
+//      runs on XCD x for p in that XCD's share [c0, c0 + n) of the positions, in
+//      increasing p.  A query block whose mask row allows more than twice its share's mean
+//      number of key blocks (the text rows of a joint sequence see every block) is moved
+//      to the front of its share, the others keep their order: the long workgroups then
+//      start first instead of trailing the last (b, h) of a share, while consecutive
+//      short ones still share their (b, h)'s keys in L2.
+
+// pass 1: number of allowed key blocks of each query block (one wave per mask row)
+__global__ __launch_bounds__(256) void sparse_plan_count_kernel(const uint8_t* __restrict__ MASK,
+                                                                int nb, int total,
+                                                                int32_t* __restrict__ CNT) {
+    const int lane = threadIdx.x & 63;
+    const int u = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (u >= total) return;                      // wave-uniform
+    const uint8_t* row = MASK + (int64_t)u * nb;
+    int c = 0;
+    for (int base = 0; base < nb; base += 64) {
+        const int j = base + lane;
+        c += __popcll(__ballot(j < nb && row[j] != 0));
+    }
+    if (lane == 0) CNT[u] = c;
+}
+
+// pass 2: one workgroup per XCD share turns the counts (in PLAN) into the order, in place
+__global__ __launch_bounds__(1024) void sparse_plan_order_kernel(int total,
+                                                                 int32_t* __restrict__ PLAN) {
+    __shared__ uint32_t longbit[JA_SPARSE_PLAN_MAX / 8 / 32];
+    __shared__ long long wsum[16];
+    __shared__ int wlong[16];
+    const int x = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = total >> 3, r = total & 7;     // the shares of xcd_remap
+    const int c0 = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+    const int n = q + (x < r ? 1 : 0);
+    // each wave owns a segment of whole 64-entry steps
+    const int seg = (((n + 15) / 16) + 63) / 64 * 64;
+    const int s0 = min(n, wv * seg), s1 = min(n, s0 + seg);
+    int32_t* P = PLAN + c0;
+    long long sum = 0;
+    for (int i = s0 + lane; i < s1; i += 64) sum += P[i];
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) wsum[wv] = sum;
+    __syncthreads();
+    long long all = 0;
+    for (int v = 0; v < 16; ++v) all += wsum[v];
+    // flags: count * n > 2 * (sum of the share's counts), i.e. above twice the mean
+    int nl = 0;
+    for (int base = s0; base < s1; base += 64) {
+        const int i = base + lane;
+        const bool lg = i < s1 && (long long)P[i] * n > 2 * all;
+        const uint64_t bl = __ballot(lg);
+        nl += __popcll(bl);
+        if (lg) atomicOr(&longbit[i >> 5], 1u << (i & 31));
+        else if (i < s1) atomicAnd(&longbit[i >> 5], ~(1u << (i & 31)));
+    }
+    if (lane == 0) wlong[wv] = nl;
+    __syncthreads();                             // every count is read before any is overwritten
+    int pl = 0, n_long = 0;
+    for (int v = 0; v < 16; ++v) {
+        pl += v < wv ? wlong[v] : 0;
+        n_long += wlong[v];
+    }
+    int ps = n_long + (s0 - pl);                 // short entries before this segment
+    for (int base = s0; base < s1; base += 64) {
+        const int i = base + lane;
+        const bool in = i < s1;
+        const bool lg = in && ((longbit[i >> 5] >> (i & 31)) & 1u);
+        const uint64_t bl = __ballot(lg), bs = __ballot(in && !lg);
+        const uint32_t below_l = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(bl >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bl, 0u));
+        const uint32_t below_s = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(bs >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bs, 0u));
+        if (in) P[lg ? pl + (int)below_l : ps + (int)below_s] = c0 + i;
+        pl += __popcll(bl);
+        ps += __popcll(bs);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sparse_plan(const uint8_t* mask, int units, int nb, int32_t* plan,
+                              hipStream_t stream) {
+    hipLaunchKernelGGL(sparse_plan_count_kernel, dim3((units + 3) / 4), dim3(256), 0, stream,
+                       mask, nb, units, plan);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sparse_plan_order_kernel, dim3(8), dim3(1024), 0, stream, units, plan);
+    return hipGetLastError();
 }
 
 int splitkv_slots(int D) {

@@ -27,9 +27,14 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* vt, int B, 
                            int D, int64_t ldv, float softmax_scale, void* o, float* lse,
                            hipStream_t stream);
 
+// plan: the dispatch order of joint_attn_sparse_plan, or nullptr for the given order
 hipError_t launch_fwd_bf16_sparse(const void* q, const void* k, const void* vt,
                                   const uint8_t* mask, int B, int H, int N, int D, int64_t ldv,
-                                  float softmax_scale, void* o, float* lse, hipStream_t stream);
+                                  float softmax_scale, void* o, float* lse, hipStream_t stream,
+                                  const int32_t* plan = nullptr);
+// units = B * H * nb query blocks of an nb x nb mask per (b, h)
+hipError_t launch_sparse_plan(const uint8_t* mask, int units, int nb, int32_t* plan,
+                              hipStream_t stream);
 
 // split-KV planning: workgroups that run at once on the current device, and query rows
 // per workgroup of the bf16 forward for head size D.  The launch takes the slot count the

@@ -173,6 +173,48 @@ int joint_attn_fwd_bf16_sparse(const void* q, const void* k, const void* vt, int
                                          static_cast<hipStream_t>(stream)));
 }
 
+int64_t joint_attn_sparse_plan_bytes(int B, int H, int64_t N) {
+    if (B <= 0 || H <= 0 || N < 0 || N > JA_SPARSE_MAX_N) return -1;
+    const int64_t units = (int64_t)B * H * ((N + JA_SPARSE_BLOCK - 1) / JA_SPARSE_BLOCK);
+    if (units > JA_SPARSE_PLAN_MAX) return -1;
+    return units * (int64_t)sizeof(int32_t);
+}
+
+int joint_attn_sparse_plan(const uint8_t* block_mask, int B, int H, int64_t N, int32_t* plan,
+                           int64_t plan_bytes, void* stream) {
+    if (B <= 0 || H <= 0 || N < 0) return JA_EINVAL;
+    if (N > JA_SPARSE_MAX_N) return JA_EUNSUPPORTED;
+    const int64_t nb = (N + JA_SPARSE_BLOCK - 1) / JA_SPARSE_BLOCK;
+    const int64_t units = (int64_t)B * H * nb;
+    if (units > JA_SPARSE_PLAN_MAX) return JA_EUNSUPPORTED;
+    if (N == 0) return JA_OK;
+    if (!block_mask || !plan) return JA_EINVAL;
+    if (plan_bytes < units * (int64_t)sizeof(int32_t)) return JA_EINVAL;
+    if (reinterpret_cast<uintptr_t>(plan) & 3u) return JA_EUNSUPPORTED;
+    JA_LAUNCH(ja::launch_sparse_plan(block_mask, (int)units, (int)nb, plan,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int joint_attn_fwd_bf16_sparse_planned(const void* q, const void* k, const void* vt, int B,
+                                       int H, int64_t N, int D, int64_t ldv,
+                                       const uint8_t* block_mask, const int32_t* plan,
+                                       float softmax_scale, void* o, float* lse, void* stream) {
+    const int st = check_shape(B, H, N, D, ldv);
+    if (st != JA_OK) return st;
+    if (N > JA_SPARSE_MAX_N) return JA_EUNSUPPORTED;
+    if ((int64_t)B * H * ((N + JA_SPARSE_BLOCK - 1) / JA_SPARSE_BLOCK) > JA_SPARSE_PLAN_MAX)
+        return JA_EUNSUPPORTED;
+    if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return JA_EINVAL;
+    if (N == 0) return JA_OK;
+    if (!q || !k || !vt || !o || !block_mask || !plan) return JA_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(vt) || !aligned16(o)) return JA_EUNSUPPORTED;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return JA_EUNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(plan) & 3u) return JA_EUNSUPPORTED;
+    JA_LAUNCH(ja::launch_fwd_bf16_sparse(q, k, vt, block_mask, B, H, (int)N, D, ldv,
+                                         softmax_scale, o, lse,
+                                         static_cast<hipStream_t>(stream), plan));
+}
+
 int64_t joint_attn_fwd_bf16_splitkv_workspace(int B, int H, int64_t N, int D, int n_split) {
     if (B <= 0 || H <= 0 || N < 0 || D <= 0 || n_split <= 0 || !head_size_ok(D)) return -1;
     // only the query tiles of the last, partial round are split: fewer than the slots

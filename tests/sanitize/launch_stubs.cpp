@@ -52,9 +52,18 @@ hipError_t launch_fwd_bf16(const void*, const void*, const void*, int B, int H, 
 
 hipError_t launch_fwd_bf16_sparse(const void*, const void*, const void*, const uint8_t* mask,
                                   int B, int H, int N, int D, int64_t ldv, float, void*, float*,
-                                  hipStream_t) {
+                                  hipStream_t, const int32_t* plan) {
     if (!mask || N > JA_SPARSE_MAX_N || ldv < N) return hipErrorInvalidValue;
+    if (plan && (int64_t)B * H * ((N + JA_SPARSE_BLOCK - 1) / JA_SPARSE_BLOCK) > JA_SPARSE_PLAN_MAX)
+        return hipErrorInvalidValue;
     return shape_ok(B, H, N, D);
+}
+
+hipError_t launch_sparse_plan(const uint8_t* mask, int units, int nb, int32_t* plan, hipStream_t) {
+    if (!mask || !plan || units <= 0 || units > JA_SPARSE_PLAN_MAX || nb <= 0 ||
+        nb > JA_SPARSE_MAX_N / JA_SPARSE_BLOCK || units % nb != 0)
+        return hipErrorInvalidValue;
+    return hipSuccess;
 }
 
 // what the library reports without a GPU: 256 compute units, one workgroup each

@@ -222,6 +222,36 @@ def test_sparse_validation(lib):
     assert f(None, None, None, 1, 2, 0, 128, 0, None, 0.1, None, None, None) == 0      # N == 0
 
 
+def test_sparse_plan_sizes_and_validation(lib):
+    fake = 0x10000
+    assert lib.joint_attn_sparse_plan_bytes(2, 24, 16896) == 4 * 2 * 24 * 132
+    assert lib.joint_attn_sparse_plan_bytes(1, 1, 1) == 4
+    assert lib.joint_attn_sparse_plan_bytes(1, 1, 0) == 0
+    assert lib.joint_attn_sparse_plan_bytes(0, 1, 128) == -1
+    assert lib.joint_attn_sparse_plan_bytes(1, 1, 131073) == -1                  # N
+    assert lib.joint_attn_sparse_plan_bytes(2048, 2, 131072) == -1               # units
+    assert lib.joint_attn_sparse_plan_bytes(1024, 2, 131072) == 4 * 2097152
+    p = lib.joint_attn_sparse_plan
+    assert p(None, 1, 2, 300, fake, 24, None) == 1                               # mask
+    assert p(fake, 1, 2, 300, None, 24, None) == 1                               # plan
+    assert p(fake, 1, 2, 300, fake, 23, None) == 1                               # too small
+    assert p(fake, 1, 2, 300, fake + 2, 24, None) == 2                           # alignment
+    assert p(fake, 1, 2, 131073, fake, 1 << 20, None) == 2                       # N
+    assert p(fake, 2048, 2, 131072, fake, 1 << 30, None) == 2                    # units
+    assert p(fake, 0, 2, 300, fake, 24, None) == 1
+    assert p(None, 1, 2, 0, None, 0, None) == 0                                  # N == 0
+    f = lib.joint_attn_fwd_bf16_sparse_planned
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, fake, None, 0.1, fake, None, None) == 1
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, None, fake, 0.1, fake, None, None) == 1
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, fake, fake + 2, 0.1, fake, None, None) == 2
+    assert f(fake, fake, fake, 1, 2, 64, 96, 64, fake, fake, 0.1, fake, None, None) == 2
+    assert f(fake, fake, fake, 1, 2, 131073, 128, 131088, fake, fake, 0.1, fake, None, None) == 2
+    assert f(fake, fake, fake, 2048, 2, 131072, 64, 131072, fake, fake, 0.1, fake, None,
+             None) == 2                                                          # units
+    assert f(fake, fake, fake, 1, 2, 64, 128, 64, fake, fake, -1.0, fake, None, None) == 1
+    assert f(None, None, None, 1, 2, 0, 128, 0, None, None, 0.1, None, None, None) == 0
+
+
 def test_splitkv_sizes_and_validation(lib):
     fake = 0x10000
     ws = lib.joint_attn_fwd_bf16_splitkv_workspace
@@ -318,6 +348,9 @@ def test_launch_failure_is_reported(lib, monkeypatch):
                                                     fake, fake, None),
         "fwd_bf16_sparse": lambda: lib.joint_attn_fwd_bf16_sparse(
             fake, fake, fake, 1, 2, N, 128, ldv, fake, 0.1, fake, None, None),
+        "sparse_plan": lambda: lib.joint_attn_sparse_plan(fake, 1, 2, N, fake, 8, None),
+        "fwd_bf16_sparse_planned": lambda: lib.joint_attn_fwd_bf16_sparse_planned(
+            fake, fake, fake, 1, 2, N, 128, ldv, fake, fake, 0.1, fake, None, None),
         "fwd_bf16_splitkv": lambda: lib.joint_attn_fwd_bf16_splitkv(
             fake, fake, fake, 1, 2, N, 128, ldv, 0.1, 2, fake, ws_bf, fake, None, None),
         "fwd_bf16_splitkv_noalloc": lambda: lib.joint_attn_fwd_bf16_splitkv_noalloc(
@@ -415,6 +448,10 @@ def test_valid_calls_reach_the_launchers(lib, monkeypatch):
                                              fake, None) == 0
         assert lib.joint_attn_fwd_bf16_sparse(fake, fake, fake, B, H, N, D, ldv, fake, 0.1,
                                               fake, None, None) == 0
+        nbytes = lib.joint_attn_sparse_plan_bytes(B, H, N)
+        assert lib.joint_attn_sparse_plan(fake, B, H, N, fake, nbytes, None) == 0
+        assert lib.joint_attn_fwd_bf16_sparse_planned(fake, fake, fake, B, H, N, D, ldv, fake,
+                                                      fake, 0.1, fake, None, None) == 0
 
 
 def test_noalloc_validation(lib):
