@@ -1,8 +1,8 @@
 """GPU: every forward at the longest sequences it is tested for, on sampled rows against
 the oracle at each path's own bar.
 
-- sparse and token repair: exactly their declared maxima, JA_SPARSE_MAX_N and
-  JA_REPAIR_MAX_N (131072 tokens);
+- sparse (unplanned, and planned bit for bit against it) and token repair: exactly their
+  declared maxima, JA_SPARSE_MAX_N and JA_REPAIR_MAX_N (131072 tokens);
 - fp8 plain and split: 130771 tokens (a ragged last tile; 511 query tiles, so the split-KV
   call splits the 255 of its last round), plain and split-KV calls;
 - dense bf16: 2^20 + 77 tokens, through the plain, split-KV and in-place stream calls.
@@ -68,7 +68,15 @@ def test_sparse_longest():
     mask = synth.block_mask(w, "structured", 0.15, band=2, seed=4)
     sel = _sample(w, 96, 7)
     print("sparse N", w.N, flush=True)
-    test_gpu_sparse._assert("sparse N=%d" % w.N, *test_gpu_sparse._run(w, mask, sel)[:4])
+    got, ref, got_lse, ref_lse, (q, k, vt, m_dev, o) = test_gpu_sparse._run(w, mask, sel)
+    test_gpu_sparse._assert("sparse N=%d" % w.N, got, ref, got_lse, ref_lse)
+    # the dispatch plan at the same size: its rule, and the planned forward bit for bit
+    import torch
+    plan = ja.joint_attn_sparse_plan(m_dev, w.N)
+    o2 = ja.joint_attn_fwd_bf16_sparse_planned(q, k, vt, m_dev, plan, 1.0 / np.sqrt(w.D))
+    torch.cuda.synchronize()
+    assert np.array_equal(plan.cpu().numpy(), test_gpu_sparse._plan_rule(mask))
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
 
 
 @pytest.mark.parametrize("split_kv", [False, True])
