@@ -60,7 +60,7 @@ MEASURED_TRAFFIC = {
     "bytes": 1897940534,
     "sources": ("joint_attention_amd/csrc/fwd_bf16.hip", "joint_attention_amd/csrc/splitkv_merge.h",
                 "joint_attention_amd/csrc/ja_device.h"),
-    "sha256_16": "4dcdc91866b0043a",
+    "sha256_16": "35a7642e521ee655",
     "summary": "profiles/fwd_bf16_t2i_2048.txt",
 }
 

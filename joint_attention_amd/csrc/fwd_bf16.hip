@@ -93,7 +93,9 @@ __device__ inline int swap_bits23(int x) { return (x & ~12) | ((x & 4) << 1) | (
 // row being D contiguous elements of its stream's row), V^T from a packed copy (BHDN).
 // SPARSE: only the key blocks that a block mask (uint8 [B][H][nqb][nkb], 128 x 128 blocks)
 // allows for at least one of the workgroup's query blocks are visited; a wave whose own
-// query block does not see a visited block gives it zero weight.
+// query block does not see a visited block gives it zero weight.  With a dispatch plan
+// (ORDER, from sparse_plan_*_kernel below) workgroup position p runs query block ORDER[p]
+// instead of p: the same work per workgroup, started in another order.
 // PARTIAL (split-KV): the first n_full query tiles (whole rounds of workgroups over the
 // CUs) run over all keys and write O as usual; for each later query tile the keys are cut
 // into n_split ranges of whole tiles, one workgroup per (query tile, range), each writing
